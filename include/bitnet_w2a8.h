@@ -1,0 +1,161 @@
+/*
+ * bitnet_w2a8.h -- C ABI of the MI355X (gfx950) BitNet b1.58 W2A8 BitLinear matmul.
+ *
+ * The operation (one BitLinear layer, no bias):
+ *   out[m, n] = acc[m, n] * w_scale[n] / a_scale[m]
+ *   acc[m, n] = sum_k xq[m, k] * w[n, k]          (exact, int32)
+ * with w in {-1, 0, +1} stored 2 bits per weight, and xq the int8 per-token absmax
+ * quantization of bf16 activations x.
+ *
+ * Pages this follows (cited by title and section):
+ *   "BitNet 深度实战：微软 32K Star 的 1-bit LLM 推理框架" (chenxutan.com):
+ *       §2.4 absmean weight quantization; §3.2 BitLinear (bias=False);
+ *       §4.3 four 2-bit weights per byte, first weight in the low bits;
+ *       §4.4 int8 activations x ternary weights accumulated in int32.
+ *   "BitNet-Triton：消费级GPU上的1.58-bit大模型推理加速方案" (zingnex.cn), 技术架构:
+ *       §1 (N, K/4) uint8 packed weights unpacked inside the matmul kernel;
+ *       §2 int8 matrix-core products; §3 activation quantization fused into one launch.
+ *   "BitNet 1-bit LLM推理优化：内存布局、量化策略与硬件加速" (blog.hotdry.top):
+ *       §3.1 encode offline / decode just before compute; §3.2 the W2A8 path;
+ *       §5.3 dimensions that break the alignment unit are rejected.
+ *
+ * Conventions for every entry point:
+ *   - All tensor arguments are DEVICE pointers owned by the caller, row-major and
+ *     contiguous, 16-byte aligned, valid until the enqueued work completes.  The
+ *     library allocates nothing and keeps no per-call state.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Work is enqueued
+ *     on it and the call returns; nothing synchronizes.
+ *   - Arguments are validated on the host before any HIP call.  On a validation error
+ *     no work is enqueued and no output is touched.  Kernel faults surface at the
+ *     caller's next synchronization as HIP errors.
+ *   - M == 0 or N == 0 is a valid empty problem: BITNET_OK, nothing enqueued, and the
+ *     tensor pointers are not examined (empty tensors may have NULL data).
+ *   - K must be a positive multiple of 4 and at most BITNET_MAX_K.
+ *   - Inputs must be finite (NaN / Inf give unspecified results).
+ *   - Entry points are reentrant and thread-safe; calls on one stream are ordered.
+ *   - Only gfx950 devices are supported (BITNET_ERR_DEVICE otherwise).
+ *
+ * Packed weight layout (the interface format, produced by bitnet_pack_weights):
+ *   packed[n * (K/4) + j] holds weights k = 4j .. 4j+3 of output row n; weight
+ *   k = 4j + i sits in bits 2i .. 2i+1 as the code (w + 1): -1 -> 0b00, 0 -> 0b01,
+ *   +1 -> 0b10 (0b11 is never produced).
+ */
+#ifndef BITNET_W2A8_H
+#define BITNET_W2A8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BITNET_ABI_VERSION 1
+/* Largest supported K: keeps every int32 partial sum exact with margin. */
+#define BITNET_MAX_K (1 << 20)
+
+typedef enum {
+    BITNET_OK = 0,
+    BITNET_ERR_INVALID_ARG = 1, /* null pointer, negative size, K == 0, bad enum, M range */
+    BITNET_ERR_UNALIGNED = 2,   /* K % 4 != 0, or a pointer not 16-byte aligned          */
+    BITNET_ERR_WORKSPACE = 3,   /* workspace smaller than the size query returned         */
+    BITNET_ERR_HIP = 4,         /* a HIP runtime call or kernel launch failed             */
+    BITNET_ERR_DEVICE = 5       /* the current device is not gfx950                       */
+} bitnet_status;
+
+typedef enum {
+    BITNET_OUT_F32 = 0,  /* float   (M, N) */
+    BITNET_OUT_BF16 = 1, /* bf16    (M, N), stored as uint16 bit patterns, RNE of fp32 */
+    BITNET_OUT_I32 = 2   /* int32   (M, N), the raw exact accumulator acc[m, n]        */
+} bitnet_out_dtype;
+
+typedef enum {
+    BITNET_ALGO_AUTO = 0,   /* choose by M                                            */
+    BITNET_ALGO_SKINNY = 1, /* weight-streaming kernel, M <= BITNET_SKINNY_MAX_M      */
+    BITNET_ALGO_TILED = 2   /* tiled int8 matrix-core kernel, any M                    */
+} bitnet_algo;
+
+#define BITNET_SKINNY_MAX_M 16
+#define BITNET_GEMV_MAX_M 16
+
+/* ABI version of the loaded library (BITNET_ABI_VERSION at build time). */
+int bitnet_abi_version(void);
+
+/* Static, never-NULL description of a status code (unknown codes included). */
+const char* bitnet_status_str(int status);
+
+/* Text of the last HIP error seen by this thread inside the library ("" if none). */
+const char* bitnet_last_hip_error(void);
+
+/*
+ * bitnet_pack_weights -- offline weight preparation ("BitNet 深度实战" §2.4, §4.3).
+ *   w        : float (N, K) latent weights.
+ *   packed   : uint8 (N, K/4) output, layout above.
+ *   w_scale  : float (N) output, w_scale[n] = max(mean_k |w[n,k]|, 1e-5), the mean being
+ *              an fp64 sum over k in ascending order divided by K, rounded once to fp32.
+ *   Codes: clamp(round_half_even(w[n,k] / w_scale[n]), -1, 1), fp32 IEEE division.
+ */
+int bitnet_pack_weights(const float* w, int64_t N, int64_t K, uint8_t* packed, float* w_scale,
+                        void* stream);
+
+/*
+ * bitnet_unpack_weights -- inverse of the packing, for inspection and tests.
+ *   codes : int8 (N, K) output in {-1, 0, +1}.
+ */
+int bitnet_unpack_weights(const uint8_t* packed, int64_t N, int64_t K, int8_t* codes,
+                          void* stream);
+
+/*
+ * bitnet_quant_act -- per-token absmax int8 activation quantization in one launch
+ * ("BitNet-Triton" 技术架构 §3; "BitNet 1-bit LLM推理优化" §3.2).
+ *   x       : bf16 (M, K) as uint16 bit patterns.
+ *   xq      : int8 (M, K) output, clamp(round_half_even(x * a_scale[m]), -127, 127).
+ *   a_scale : float (M) output, a_scale[m] = 127 / max(max_k |x[m,k]|, 1e-5)
+ *             (one fp32 IEEE division; the product x * a_scale is one fp32 multiply).
+ */
+int bitnet_quant_act(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float* a_scale,
+                     void* stream);
+
+/*
+ * bitnet_w2a8_gemv -- decode-sized product, 1 <= M <= BITNET_GEMV_MAX_M
+ * ("BitNet 深度实战" §4.4; "BitNet-Triton" 技术架构 §1).
+ *   xq, a_scale       : as produced by bitnet_quant_act.
+ *   packed, w_scale   : as produced by bitnet_pack_weights.
+ *   out               : (M, N) of out_dtype (bitnet_out_dtype).
+ * out = acc * w_scale[n] * (1 / a_scale[m]) in fp32 (within 3 fp32 roundings of the exact
+ * value); bf16 is the RNE of that fp32 value; int32 is acc itself.
+ * M > BITNET_GEMV_MAX_M returns BITNET_ERR_INVALID_ARG.
+ */
+int bitnet_w2a8_gemv(const int8_t* xq, const float* a_scale, const uint8_t* packed,
+                     const float* w_scale, int64_t M, int64_t N, int64_t K, void* out,
+                     int out_dtype, void* stream);
+
+/*
+ * bitnet_w2a8_gemm -- the same product for any M >= 0 (prefill).  `algo` selects the
+ * kernel (bitnet_algo); BITNET_ALGO_SKINNY with M > BITNET_SKINNY_MAX_M returns
+ * BITNET_ERR_INVALID_ARG.  `workspace` / `ws_bytes` must cover
+ * bitnet_w2a8_gemm_workspace_size(M, N, K) bytes (may be NULL / 0 when that is 0).
+ */
+size_t bitnet_w2a8_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
+int bitnet_w2a8_gemm(const int8_t* xq, const float* a_scale, const uint8_t* packed,
+                     const float* w_scale, int64_t M, int64_t N, int64_t K, void* out,
+                     int out_dtype, int algo, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * bitnet_quant_gemv -- activation quantization fused into the decode product, one
+ * launch ("BitNet-Triton" 技术架构 §3: the quantization folded into the matmul launch).
+ *   x               : bf16 (M, K) as uint16, 1 <= M <= BITNET_GEMV_MAX_M.
+ *   packed, w_scale : as produced by bitnet_pack_weights.
+ *   out             : (M, N) of out_dtype, same arithmetic as bitnet_w2a8_gemv.
+ *   xq_out, a_scale_out : optional (NULL = not written) copies of the quantized
+ *                     activations and scales, bit-identical to bitnet_quant_act.
+ */
+int bitnet_quant_gemv(const uint16_t* x, const uint8_t* packed, const float* w_scale,
+                      int64_t M, int64_t N, int64_t K, void* out, int out_dtype,
+                      int8_t* xq_out, float* a_scale_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BITNET_W2A8_H */

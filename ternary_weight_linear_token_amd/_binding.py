@@ -1,0 +1,230 @@
+"""ctypes binding of libbitnet_w2a8.so: names mirror the C ABI in include/bitnet_w2a8.h.
+
+Marshalling only: tensors are checked (device, dtype, shape, contiguity) and their
+device pointers and the current HIP stream are handed to the library.  Outputs are
+allocated with torch unless passed in.
+"""
+from __future__ import annotations
+
+import ctypes
+import threading
+
+import torch
+
+from . import build as _build
+
+OUT_F32, OUT_BF16, OUT_I32 = 0, 1, 2
+ALGO_AUTO, ALGO_SKINNY, ALGO_TILED = 0, 1, 2
+GEMV_MAX_M = 16
+SKINNY_MAX_M = 16
+
+_OUT_TORCH = {OUT_F32: torch.float32, OUT_BF16: torch.bfloat16, OUT_I32: torch.int32}
+_OUT_NAMES = {"f32": OUT_F32, "float32": OUT_F32, "bf16": OUT_BF16, "bfloat16": OUT_BF16,
+              "i32": OUT_I32, "int32": OUT_I32}
+_ALGO_NAMES = {"auto": ALGO_AUTO, "skinny": ALGO_SKINNY, "tiled": ALGO_TILED}
+
+_lib = None
+_lock = threading.Lock()
+
+
+class BitnetError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        detail = status_str(status)
+        if status == 4:
+            detail += ": " + lib().bitnet_last_hip_error().decode()
+        super().__init__(f"{what}: {detail} (status {status})")
+
+
+def library_path() -> str:
+    return _build.LIB_PATH
+
+
+def lib():
+    """Load libbitnet_w2a8.so, building it first if it is missing or out of date."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not _build.is_current():
+            _build.build()
+        L = ctypes.CDLL(_build.LIB_PATH)
+        p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        sigs = {
+            "bitnet_abi_version": ([], i32),
+            "bitnet_status_str": ([i32], ctypes.c_char_p),
+            "bitnet_last_hip_error": ([], ctypes.c_char_p),
+            "bitnet_pack_weights": ([p, i64, i64, p, p, p], i32),
+            "bitnet_unpack_weights": ([p, i64, i64, p, p], i32),
+            "bitnet_quant_act": ([p, i64, i64, p, p, p], i32),
+            "bitnet_w2a8_gemv": ([p, p, p, p, i64, i64, i64, p, i32, p], i32),
+            "bitnet_w2a8_gemm_workspace_size": ([i64, i64, i64], ctypes.c_size_t),
+            "bitnet_w2a8_gemm": ([p, p, p, p, i64, i64, i64, p, i32, i32, p, ctypes.c_size_t, p], i32),
+            "bitnet_quant_gemv": ([p, p, p, i64, i64, i64, p, i32, p, p, p], i32),
+        }
+        for name, (args, res) in sigs.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+        return L
+
+
+def abi_version() -> int:
+    return int(lib().bitnet_abi_version())
+
+
+def status_str(status: int) -> str:
+    return lib().bitnet_status_str(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise BitnetError(status, what)
+
+
+def _out_code(out_dtype) -> int:
+    if isinstance(out_dtype, int):
+        return out_dtype
+    if isinstance(out_dtype, torch.dtype):
+        for k, v in _OUT_TORCH.items():
+            if v == out_dtype:
+                return k
+    return _OUT_NAMES[str(out_dtype)]
+
+
+def _tensor(t: torch.Tensor, dtype, name: str, shape=None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor (the library has no CPU path)")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t.data_ptr()
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _opt_ptr(t, dtype, name, shape):
+    return None if t is None else _tensor(t, dtype, name, shape)
+
+
+def pack_weights(w: torch.Tensor, packed: torch.Tensor | None = None,
+                 w_scale: torch.Tensor | None = None):
+    """fp32 (N, K) latent weights -> (packed uint8 (N, K/4), w_scale fp32 (N,))."""
+    N, K = w.shape
+    if packed is None:
+        packed = torch.empty((N, K // 4), dtype=torch.uint8, device=w.device)
+    if w_scale is None:
+        w_scale = torch.empty((N,), dtype=torch.float32, device=w.device)
+    _check(lib().bitnet_pack_weights(_tensor(w, torch.float32, "w", (N, K)), N, K,
+                                     _tensor(packed, torch.uint8, "packed", (N, K // 4)),
+                                     _tensor(w_scale, torch.float32, "w_scale", (N,)), _stream(w)),
+           "bitnet_pack_weights")
+    return packed, w_scale
+
+
+def unpack_weights(packed: torch.Tensor, K: int, codes: torch.Tensor | None = None):
+    """packed uint8 (N, K/4) -> int8 codes (N, K) in {-1, 0, 1}."""
+    N = packed.shape[0]
+    if codes is None:
+        codes = torch.empty((N, K), dtype=torch.int8, device=packed.device)
+    _check(lib().bitnet_unpack_weights(_tensor(packed, torch.uint8, "packed", (N, K // 4)), N, K,
+                                       _tensor(codes, torch.int8, "codes", (N, K)), _stream(packed)),
+           "bitnet_unpack_weights")
+    return codes
+
+
+def quant_act(x: torch.Tensor, xq: torch.Tensor | None = None,
+              a_scale: torch.Tensor | None = None):
+    """bf16 (M, K) -> (xq int8 (M, K), a_scale fp32 (M,) = 127 / max|x|)."""
+    M, K = x.shape
+    if xq is None:
+        xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if a_scale is None:
+        a_scale = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _check(lib().bitnet_quant_act(_tensor(x, torch.bfloat16, "x", (M, K)), M, K,
+                                  _tensor(xq, torch.int8, "xq", (M, K)),
+                                  _tensor(a_scale, torch.float32, "a_scale", (M,)), _stream(x)),
+           "bitnet_quant_act")
+    return xq, a_scale
+
+
+def _alloc_out(out, M, N, code, device):
+    if out is None:
+        out = torch.empty((M, N), dtype=_OUT_TORCH[code], device=device)
+    return out
+
+
+def gemv(xq, a_scale, packed, w_scale, out_dtype="f32", out=None):
+    """Decode-sized product (M <= 16): int8 xq x packed ternary -> (M, N)."""
+    M, K = xq.shape
+    N = packed.shape[0]
+    code = _out_code(out_dtype)
+    out = _alloc_out(out, M, N, code, xq.device)
+    _check(lib().bitnet_w2a8_gemv(_tensor(xq, torch.int8, "xq", (M, K)),
+                                  _tensor(a_scale, torch.float32, "a_scale", (M,)),
+                                  _tensor(packed, torch.uint8, "packed", (N, K // 4)),
+                                  _tensor(w_scale, torch.float32, "w_scale", (N,)), M, N, K,
+                                  _tensor(out, _OUT_TORCH[code], "out", (M, N)), code, _stream(xq)),
+           "bitnet_w2a8_gemv")
+    return out
+
+
+def gemm(xq, a_scale, packed, w_scale, out_dtype="f32", algo="auto", out=None, workspace=None):
+    """Product for any M: int8 xq x packed ternary -> (M, N)."""
+    M, K = xq.shape
+    N = packed.shape[0]
+    code = _out_code(out_dtype)
+    algo_code = _ALGO_NAMES[algo] if isinstance(algo, str) else int(algo)
+    out = _alloc_out(out, M, N, code, xq.device)
+    ws_bytes = int(lib().bitnet_w2a8_gemm_workspace_size(M, N, K))
+    ws_ptr = None
+    if ws_bytes:
+        if workspace is None:
+            workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=xq.device)
+        ws_ptr = _tensor(workspace, torch.uint8, "workspace")
+        ws_bytes = workspace.numel()
+    _check(lib().bitnet_w2a8_gemm(_tensor(xq, torch.int8, "xq", (M, K)),
+                                  _tensor(a_scale, torch.float32, "a_scale", (M,)),
+                                  _tensor(packed, torch.uint8, "packed", (N, K // 4)),
+                                  _tensor(w_scale, torch.float32, "w_scale", (N,)), M, N, K,
+                                  _tensor(out, _OUT_TORCH[code], "out", (M, N)), code, algo_code,
+                                  ws_ptr, ws_bytes, _stream(xq)),
+           "bitnet_w2a8_gemm")
+    return out
+
+
+def quant_gemv(x, packed, w_scale, out_dtype="f32", out=None, return_quant=False):
+    """Fused per-token int8 quantization + decode product (M <= 16) in one launch."""
+    M, K = x.shape
+    N = packed.shape[0]
+    code = _out_code(out_dtype)
+    out = _alloc_out(out, M, N, code, x.device)
+    xq = a_scale = None
+    if return_quant:
+        xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
+        a_scale = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _check(lib().bitnet_quant_gemv(_tensor(x, torch.bfloat16, "x", (M, K)),
+                                   _tensor(packed, torch.uint8, "packed", (N, K // 4)),
+                                   _tensor(w_scale, torch.float32, "w_scale", (N,)), M, N, K,
+                                   _tensor(out, _OUT_TORCH[code], "out", (M, N)), code,
+                                   _opt_ptr(xq, torch.int8, "xq_out", (M, K)),
+                                   _opt_ptr(a_scale, torch.float32, "a_scale_out", (M,)), _stream(x)),
+           "bitnet_quant_gemv")
+    return (out, xq, a_scale) if return_quant else out
+
+
+def bitlinear(x, packed, w_scale, out_dtype="f32"):
+    """One BitLinear forward: fused quant+GEMV for M <= 16, else quant + GEMM."""
+    M = x.shape[0]
+    if M <= GEMV_MAX_M:
+        return quant_gemv(x, packed, w_scale, out_dtype)
+    xq, a_scale = quant_act(x)
+    return gemm(xq, a_scale, packed, w_scale, out_dtype)

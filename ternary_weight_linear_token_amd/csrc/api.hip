@@ -1,0 +1,183 @@
+// api.hip -- the extern "C" entry points declared in include/bitnet_w2a8.h.
+//
+// Every entry point validates its arguments on the host, before any HIP call, and
+// returns a bitnet_status code; nothing throws across the ABI.  Work is enqueued on the
+// caller's stream; nothing here synchronizes or allocates.
+#include <atomic>
+#include <cstdio>
+#include <cstring>
+
+#include "bitnet_w2a8.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_last_hip_error[256] = "";
+
+int record_hip(hipError_t e) {
+    if (e == hipSuccess) return BITNET_OK;
+    std::snprintf(g_last_hip_error, sizeof g_last_hip_error, "%s (%d)", hipGetErrorString(e),
+                  (int)e);
+    return BITNET_ERR_HIP;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Per-device cache of "is this a gfx950": 0 unknown, 1 yes, 2 no.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch[kMaxDevices];
+
+int check_device() {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return record_hip(e);
+    if (dev < 0 || dev >= kMaxDevices) return BITNET_ERR_DEVICE;
+    int state = g_arch[dev].load(std::memory_order_acquire);
+    if (state == 0) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess) return record_hip(e);
+        state = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        g_arch[dev].store(state, std::memory_order_release);
+    }
+    return state == 1 ? BITNET_OK : BITNET_ERR_DEVICE;
+}
+
+// Shared shape checks: M, N >= 0, 4 <= K <= BITNET_MAX_K, K % 4 == 0, sizes that fit the
+// kernels' 32-bit indices and grids.
+int check_shape(int64_t M, int64_t N, int64_t K) {
+    if (M < 0 || N < 0 || K < 1) return BITNET_ERR_INVALID_ARG;
+    if (K > BITNET_MAX_K) return BITNET_ERR_INVALID_ARG;
+    if (M > INT32_MAX || N > INT32_MAX) return BITNET_ERR_INVALID_ARG;
+    if (K % 4 != 0) return BITNET_ERR_UNALIGNED;
+    return BITNET_OK;
+}
+
+bool valid_dtype(int dt) {
+    return dt == BITNET_OUT_F32 || dt == BITNET_OUT_BF16 || dt == BITNET_OUT_I32;
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+int bitnet_abi_version(void) { return BITNET_ABI_VERSION; }
+
+const char* bitnet_status_str(int status) {
+    switch (status) {
+        case BITNET_OK: return "ok";
+        case BITNET_ERR_INVALID_ARG: return "invalid argument";
+        case BITNET_ERR_UNALIGNED: return "unaligned size or pointer";
+        case BITNET_ERR_WORKSPACE: return "workspace too small";
+        case BITNET_ERR_HIP: return "HIP runtime error";
+        case BITNET_ERR_DEVICE: return "unsupported device (gfx950 required)";
+        default: return "unknown status";
+    }
+}
+
+const char* bitnet_last_hip_error(void) { return g_last_hip_error; }
+
+int bitnet_pack_weights(const float* w, int64_t N, int64_t K, uint8_t* packed, float* w_scale,
+                        void* stream) {
+    int st = check_shape(0, N, K);
+    if (st) return st;
+    if (N == 0) return BITNET_OK;
+    if (!w || !packed || !w_scale) return BITNET_ERR_INVALID_ARG;
+    if (!aligned16(w) || !aligned16(packed) || !aligned16(w_scale)) return BITNET_ERR_UNALIGNED;
+    if ((st = check_device())) return st;
+    return record_hip(bitnet::launch_pack_weights(w, N, K, packed, w_scale, as_stream(stream)));
+}
+
+int bitnet_unpack_weights(const uint8_t* packed, int64_t N, int64_t K, int8_t* codes,
+                          void* stream) {
+    int st = check_shape(0, N, K);
+    if (st) return st;
+    if (N == 0) return BITNET_OK;
+    if (!packed || !codes) return BITNET_ERR_INVALID_ARG;
+    if (!aligned16(packed) || !aligned16(codes)) return BITNET_ERR_UNALIGNED;
+    if ((st = check_device())) return st;
+    return record_hip(bitnet::launch_unpack_weights(packed, N, K, codes, as_stream(stream)));
+}
+
+int bitnet_quant_act(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float* a_scale,
+                     void* stream) {
+    int st = check_shape(M, 0, K);
+    if (st) return st;
+    if (M == 0) return BITNET_OK;
+    if (!x || !xq || !a_scale) return BITNET_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(xq) || !aligned16(a_scale)) return BITNET_ERR_UNALIGNED;
+    if ((st = check_device())) return st;
+    return record_hip(bitnet::launch_quant_act(x, M, K, xq, a_scale, as_stream(stream)));
+}
+
+int bitnet_w2a8_gemv(const int8_t* xq, const float* a_scale, const uint8_t* packed,
+                     const float* w_scale, int64_t M, int64_t N, int64_t K, void* out,
+                     int out_dtype, void* stream) {
+    if (!valid_dtype(out_dtype)) return BITNET_ERR_INVALID_ARG;
+    int st = check_shape(M, N, K);
+    if (st) return st;
+    if (M > BITNET_GEMV_MAX_M) return BITNET_ERR_INVALID_ARG;
+    if (M == 0 || N == 0) return BITNET_OK;
+    if (!xq || !a_scale || !packed || !w_scale || !out) return BITNET_ERR_INVALID_ARG;
+    if (!aligned16(xq) || !aligned16(a_scale) || !aligned16(packed) || !aligned16(w_scale) ||
+        !aligned16(out))
+        return BITNET_ERR_UNALIGNED;
+    if ((st = check_device())) return st;
+    return record_hip(bitnet::launch_skinny(xq, a_scale, nullptr, packed, w_scale, M, N, K, out,
+                                            out_dtype, nullptr, nullptr, as_stream(stream)));
+}
+
+size_t bitnet_w2a8_gemm_workspace_size(int64_t M, int64_t N, int64_t K) {
+    (void)M;
+    (void)N;
+    (void)K;
+    return 0;
+}
+
+int bitnet_w2a8_gemm(const int8_t* xq, const float* a_scale, const uint8_t* packed,
+                     const float* w_scale, int64_t M, int64_t N, int64_t K, void* out,
+                     int out_dtype, int algo, void* workspace, size_t ws_bytes, void* stream) {
+    if (!valid_dtype(out_dtype)) return BITNET_ERR_INVALID_ARG;
+    if (algo != BITNET_ALGO_AUTO && algo != BITNET_ALGO_SKINNY && algo != BITNET_ALGO_TILED)
+        return BITNET_ERR_INVALID_ARG;
+    int st = check_shape(M, N, K);
+    if (st) return st;
+    if (algo == BITNET_ALGO_SKINNY && M > BITNET_SKINNY_MAX_M) return BITNET_ERR_INVALID_ARG;
+    if (M == 0 || N == 0) return BITNET_OK;
+    if (!xq || !a_scale || !packed || !w_scale || !out) return BITNET_ERR_INVALID_ARG;
+    if (ws_bytes < bitnet_w2a8_gemm_workspace_size(M, N, K)) return BITNET_ERR_WORKSPACE;
+    if (ws_bytes > 0 && !workspace) return BITNET_ERR_INVALID_ARG;
+    if (!aligned16(xq) || !aligned16(a_scale) || !aligned16(packed) || !aligned16(w_scale) ||
+        !aligned16(out) || !aligned16(workspace))
+        return BITNET_ERR_UNALIGNED;
+    if ((st = check_device())) return st;
+    const bool skinny =
+        algo == BITNET_ALGO_SKINNY || (algo == BITNET_ALGO_AUTO && M <= BITNET_SKINNY_MAX_M);
+    if (skinny)
+        return record_hip(bitnet::launch_skinny(xq, a_scale, nullptr, packed, w_scale, M, N, K,
+                                                out, out_dtype, nullptr, nullptr,
+                                                as_stream(stream)));
+    return record_hip(
+        bitnet::launch_tiled(xq, a_scale, packed, w_scale, M, N, K, out, out_dtype, as_stream(stream)));
+}
+
+int bitnet_quant_gemv(const uint16_t* x, const uint8_t* packed, const float* w_scale,
+                      int64_t M, int64_t N, int64_t K, void* out, int out_dtype,
+                      int8_t* xq_out, float* a_scale_out, void* stream) {
+    if (!valid_dtype(out_dtype)) return BITNET_ERR_INVALID_ARG;
+    int st = check_shape(M, N, K);
+    if (st) return st;
+    if (M > BITNET_GEMV_MAX_M) return BITNET_ERR_INVALID_ARG;
+    if (M == 0 || N == 0) return BITNET_OK;
+    if (!x || !packed || !w_scale || !out) return BITNET_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(packed) || !aligned16(w_scale) || !aligned16(out) ||
+        !aligned16(xq_out) || !aligned16(a_scale_out))
+        return BITNET_ERR_UNALIGNED;
+    if ((st = check_device())) return st;
+    return record_hip(bitnet::launch_skinny(nullptr, nullptr, x, packed, w_scale, M, N, K, out,
+                                            out_dtype, xq_out, a_scale_out, as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,81 @@
+// device_common.hpp -- small device helpers shared by the gfx950 kernels of the
+// W2A8 BitLinear library (bf16 conversion, byte transposes, wave reductions).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bitnet {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+// bf16 bit pattern -> fp32: bf16 is the upper half of binary32, so this is exact.
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
+    return __uint_as_float(h << 16);
+}
+
+// fp32 -> bf16 bit pattern, round to nearest, ties to even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// 4x4 byte transpose: d[b] holds bytes (b, 0..3) of a 16-byte group; on return e[i]
+// holds byte i of d[0], d[1], d[2], d[3] (in that order).  v_perm_b32 picks bytes
+// from the 8-byte pool {hi:lo}, selector values 0-3 address lo, 4-7 address hi.
+__device__ __forceinline__ void transpose4x4_bytes(const uint32_t d[4], uint32_t e[4]) {
+    uint32_t lo01 = __builtin_amdgcn_perm(d[1], d[0], 0x05010400u);  // d0.0 d1.0 d0.1 d1.1
+    uint32_t hi01 = __builtin_amdgcn_perm(d[1], d[0], 0x07030602u);  // d0.2 d1.2 d0.3 d1.3
+    uint32_t lo23 = __builtin_amdgcn_perm(d[3], d[2], 0x05010400u);  // d2.0 d3.0 d2.1 d3.1
+    uint32_t hi23 = __builtin_amdgcn_perm(d[3], d[2], 0x07030602u);  // d2.2 d3.2 d2.3 d3.3
+    e[0] = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u);           // d0.0 d1.0 d2.0 d3.0
+    e[1] = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u);           // d0.1 d1.1 d2.1 d3.1
+    e[2] = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u);
+    e[3] = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
+}
+
+// Sum of the four signed bytes of v (dot product with 0x01010101).
+__device__ __forceinline__ int sum_i8x4(uint32_t v, int acc) {
+    return __builtin_amdgcn_sdot4((int)v, 0x01010101, acc, false);
+}
+
+// Signed weight bytes from 2-bit codes: field i (bits 2i..2i+1) of each byte of d,
+// code c in {0,1,2} -> w = c - 1 as int8 {0xFF, 0x00, 0x01} through a v_perm lookup.
+template <int I>
+__device__ __forceinline__ uint32_t ternary_field_i8(uint32_t d) {
+    uint32_t sel = (d >> (2 * I)) & 0x03030303u;
+    return __builtin_amdgcn_perm(0u, 0x000100FFu, sel);
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        uint32_t o = (uint32_t)__shfl_xor((int)v, off, 64);
+        v = v > o ? v : o;
+    }
+    return v;
+}
+
+__device__ __forceinline__ int wave_sum_i32(int v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// Store one output element in the requested dtype (0 = f32, 1 = bf16, 2 = int32).
+__device__ __forceinline__ void store_out(void* out, int64_t idx, int dtype, int acc, float s,
+                                          float inv_a) {
+    if (dtype == 2) {
+        static_cast<int*>(out)[idx] = acc;
+    } else {
+        float v = ((float)acc * s) * inv_a;
+        if (dtype == 0)
+            static_cast<float*>(out)[idx] = v;
+        else
+            static_cast<uint16_t*>(out)[idx] = f32_to_bf16_rne(v);
+    }
+}
+
+}  // namespace bitnet

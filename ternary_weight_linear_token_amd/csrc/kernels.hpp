@@ -1,0 +1,29 @@
+// kernels.hpp -- host-side launchers of the gfx950 kernels (internal to the library).
+// Arguments are validated by the C ABI layer (api.hip) before any launcher runs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bitnet {
+
+hipError_t launch_pack_weights(const float* w, int64_t N, int64_t K, uint8_t* packed,
+                               float* scale, hipStream_t stream);
+hipError_t launch_unpack_weights(const uint8_t* packed, int64_t N, int64_t K, int8_t* codes,
+                                 hipStream_t stream);
+hipError_t launch_quant_act(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float* a_scale,
+                            hipStream_t stream);
+
+// Weight-streaming product for 1 <= M <= 16.  When x_bf16 is non-null the activations
+// are quantized inside the kernel (xq / a_scale ignored; xq_out / a_out optional copies).
+hipError_t launch_skinny(const int8_t* xq, const float* a_scale, const uint16_t* x_bf16,
+                         const uint8_t* packed, const float* w_scale, int64_t M, int64_t N,
+                         int64_t K, void* out, int out_dtype, int8_t* xq_out, float* a_out,
+                         hipStream_t stream);
+
+// Tiled int8 matrix-core product for any M.
+hipError_t launch_tiled(const int8_t* xq, const float* a_scale, const uint8_t* packed,
+                        const float* w_scale, int64_t M, int64_t N, int64_t K, void* out,
+                        int out_dtype, hipStream_t stream);
+
+}  // namespace bitnet

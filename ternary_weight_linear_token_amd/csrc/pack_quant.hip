@@ -1,0 +1,180 @@
+// pack_quant.hip -- offline weight packing and per-token activation quantization for
+// gfx950.
+//
+// Weight packing follows "BitNet 深度实战" (chenxutan.com) §2.4 (per-row absmean scale,
+// round, clamp to {-1,0,+1}) and §4.3 (four 2-bit weights per byte, the first in the
+// low bits), with code = w + 1, into the (N, K/4) uint8 array of "BitNet-Triton"
+// (zingnex.cn) 技术架构 §1.  Activation quantization follows "BitNet-Triton" 技术架构 §3
+// (one fused launch) with the per-token absmax scale 127 / max|x|.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace bitnet {
+
+// ---------------------------------------------------------------- weight scale ---
+// One thread per output row: the absmean is an fp64 sum over k in ascending order
+// (a fixed order, so the scale is reproducible bit for bit), divided by K, rounded
+// once to fp32 and clamped below at 1e-5.  Offline work: simplicity over speed.
+__global__ __launch_bounds__(256) void weight_scale_kernel(const float* __restrict__ w,
+                                                           int64_t N, int64_t K,
+                                                           float* __restrict__ scale) {
+    int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (n >= N) return;
+    const float* row = w + n * K;
+    double sum = 0.0;
+    for (int64_t k = 0; k < K; ++k) sum += fabs((double)row[k]);
+    float s = (float)(sum / (double)K);
+    scale[n] = s < 1e-5f ? 1e-5f : s;
+}
+
+// ---------------------------------------------------------------- weight codes ---
+// One thread per packed byte (4 weights): q = clamp(rne(w / s), -1, 1) with one IEEE
+// fp32 division, code = q + 1 in bits 2i..2i+1.
+__global__ __launch_bounds__(256) void weight_codes_kernel(const float* __restrict__ w,
+                                                           const float* __restrict__ scale,
+                                                           int64_t N, int64_t K,
+                                                           uint8_t* __restrict__ packed) {
+    const int64_t kb = K / 4;
+    int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= N * kb) return;
+    int64_t n = idx / kb;
+    const float s = scale[n];
+    const float4 v = *reinterpret_cast<const float4*>(w + idx * 4);
+    const float vals[4] = {v.x, v.y, v.z, v.w};
+    uint32_t byte = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float r = rintf(vals[i] / s);
+        r = fminf(fmaxf(r, -1.0f), 1.0f);
+        byte |= (uint32_t)((int)r + 1) << (2 * i);
+    }
+    packed[idx] = (uint8_t)byte;
+}
+
+// One thread per packed byte -> four int8 codes (inspection / tests).
+__global__ __launch_bounds__(256) void unpack_kernel(const uint8_t* __restrict__ packed,
+                                                     int64_t total_bytes,
+                                                     int8_t* __restrict__ codes) {
+    int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= total_bytes) return;
+    uint32_t b = packed[idx];
+    uint32_t out = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out |= (uint32_t)(uint8_t)((int)((b >> (2 * i)) & 3u) - 1) << (8 * i);
+    *reinterpret_cast<uint32_t*>(codes + idx * 4) = out;
+}
+
+// ------------------------------------------------------- activation quantization ---
+// One 256-thread block per token row.  Pass 1: max |x| as the integer max of the bf16
+// magnitude bits (monotone in |x| for finite values), 4 elements (8 bytes) per load.
+// Pass 2: a = 127 / max(amax, 1e-5) (IEEE division), q = clamp(rne(x * a), +-127).
+// Rows up to G*1024 elements keep their loads in registers between the passes; longer
+// rows (G == 0) read the row twice.
+template <int G>
+__global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restrict__ x,
+                                                        int64_t K, int8_t* __restrict__ xq,
+                                                        float* __restrict__ a_scale) {
+    __shared__ uint32_t s_max[4];
+    const int64_t m = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int64_t groups = K / 4;
+    const uint2* row = reinterpret_cast<const uint2*>(x + m * K);
+
+    uint2 held[G > 0 ? G : 1];
+    uint32_t mx = 0;
+    if (G > 0) {
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            int64_t g = tid + (int64_t)i * 256;
+            held[i] = g < groups ? row[g] : make_uint2(0u, 0u);
+        }
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            uint32_t a = held[i].x & 0x7FFF7FFFu, b = held[i].y & 0x7FFF7FFFu;
+            mx = max(mx, max(max(a & 0xFFFFu, a >> 16), max(b & 0xFFFFu, b >> 16)));
+        }
+    } else {
+        for (int64_t g = tid; g < groups; g += 256) {
+            uint2 v = row[g];
+            uint32_t a = v.x & 0x7FFF7FFFu, b = v.y & 0x7FFF7FFFu;
+            mx = max(mx, max(max(a & 0xFFFFu, a >> 16), max(b & 0xFFFFu, b >> 16)));
+        }
+    }
+    mx = wave_max_u32(mx);
+    if ((tid & 63) == 0) s_max[tid >> 6] = mx;
+    __syncthreads();
+    mx = max(max(s_max[0], s_max[1]), max(s_max[2], s_max[3]));
+    float amax = bf16_bits_to_f32(mx);
+    amax = amax < 1e-5f ? 1e-5f : amax;
+    const float a = 127.0f / amax;
+    if (tid == 0) a_scale[m] = a;
+
+    uint32_t* orow = reinterpret_cast<uint32_t*>(xq + m * K);
+    auto quant4 = [&](uint2 v) -> uint32_t {
+        const uint32_t h[4] = {v.x & 0xFFFFu, v.x >> 16, v.y & 0xFFFFu, v.y >> 16};
+        uint32_t packed = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float r = rintf(bf16_bits_to_f32(h[j]) * a);
+            r = fminf(fmaxf(r, -127.0f), 127.0f);
+            packed |= ((uint32_t)(int)r & 0xFFu) << (8 * j);
+        }
+        return packed;
+    };
+    if (G > 0) {
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            int64_t g = tid + (int64_t)i * 256;
+            if (g < groups) orow[g] = quant4(held[i]);
+        }
+    } else {
+        for (int64_t g = tid; g < groups; g += 256) orow[g] = quant4(row[g]);
+    }
+}
+
+// ------------------------------------------------------------------ launchers ---
+
+hipError_t launch_pack_weights(const float* w, int64_t N, int64_t K, uint8_t* packed,
+                               float* scale, hipStream_t stream) {
+    dim3 blk(256);
+    hipLaunchKernelGGL(weight_scale_kernel, dim3((unsigned)((N + 255) / 256)), blk, 0, stream, w,
+                       N, K, scale);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    int64_t total = N * (K / 4);
+    hipLaunchKernelGGL(weight_codes_kernel, dim3((unsigned)((total + 255) / 256)), blk, 0,
+                       stream, w, scale, N, K, packed);
+    return hipGetLastError();
+}
+
+hipError_t launch_unpack_weights(const uint8_t* packed, int64_t N, int64_t K, int8_t* codes,
+                                 hipStream_t stream) {
+    int64_t total = N * (K / 4);
+    hipLaunchKernelGGL(unpack_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
+                       packed, total, codes);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_act(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float* a_scale,
+                            hipStream_t stream) {
+    const int64_t groups = K / 4;
+    const int64_t per_thread = (groups + 255) / 256;
+    dim3 grid((unsigned)M), blk(256);
+    if (per_thread <= 1)
+        hipLaunchKernelGGL(quant_act_kernel<1>, grid, blk, 0, stream, x, K, xq, a_scale);
+    else if (per_thread <= 2)
+        hipLaunchKernelGGL(quant_act_kernel<2>, grid, blk, 0, stream, x, K, xq, a_scale);
+    else if (per_thread <= 4)
+        hipLaunchKernelGGL(quant_act_kernel<4>, grid, blk, 0, stream, x, K, xq, a_scale);
+    else if (per_thread <= 8)
+        hipLaunchKernelGGL(quant_act_kernel<8>, grid, blk, 0, stream, x, K, xq, a_scale);
+    else if (per_thread <= 16)
+        hipLaunchKernelGGL(quant_act_kernel<16>, grid, blk, 0, stream, x, K, xq, a_scale);
+    else if (per_thread <= 32)
+        hipLaunchKernelGGL(quant_act_kernel<32>, grid, blk, 0, stream, x, K, xq, a_scale);
+    else
+        hipLaunchKernelGGL(quant_act_kernel<0>, grid, blk, 0, stream, x, K, xq, a_scale);
+    return hipGetLastError();
+}
+
+}  // namespace bitnet

@@ -1,0 +1,145 @@
+"""The C ABI boundary, on the CPU: the library loads, exports every entry point that
+include/bitnet_w2a8.h declares, and rejects bad arguments on the host before any HIP
+call (so these run without a GPU and never launch a kernel)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import ternary_weight_linear_token_amd as bw
+from ternary_weight_linear_token_amd import build as bw_build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bitnet_w2a8.h")
+
+OK, INVALID, UNALIGNED, WORKSPACE, HIP, DEVICE = 0, 1, 2, 3, 4, 5
+
+# Fake, 16-byte-aligned, never-dereferenced addresses: validation must reject the call
+# before anything could touch them.
+A, B, C, D, E, F = 0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bitnet_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return bw.lib()
+
+
+def test_library_is_current_build():
+    bw.lib()
+    assert bw_build.is_current()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert len(names) >= 10
+    for name in names:
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", bw.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\b(bitnet_\w+)\b", out))
+    assert set(names) <= exported
+
+
+def test_library_has_gfx950_code_only():
+    # The offload bundle ids embedded in our own build name the GPU targets it carries.
+    blob = open(bw.library_path(), "rb").read()
+    targets = set(re.findall(rb"amdgcn-amd-amdhsa-[-\w:+]*?(gfx\w+)", blob))
+    assert targets == {b"gfx950"}
+
+
+def test_abi_version_and_status_strings(L):
+    assert bw.abi_version() == 1
+    for s in range(6):
+        assert bw.status_str(s) not in ("", "unknown status")
+    assert bw.status_str(99) == "unknown status"
+    assert bw.status_str(-1) == "unknown status"
+
+
+def test_quant_act_validation(L):
+    f = L.bitnet_quant_act
+    assert f(None, 1, 8, B, C, None) == INVALID
+    assert f(A, 1, 8, None, C, None) == INVALID
+    assert f(A, 1, 8, B, None, None) == INVALID
+    assert f(A, -1, 8, B, C, None) == INVALID
+    assert f(A, 1, 0, B, C, None) == INVALID
+    assert f(A, 1, -4, B, C, None) == INVALID
+    assert f(A, 1, 6, B, C, None) == UNALIGNED
+    assert f(A + 2, 1, 8, B, C, None) == UNALIGNED
+    assert f(A, 1, (1 << 20) + 4, B, C, None) == INVALID
+    assert f(A, 1 << 31, 8, B, C, None) == INVALID
+    assert f(A, 0, 8, B, C, None) == OK  # empty problem: nothing enqueued
+
+
+def test_pack_validation(L):
+    f = L.bitnet_pack_weights
+    assert f(None, 4, 8, B, C, None) == INVALID
+    assert f(A, 4, 10, B, C, None) == UNALIGNED
+    assert f(A, 4, 8, B + 1, C, None) == UNALIGNED
+    assert f(A, -4, 8, B, C, None) == INVALID
+    assert f(A, 0, 8, B, C, None) == OK
+    g = L.bitnet_unpack_weights
+    assert g(None, 4, 8, B, None) == INVALID
+    assert g(A, 4, 9, B, None) == UNALIGNED
+    assert g(A, 0, 8, B, None) == OK
+
+
+def test_gemv_validation(L):
+    f = L.bitnet_w2a8_gemv
+    assert f(None, B, C, D, 1, 16, 256, E, 0, None) == INVALID
+    assert f(A, B, C, D, 1, 16, 256, None, 0, None) == INVALID
+    assert f(A, B, C, D, 17, 16, 256, E, 0, None) == INVALID  # M above the GEMV limit
+    assert f(A, B, C, D, 1, 16, 256, E, 3, None) == INVALID   # bad dtype
+    assert f(A, B, C, D, 1, 16, 254, E, 0, None) == UNALIGNED
+    assert f(A, B, C + 4, D, 1, 16, 256, E, 0, None) == UNALIGNED
+    assert f(A, B, C, D, 0, 16, 256, E, 0, None) == OK
+    assert f(A, B, C, D, 1, 0, 256, E, 0, None) == OK
+
+
+def test_gemm_validation(L):
+    f = L.bitnet_w2a8_gemm
+    assert f(A, B, C, D, 64, 16, 256, E, 0, 7, None, 0, None) == INVALID     # bad algo
+    assert f(A, B, C, D, 64, 16, 256, E, 0, 1, None, 0, None) == INVALID     # skinny with M > 16
+    assert f(A, B, C, D, 64, 16, 256, E, 5, 0, None, 0, None) == INVALID     # bad dtype
+    assert f(A, B, C, D, 64, 16, 256, E, 0, 0, F + 8, 16, None) == UNALIGNED
+    assert f(A, B, C, D, 64, 16, 256, E, 0, 0, None, 16, None) == INVALID    # bytes but no buffer
+    assert f(A, B, C, D, 0, 16, 256, E, 0, 2, None, 0, None) == OK
+    assert L.bitnet_w2a8_gemm_workspace_size(512, 2560, 2560) == 0
+
+
+def test_quant_gemv_validation(L):
+    f = L.bitnet_quant_gemv
+    assert f(None, B, C, 1, 16, 256, D, 0, None, None, None) == INVALID
+    assert f(A, B, C, 17, 16, 256, D, 0, None, None, None) == INVALID
+    assert f(A, B, C, 1, 16, 256, D, 0, E + 4, None, None) == UNALIGNED
+    assert f(A, B, C, 1, 16, 256, D, 0, None, F + 4, None) == UNALIGNED
+    assert f(A, B, C, 1, 16, 250, D, 0, None, None, None) == UNALIGNED
+    assert f(A, B, C, 0, 16, 256, D, 0, None, None, None) == OK
+
+
+def test_valid_call_without_gpu_reports_hip_error(L):
+    # Arguments pass validation, so the library asks HIP for the device; with no GPU in
+    # this container that fails and comes back as BITNET_ERR_HIP with the HIP message.
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    rc = L.bitnet_quant_act(A, 1, 8, B, C, None)
+    assert rc in (HIP, DEVICE)
+    if rc == HIP:
+        assert L.bitnet_last_hip_error()
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros((1, 8), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="device tensor"):
+        bw.quant_act(x)
+    with pytest.raises(ValueError, match="device tensor"):
+        bw.pack_weights(torch.zeros((4, 8)))

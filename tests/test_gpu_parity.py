@@ -1,0 +1,212 @@
+"""GPU parity: every entry point of the C ABI against the CPU oracle on the same seeded
+inputs.  Integer results (int8 codes, packed bytes, int32 accumulators) and the fp32
+scales must be bit-exact; fp32 outputs within 1e-6 relative of the exact value; bf16
+outputs within 1 ulp of the round-to-nearest-even of the exact value.
+
+Inputs for a kernel under test come from the generators or from the oracle, never from
+another HIP kernel, so each kernel is checked on its own; the chained tests then check
+the whole path.  Run on an MI355X: pytest -m gpu.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import ternary_weight_linear_token_amd as bw
+import workloads
+from gpu_helpers import Problem, check_out, to_np
+
+pytestmark = pytest.mark.gpu
+
+DT = ["f32", "bf16", "i32"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    torch.cuda.set_device(0)
+    yield
+    torch.cuda.synchronize()
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+# ------------------------------------------------------------- activation quant
+
+
+@pytest.mark.parametrize("M,K", [(4, 256), (1, 2560), (3, 260), (5, 4), (2, 28672), (7, 1028),
+                                 (512, 2560), (64, 14336), (1, 8196), (3, 32772)])
+def test_quant_act_matches_oracle(M, K):
+    X = workloads.activations(M, K, seed=M * 7 + K)
+    xq_ref, a_ref = oracle.act_quant(workloads.bf16_bits(X))
+    xq, a = bw.quant_act(X.cuda())
+    assert np.array_equal(to_np(a), a_ref)
+    assert np.array_equal(to_np(xq), xq_ref)
+
+
+def test_quant_act_special_rows():
+    K = 64
+    rows = torch.zeros((6, K), dtype=torch.float32)
+    rows[1, :8] = torch.tensor([254, 125, 5, 1, -1, -3, 0, -254])  # exact half-way ties
+    rows[2, 17] = -3.0                                            # a single nonzero
+    rows[3] = torch.linspace(-1, 1, K)
+    rows[3, 63] = 3.0e38                                          # huge maximum
+    rows[4] = 1e-30                                               # below the eps clamp
+    rows[5] = torch.arange(K) - 31.5
+    X = rows.to(torch.bfloat16)
+    xq_ref, a_ref = oracle.act_quant(workloads.bf16_bits(X))
+    xq, a = bw.quant_act(X.cuda())
+    assert np.array_equal(to_np(a), a_ref)
+    assert np.array_equal(to_np(xq), xq_ref)
+    assert to_np(xq)[1, :8].tolist() == [127, 62, 2, 0, 0, -2, 0, -127]
+
+
+# ---------------------------------------------------------------- weight packing
+
+
+@pytest.mark.parametrize("N,K", [(128, 256), (33, 260), (1, 4), (640, 2560), (2560, 6912),
+                                 (7, 28672)])
+def test_pack_matches_oracle(N, K):
+    W = workloads.latent_weights(N, K, seed=N + K)
+    p_ref, s_ref = oracle.pack_weights(W.numpy())
+    packed, scale = bw.pack_weights(W.cuda())
+    assert np.array_equal(to_np(scale), s_ref)
+    assert np.array_equal(to_np(packed), p_ref)
+    codes = bw.unpack_weights(packed, K)
+    assert np.array_equal(to_np(codes), oracle.unpack(p_ref, K))
+
+
+def test_pack_special_rows():
+    W = torch.zeros((5, 16))
+    W[1] = 0.25
+    W[2, :4] = torch.tensor([2.0, -2.0, 0.5, -0.5])
+    W[3, :6] = torch.tensor([-0.3, 1.7, 0.0, -2.1, 0.8, -0.1])
+    W[4] = -1e-8
+    p_ref, s_ref = oracle.pack_weights(W.numpy())
+    packed, scale = bw.pack_weights(W.cuda())
+    assert np.array_equal(to_np(scale), s_ref)
+    assert np.array_equal(to_np(packed), p_ref)
+
+
+# --------------------------------------------------------- products (oracle inputs)
+
+
+def product_inputs(pb: Problem):
+    o = pb.oracle()
+    return dev(o["xq"]), dev(o["a_scale"]), dev(o["packed"]), dev(o["w_scale"]), o
+
+
+@pytest.mark.parametrize("M", [1, 2, 5, 16])
+@pytest.mark.parametrize("N,K", [(16, 256), (37, 260), (300, 1024), (129, 2816), (64, 4),
+                                 (33, 7168)])
+def test_gemv_matches_oracle(M, N, K):
+    pb = Problem(M, N, K, seed=M * 1000 + N + K)
+    xq, a, packed, s, o = product_inputs(pb)
+    for dt in DT:
+        out = bw.gemv(xq, a, packed, s, dt)
+        check_out(to_np(out), o["acc"], o["ref"], dt, f"gemv M={M} N={N} K={K} {dt}")
+
+
+@pytest.mark.parametrize("algo", ["tiled", "auto"])
+@pytest.mark.parametrize("M", [1, 16, 17, 130, 300])
+@pytest.mark.parametrize("N,K", [(64, 64), (200, 256), (130, 1000), (257, 320), (96, 2560)])
+def test_gemm_matches_oracle(algo, M, N, K):
+    pb = Problem(M, N, K, seed=M * 3000 + N + K)
+    xq, a, packed, s, o = product_inputs(pb)
+    for dt in DT:
+        out = bw.gemm(xq, a, packed, s, dt, algo=algo)
+        check_out(to_np(out), o["acc"], o["ref"], dt, f"gemm {algo} M={M} N={N} K={K} {dt}")
+
+
+@pytest.mark.parametrize("M", [1, 3, 16])
+@pytest.mark.parametrize("N,K", [(16, 256), (300, 1024), (37, 260), (50, 6912)])
+def test_quant_gemv_matches_oracle(M, N, K):
+    pb = Problem(M, N, K, seed=M * 5000 + N + K)
+    o = pb.oracle()
+    packed, s = dev(o["packed"]), dev(o["w_scale"])
+    for dt in DT:
+        out, xq, a = bw.quant_gemv(pb.x_dev, packed, s, dt, return_quant=True)
+        assert np.array_equal(to_np(a), o["a_scale"])
+        assert np.array_equal(to_np(xq), o["xq"])
+        check_out(to_np(out), o["acc"], o["ref"], dt, f"quant_gemv M={M} N={N} K={K} {dt}")
+
+
+def test_extreme_accumulators():
+    # every activation at +-127 and every weight +1 / -1: |acc| = 127 K, the largest sums
+    M, N, K = 3, 40, 28672
+    xq = np.full((M, K), 127, np.int8)
+    xq[1] = -127
+    xq[2, ::2] = -127
+    q = np.ones((N, K), np.int8)
+    q[1::2] = -1
+    packed = oracle.pack(q)
+    a = np.full((M,), 1.0, np.float32)
+    s = np.linspace(0.5, 2.0, N).astype(np.float32)
+    acc = oracle.accumulate(xq, packed, K)
+    ref, _, _ = oracle.rescale(acc, a, s)
+    for algo in ("skinny", "tiled"):
+        for dt in DT:
+            out = bw.gemm(dev(xq), dev(a), dev(packed), dev(s), dt, algo=algo)
+            check_out(to_np(out), acc, ref, dt, f"extreme {algo} {dt}")
+
+
+def test_zero_rows_and_zero_weights():
+    M, N, K = 4, 48, 512
+    X = workloads.activations(M, K, seed=1)
+    X[2] = 0
+    W = workloads.latent_weights(N, K, seed=2)
+    W[5] = 0
+    W[17] = 1e-9
+    pb = Problem(M, N, K, X=X, W=W)
+    o = pb.oracle()
+    packed, s = dev(o["packed"]), dev(o["w_scale"])
+    for dt in DT:
+        out = bw.quant_gemv(pb.x_dev, packed, s, dt)
+        check_out(to_np(out), o["acc"], o["ref"], dt, f"zero rows {dt}")
+        out2 = bw.gemm(dev(o["xq"]), dev(o["a_scale"]), packed, s, dt, algo="tiled")
+        check_out(to_np(out2), o["acc"], o["ref"], dt, f"zero rows tiled {dt}")
+
+
+def test_empty_problems_are_noops():
+    xq = torch.zeros((0, 256), dtype=torch.int8, device="cuda")
+    a = torch.zeros((0,), dtype=torch.float32, device="cuda")
+    packed = torch.zeros((8, 64), dtype=torch.uint8, device="cuda")
+    s = torch.ones((8,), dtype=torch.float32, device="cuda")
+    out = bw.gemm(xq, a, packed, s, "f32")
+    assert out.shape == (0, 8)
+    out = bw.gemv(torch.zeros((1, 256), dtype=torch.int8, device="cuda"),
+                  torch.ones((1,), device="cuda"), packed[:0], s[:0], "f32")
+    assert out.shape == (1, 0)
+
+
+def test_outputs_are_deterministic():
+    pb = Problem(300, 257, 2560, seed=11)
+    xq, a, packed, s, _ = product_inputs(pb)
+    for algo in ("tiled",):
+        o1 = bw.gemm(xq, a, packed, s, "f32", algo=algo)
+        o2 = bw.gemm(xq, a, packed, s, "f32", algo=algo)
+        assert torch.equal(o1.view(torch.int32), o2.view(torch.int32))
+    x1 = bw.quant_gemv(pb.x_dev[:7], packed, s, "bf16")
+    x2 = bw.quant_gemv(pb.x_dev[:7], packed, s, "bf16")
+    assert torch.equal(x1.view(torch.int16), x2.view(torch.int16))
+
+
+# ------------------------------------------------------------ chained GPU path
+
+
+@pytest.mark.parametrize("dt", DT)
+def test_tiny_workload_chain(dt):
+    # The tiny workload end to end on the GPU: pack, quantize, product (both kernels).
+    (name, N, K), = workloads.WORKLOADS["tiny"]["layer"]
+    M = workloads.WORKLOADS["tiny"]["Ms"][0]
+    pb = Problem(M, N, K, seed=0, outliers=False)
+    o = pb.oracle()
+    packed, s = bw.pack_weights(pb.w_dev)
+    xq, a = bw.quant_act(pb.x_dev)
+    assert np.array_equal(to_np(packed), o["packed"]) and np.array_equal(to_np(s), o["w_scale"])
+    assert np.array_equal(to_np(xq), o["xq"]) and np.array_equal(to_np(a), o["a_scale"])
+    for out in (bw.gemv(xq, a, packed, s, dt), bw.gemm(xq, a, packed, s, dt, algo="tiled"),
+                bw.quant_gemv(pb.x_dev, packed, s, dt), bw.bitlinear(pb.x_dev, packed, s, dt)):
+        check_out(to_np(out), o["acc"], o["ref"], dt, f"tiny chain {dt}")
