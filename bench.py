@@ -1,0 +1,332 @@
+#!/usr/bin/env python3
+"""Benchmark of the W2A8 BitLinear hot path on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+A step is one BitNet-2B-shaped decode layer set at M = 1: the seven projections
+(q, k, v, o, gate, up, down; (N, K) = (2560,2560) (640,2560) (640,2560) (2560,2560)
+(6912,2560) (6912,2560) (2560,6912)), each one fused quant + GEMV launch (bf16
+activations in, fp32 out), i.e. every step of the path: absmax, quantize, stream and
+unpack the packed weights, int8 x ternary dot with int32 accumulation, rescale.
+
+* Inputs are resident in HBM before timing.  The packed weights are replicated into
+  enough copies to exceed 1 GiB and every step uses the next copy, so the weights come
+  from HBM rather than the 256 MB Infinity Cache.
+* Each step's seven launches are captured in a HIP graph (one graph per weight copy)
+  so host launch overhead does not pace the GPU; W warmup steps, then exactly K steps
+  between two synchronizations timed with events.
+* value = packed-weight bytes of the set / step time (GB/s).
+* roofline: the fused quant+GEMV kernel, algorithmic bytes (N*K/4 packed bytes per
+  launch) / its mean launch duration (a graph of back-to-back launches over the weight
+  copies, timed with events), against 8 TB/s; traffic from the committed rocprofv3 counter summary when it matches the
+  current kernel source.
+* gemm: the BitNet-2B-shaped prefill set at M = 512 (quant kernel + tiled int8-MFMA
+  GEMM, bf16 out), int8 TOPS against 5.0 POPS dense.
+* cpu_baseline: the CPU oracle on the host cores (test infrastructure, timed only
+  here), on the same decode step repeated for ~10 s.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+INT8_MFMA_PEAK_TOPS = 5000.0  # MI355X dense int8 matrix cores, TOPS
+ROTATE_BYTES = 1 << 30        # weight copies per rotation (> 4x the 256 MB MALL)
+METRIC = "W2A8 ternary GEMV GB/s (%HBM peak) at M=1; GEMM int8 TOPS (%MFMA) at M=512"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "quant_gemv_2b_decode_m1_traffic.txt")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--kernel-reps", type=int, default=5)
+    return ap.parse_args()
+
+
+def load_traffic(kernel_hash: str):
+    """Per-launch HBM bytes from the committed counter summary, if it still applies."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256") != kernel_hash:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path has no "
+              "multi-GPU mode in this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import ternary_weight_linear_token_amd as bw
+    from ternary_weight_linear_token_amd import build as bw_build
+    import workloads
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    bw.lib()
+    layer = workloads.LAYER_2B
+    print(f"[bench] packing {len(layer)} 2B-shaped projections", file=sys.stderr, flush=True)
+
+    packed0, scales, xs, outs = [], [], [], []
+    for name, N, K in layer:
+        W = workloads.latent_weights(N, K, seed=0).to(dev)
+        p, s = bw.pack_weights(W)
+        del W
+        packed0.append(p)
+        scales.append(s)
+        xs.append(workloads.activations(1, K, seed=0, outliers=True).to(dev))
+        outs.append(torch.empty((1, N), dtype=torch.float32, device=dev))
+    set_bytes = sum(N * K // 4 for _, N, K in layer)
+    R = max(2, math.ceil(ROTATE_BYTES / set_bytes))
+    copies = [packed0] + [[p.clone() for p in packed0] for _ in range(R - 1)]
+    torch.cuda.synchronize()
+
+    def launch_set(r):
+        for i in range(len(layer)):
+            bw.quant_gemv(xs[i], copies[r][i], scales[i], "f32", out=outs[i])
+
+    # one graph per weight copy: a step is one replay
+    graphs = []
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        launch_set(0)  # eager warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for r in range(R):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            launch_set(r)
+        graphs.append(g)
+    torch.cuda.synchronize()
+
+    # ---- timed region: W warmup steps, then exactly K steps ----
+    for i in range(args.warmup):
+        graphs[i % R].replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(args.steps):
+        graphs[(args.warmup + i) % R].replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    value = set_bytes / (ms_step * 1e-3) / 1e9
+
+    # ---- per-launch kernel durations: one graph per shape holding R back-to-back
+    # launches (one per weight copy); event time of the replay / R ----
+    per_shape_us = [graph_launch_us(torch, lambda r, i=i: bw.quant_gemv(
+        xs[i], copies[r][i], scales[i], "f32", out=outs[i]), R, args.kernel_reps)
+        for i in range(len(layer))]
+    kern_us_total = sum(per_shape_us)
+    achieved = set_bytes / (kern_us_total * 1e-6) / 1e9
+    kernel_hash = bw_build.source_hash()
+    traffic_bytes = load_traffic(kernel_hash)
+    roofline = {
+        "bound": "hbm",
+        "achieved": round(achieved, 1),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "traffic": traffic_bytes,
+        "kernel": "skinny_kernel<1,true,true> (fused quant+GEMV)",
+        "mean_launch_us": round(kern_us_total / len(layer), 3),
+        "algorithmic_bytes_per_launch": set_bytes / len(layer),
+        "per_shape_us": {name: round(us, 3) for (name, _, _), us in zip(layer, per_shape_us)},
+    }
+
+    # ---- prefill GEMM, M = 512 ----
+    gemm = bench_gemm(bw, workloads, torch, np, dev, layer, R_bytes=ROTATE_BYTES,
+                      reps=args.kernel_reps)
+
+    # ---- CPU oracle baseline ----
+    cpu = None if args.no_cpu_baseline else cpu_baseline(workloads, layer, args.cpu_seconds)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {
+            "workload": "bitnet-2b-decode-layer-set",
+            "M": 1,
+            "shapes_NK": [[N, K] for _, N, K in layer],
+            "entry": "bitnet_quant_gemv (fused quant + GEMV), fp32 out, HIP graph per step",
+            "packed_bytes_per_step": set_bytes,
+            "weight_copies_rotated": R,
+            "frac_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        },
+        "roofline": roofline,
+        "gemm": gemm,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+def graph_launch_us(torch, launch, R, reps):
+    """Mean duration (us) of one launch: R launches (weight copies 0..R-1) captured in a
+    graph and replayed back to back, timed with events on the launching stream."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        launch(0)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for r in range(R):
+            launch(r)
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) * 1e3 / (reps * R)
+
+
+def bench_gemm(bw, workloads, torch, np, dev, layer, R_bytes, reps):
+    M = 512
+    print(f"[bench] prefill M={M}", file=sys.stderr, flush=True)
+    packed0, scales, xs, xqs, avs, outs = [], [], [], [], [], []
+    for name, N, K in layer:
+        W = workloads.latent_weights(N, K, seed=0).to(dev)
+        p, s = bw.pack_weights(W)
+        del W
+        packed0.append(p)
+        scales.append(s)
+        x = workloads.activations(M, K, seed=0, outliers=True).to(dev)
+        xs.append(x)
+        xq, a = bw.quant_act(x)
+        xqs.append(xq)
+        avs.append(a)
+        outs.append(torch.empty((M, N), dtype=torch.bfloat16, device=dev))
+    set_bytes = sum(N * K // 4 for _, N, K in layer)
+    R = max(2, math.ceil(R_bytes / set_bytes))
+    copies = [packed0] + [[p.clone() for p in packed0] for _ in range(R - 1)]
+    ops = sum(2.0 * M * N * K for _, N, K in layer)
+
+    def step(r):
+        for i in range(len(layer)):
+            bw.quant_act(xs[i], xq=xqs[i], a_scale=avs[i])
+            bw.gemm(xqs[i], avs[i], copies[r][i], scales[i], "bf16", out=outs[i])
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(0)
+    torch.cuda.current_stream().wait_stream(side)
+    graphs = []
+    for r in range(R):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(r)
+        graphs.append(g)
+    for r in range(3):
+        graphs[r % R].replay()
+    torch.cuda.synchronize()
+    steps = 40
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        graphs[i % R].replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / steps
+
+    per_shape_us = [graph_launch_us(torch, lambda r, i=i: bw.gemm(
+        xqs[i], avs[i], copies[r][i], scales[i], "bf16", out=outs[i]), R, reps)
+        for i in range(len(layer))]
+    tops = ops / (sum(per_shape_us) * 1e-6) / 1e12
+    return {
+        "metric": "GEMM int8 TOPS at M=512 (prefill layer set, bf16 out)",
+        "workload": "bitnet-2b-prefill-layer-set",
+        "value": round(tops, 2),
+        "unit": "TOPS",
+        "step_tops_incl_quant": round(ops / (ms_step * 1e-3) / 1e12, 2),
+        "ms_per_step_incl_quant": round(ms_step, 4),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(tops, 2),
+            "peak": INT8_MFMA_PEAK_TOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tops / INT8_MFMA_PEAK_TOPS, 4),
+            "traffic": None,
+            "kernel": "tiled_kernel<128,128,true>",
+            "per_shape_us": {name: round(us, 3) for (name, _, _), us in zip(layer, per_shape_us)},
+        },
+    }
+
+
+def cpu_baseline(workloads, layer, seconds):
+    """The CPU oracle on the decode step (act quant + accumulate + rescale per shape)."""
+    import oracle
+    print(f"[bench] cpu oracle baseline (~{seconds:.0f} s)", file=sys.stderr, flush=True)
+    prep = []
+    for name, N, K in layer:
+        packed, w_scale = oracle.pack_weights(workloads.latent_weights(N, K, seed=0).numpy())
+        xb = workloads.bf16_bits(workloads.activations(1, K, seed=0, outliers=True))
+        prep.append((packed, w_scale, xb, K))
+    set_bytes = sum(N * K // 4 for _, N, K in layer)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        for packed, w_scale, xb, K in prep:
+            xq, a = oracle.act_quant(xb)
+            acc = oracle.accumulate(xq, packed, K)
+            oracle.rescale(acc, a, w_scale)
+        n += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {
+        "value": round(set_bytes * n / dt / 1e9, 3),
+        "unit": "GB/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"2B decode layer set at M=1 (act quant + accumulate + rescale, pack "
+                  f"excluded), {n} passes in {dt:.1f} s",
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -64,7 +64,86 @@ __device__ __forceinline__ uint4 load_w16(const uint8_t* __restrict__ packed, in
     return make_uint4(d[0], d[1], d[2], d[3]);
 }
 
-template <int NG, bool FUSED, bool ALIGNED>
+// Quantize 16 bf16 values (h: 8 words, 2 values each, low half first) with scale a into
+// 16 int8 codes d[0..3] (value j in byte j%4 of d[j/4]).
+__device__ __forceinline__ void quant16(const uint32_t h[8], float a, uint32_t d[4]) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const uint32_t hw = h[2 * b + (t >> 1)];
+            const uint32_t bits = (t & 1) ? (hw >> 16) : (hw & 0xFFFFu);
+            float r = rintf(bf16_bits_to_f32(bits) * a);
+            r = fminf(fmaxf(r, -127.0f), 127.0f);
+            word |= ((uint32_t)(int)r & 0xFFu) << (8 * t);
+        }
+        d[b] = word;
+    }
+}
+
+// Load 16 bf16 activations x[m][k0 .. k0+15] (zeros past K) as 8 words.
+template <bool ALIGNED>
+__device__ __forceinline__ void load_x16_bf16(const uint16_t* __restrict__ xb, int K, int m,
+                                              int k0, uint32_t h[8]) {
+    const uint16_t* src = xb + (int64_t)m * K + k0;
+    if (ALIGNED) {
+        const uint4 v0 = reinterpret_cast<const uint4*>(src)[0];
+        const uint4 v1 = reinterpret_cast<const uint4*>(src)[1];
+        h[0] = v0.x; h[1] = v0.y; h[2] = v0.z; h[3] = v0.w;
+        h[4] = v1.x; h[5] = v1.y; h[6] = v1.z; h[7] = v1.w;
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t lo = (k0 + 2 * j < K) ? src[2 * j] : 0u;
+            const uint32_t hi = (k0 + 2 * j + 1 < K) ? src[2 * j + 1] : 0u;
+            h[j] = lo | (hi << 16);
+        }
+    }
+}
+
+__device__ __forceinline__ uint32_t absmax_bits16(const uint32_t h[8]) {
+    uint32_t mx = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t a = h[j] & 0x7FFF7FFFu;
+        mx = max(mx, max(a & 0xFFFFu, a >> 16));
+    }
+    return mx;
+}
+
+// One 16-element group of activations, quantized (d), into the permuted LDS layout;
+// also adds its code sum to s_rowsum[m] and (block 0, if requested) writes the codes.
+template <bool ALIGNED>
+__device__ __forceinline__ void put_group(unsigned char* x_lds, int KSP, int* s_rowsum, int m,
+                                          int u, const uint32_t d[4]) {
+    const int rs = sum_i8x4(d[0], sum_i8x4(d[1], sum_i8x4(d[2], sum_i8x4(d[3], 0))));
+    atomicAdd(&s_rowsum[m], rs);
+    uint32_t e[4];
+    transpose4x4_bytes(d, e);
+    unsigned char* dst = x_lds + m * KSP + (u >> 2) * 64 + 4 * (u & 3);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint32_t*>(dst + 16 * i) = e[i];
+}
+
+template <bool ALIGNED>
+__device__ __forceinline__ void store_codes16(int8_t* xq_out, int K, int m, int k0,
+                                              const uint32_t d[4]) {
+    int8_t* dst = xq_out + (int64_t)m * K + k0;
+    if (ALIGNED) {
+        *reinterpret_cast<uint4*>(dst) = make_uint4(d[0], d[1], d[2], d[3]);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+            if (k0 + j < K) dst[j] = (int8_t)(d[j >> 2] >> (8 * (j & 3)));
+    }
+}
+
+constexpr int kU = 4;  // 256-weight chunks per wave per batch (loads in flight per lane)
+
+// XREG > 0: the block's activation groups (at most XREG per thread, single K stage) stay
+// in registers between the max pass and the quantization pass.
+template <int NG, bool FUSED, bool ALIGNED, int XREG>
 __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
     extern __shared__ __align__(16) unsigned char smem[];
     const int KSP = p.KS + 16;  // padded LDS row stride: spreads rows over the banks
@@ -79,6 +158,69 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t row_bytes = K / 4;
     const int n0 = blockIdx.x * (16 * NG);
+    const int mrow = lane & 15;  // operand-A row (token) and operand-B column of this lane
+    const int q = lane >> 4;     // k-group of this lane inside a 256-weight chunk
+    const bool a_active = mrow < M;
+
+    // weights of chunks c0 + 4*uu (uu < kU) of the stage starting at byte stage_off
+    auto load_batch = [&](uint4 (&w)[kU][NG], int c0, int nch, int64_t stage_off) {
+#pragma unroll
+        for (int uu = 0; uu < kU; ++uu) {
+            const int c = c0 + kSkWaves * uu;
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                const int n = n0 + 16 * g + mrow;
+                w[uu][g] = (c < nch && n < N)
+                               ? load_w16<ALIGNED>(p.packed, row_bytes, n, stage_off + c * 64 + 16 * q)
+                               : make_uint4(0u, 0u, 0u, 0u);
+            }
+        }
+    };
+
+    v4i acc1[NG], acc4[NG], acc16[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) acc1[g] = acc4[g] = acc16[g] = v4i{0, 0, 0, 0};
+
+    auto compute_batch = [&](const uint4 (&w)[kU][NG], int c0, int nch) {
+#pragma unroll
+        for (int uu = 0; uu < kU; ++uu) {
+            const int c = c0 + kSkWaves * uu;
+            if (c >= nch) break;
+            v4i A[4];
+            if (a_active) {
+                const unsigned char* src = x_lds + mrow * KSP + (c * 4 + q) * 64;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) A[i] = *reinterpret_cast<const v4i*>(src + 16 * i);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) A[i] = v4i{0, 0, 0, 0};
+            }
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                const uint32_t w4[4] = {w[uu][g].x, w[uu][g].y, w[uu][g].z, w[uu][g].w};
+                v4i b0, b1, b2, b3;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    b0[r] = (int)(w4[r] & 0x03030303u);
+                    b1[r] = (int)(w4[r] & 0x0C0C0C0Cu);
+                    b2[r] = (int)(w4[r] & 0x30303030u);
+                    b3[r] = (int)((w4[r] >> 2) & 0x30303030u);
+                }
+                acc1[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[0], b0, acc1[g], 0, 0, 0);
+                acc4[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[1], b1, acc4[g], 0, 0, 0);
+                acc16[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2], b2, acc16[g], 0, 0, 0);
+                acc16[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[3], b3, acc16[g], 0, 0, 0);
+            }
+        }
+    };
+
+    // The first weight batch is requested before anything else, so its memory latency
+    // overlaps the activation phases below.
+    uint4 cur[kU][NG], nxt[kU][NG];
+    {
+        const int len0 = min(p.KS, p.Kp);
+        load_batch(cur, wave, len0 >> 8, 0);
+    }
 
     if (tid < 16) {
         s_amax[tid] = 0u;
@@ -86,19 +228,53 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
     }
     __syncthreads();
 
+    uint32_t held[XREG > 0 ? XREG : 1][8];
     if constexpr (FUSED) {
-        // max |x| per token: integer max of the bf16 magnitude bits, 4 elements per load
-        const int64_t groups = K / 4;
-        for (int m = 0; m < M; ++m) {
-            const uint2* row = reinterpret_cast<const uint2*>(p.xb + (int64_t)m * K);
-            uint32_t mx = 0;
-            for (int64_t g = tid; g < groups; g += kSkThreads) {
-                uint2 v = row[g];
-                uint32_t a = v.x & 0x7FFF7FFFu, b = v.y & 0x7FFF7FFFu;
-                mx = max(mx, max(max(a & 0xFFFFu, a >> 16), max(b & 0xFFFFu, b >> 16)));
+        if constexpr (XREG > 0) {
+            const int gpr = p.Kp >> 4;
+#pragma unroll
+            for (int t = 0; t < XREG; ++t) {
+                const int gi = tid + t * kSkThreads;
+                if (gi < M * gpr) {
+                    const int m = gi / gpr, u = gi - m * gpr;
+                    load_x16_bf16<ALIGNED>(p.xb, K, m, 16 * u, held[t]);
+                }
             }
-            mx = wave_max_u32(mx);
-            if (lane == 0) atomicMax(&s_amax[m], mx);
+            uint32_t mx = 0;
+            int mcur = -1;
+#pragma unroll
+            for (int t = 0; t < XREG; ++t) {
+                const int gi = tid + t * kSkThreads;
+                if (gi < M * gpr) {
+                    const int m = gi / gpr;
+                    if (m != mcur && mcur >= 0) {
+                        atomicMax(&s_amax[mcur], mx);
+                        mx = 0;
+                    }
+                    mcur = m;
+                    mx = max(mx, absmax_bits16(held[t]));
+                }
+            }
+            if (M == 1) {
+                mx = wave_max_u32(mx);
+                if (lane == 0) atomicMax(&s_amax[0], mx);
+            } else if (mcur >= 0) {
+                atomicMax(&s_amax[mcur], mx);
+            }
+        } else {
+            // max |x| per token over the whole row, 4 elements per load
+            const int64_t groups = K / 4;
+            for (int m = 0; m < M; ++m) {
+                const uint2* row = reinterpret_cast<const uint2*>(p.xb + (int64_t)m * K);
+                uint32_t mx = 0;
+                for (int64_t g = tid; g < groups; g += kSkThreads) {
+                    const uint2 v = row[g];
+                    const uint32_t a = v.x & 0x7FFF7FFFu, b = v.y & 0x7FFF7FFFu;
+                    mx = max(mx, max(max(a & 0xFFFFu, a >> 16), max(b & 0xFFFFu, b >> 16)));
+                }
+                mx = wave_max_u32(mx);
+                if (lane == 0) atomicMax(&s_amax[m], mx);
+            }
         }
         __syncthreads();
     }
@@ -116,133 +292,64 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
         s_inva[tid] = 1.0f / a;
     }
 
-    v4i acc1[NG], acc4[NG], acc16[NG];
-#pragma unroll
-    for (int g = 0; g < NG; ++g) acc1[g] = acc4[g] = acc16[g] = v4i{0, 0, 0, 0};
-
-    const int mrow = lane & 15;  // operand-A row (token) and operand-B column of this lane
-    const int q = lane >> 4;     // k-group of this lane inside a 256-weight chunk
-    const bool a_active = mrow < M;
-
     for (int ks = 0; ks < p.Kp; ks += p.KS) {
         const int len = min(p.KS, p.Kp - ks);
-        __syncthreads();  // previous stage fully consumed; s_a visible
+        const int nch = len >> 8;
+        const int64_t stage_off = ks >> 2;
+        if (ks > 0) load_batch(cur, wave, nch, stage_off);
+        __syncthreads();  // previous stage consumed; s_a visible
 
         // ---- stage activations [ks, ks+len) of all M rows into LDS, permuted ----
         const int gpr = len >> 4;  // 16-element groups per row
-        for (int gi = tid; gi < M * gpr; gi += kSkThreads) {
-            const int m = gi / gpr, u = gi - m * gpr;
-            const int k0 = ks + 16 * u;
-            uint32_t d[4];
-            if constexpr (FUSED) {
-                const uint16_t* src = p.xb + (int64_t)m * K + k0;
-                uint32_t h[8];
-                if (ALIGNED) {
-                    const uint4 v0 = reinterpret_cast<const uint4*>(src)[0];
-                    const uint4 v1 = reinterpret_cast<const uint4*>(src)[1];
-                    h[0] = v0.x; h[1] = v0.y; h[2] = v0.z; h[3] = v0.w;
-                    h[4] = v1.x; h[5] = v1.y; h[6] = v1.z; h[7] = v1.w;
-                } else {
+        if (FUSED && XREG > 0) {
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        uint32_t lo = (k0 + 2 * j < K) ? src[2 * j] : 0u;
-                        uint32_t hi = (k0 + 2 * j + 1 < K) ? src[2 * j + 1] : 0u;
-                        h[j] = lo | (hi << 16);
-                    }
-                }
-                const float a = s_a[m];
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    uint32_t word = 0;
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        const uint32_t bits = (t & 1) ? (h[2 * b + (t >> 1)] >> 16)
-                                                      : (h[2 * b + (t >> 1)] & 0xFFFFu);
-                        float r = rintf(bf16_bits_to_f32(bits) * a);
-                        r = fminf(fmaxf(r, -127.0f), 127.0f);
-                        word |= ((uint32_t)(int)r & 0xFFu) << (8 * t);
-                    }
-                    d[b] = word;
-                }
-                if (blockIdx.x == 0 && p.xq_out) {
-                    int8_t* dst = p.xq_out + (int64_t)m * K + k0;
-                    if (ALIGNED) {
-                        *reinterpret_cast<uint4*>(dst) = make_uint4(d[0], d[1], d[2], d[3]);
-                    } else {
-#pragma unroll
-                        for (int j = 0; j < 16; ++j)
-                            if (k0 + j < K) dst[j] = (int8_t)(d[j >> 2] >> (8 * (j & 3)));
-                    }
-                }
-            } else {
-                const int8_t* src = p.xq + (int64_t)m * K + k0;
-                if (ALIGNED) {
-                    const uint4 v = *reinterpret_cast<const uint4*>(src);
-                    d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
-                } else {
-                    d[0] = d[1] = d[2] = d[3] = 0u;
-#pragma unroll
-                    for (int j = 0; j < 16; ++j)
-                        if (k0 + j < K) d[j >> 2] |= (uint32_t)(uint8_t)src[j] << (8 * (j & 3));
+            for (int t = 0; t < (XREG > 0 ? XREG : 1); ++t) {
+                const int gi = tid + t * kSkThreads;
+                if (gi < M * gpr) {
+                    const int m = gi / gpr, u = gi - m * gpr;
+                    uint32_t d[4];
+                    quant16(held[t], s_a[m], d);
+                    if (blockIdx.x == 0 && p.xq_out) store_codes16<ALIGNED>(p.xq_out, K, m, 16 * u, d);
+                    put_group<ALIGNED>(x_lds, KSP, s_rowsum, m, u, d);
                 }
             }
-            const int rs = sum_i8x4(d[0], sum_i8x4(d[1], sum_i8x4(d[2], sum_i8x4(d[3], 0))));
-            atomicAdd(&s_rowsum[m], rs);
-            uint32_t e[4];
-            transpose4x4_bytes(d, e);
-            unsigned char* dst = x_lds + m * KSP + (u >> 2) * 64 + 4 * (u & 3);
+        } else {
+            for (int gi = tid; gi < M * gpr; gi += kSkThreads) {
+                const int m = gi / gpr, u = gi - m * gpr;
+                const int k0 = ks + 16 * u;
+                uint32_t d[4];
+                if constexpr (FUSED) {
+                    uint32_t h[8];
+                    load_x16_bf16<ALIGNED>(p.xb, K, m, k0, h);
+                    quant16(h, s_a[m], d);
+                    if (blockIdx.x == 0 && p.xq_out) store_codes16<ALIGNED>(p.xq_out, K, m, k0, d);
+                } else {
+                    const int8_t* src = p.xq + (int64_t)m * K + k0;
+                    if (ALIGNED) {
+                        const uint4 v = *reinterpret_cast<const uint4*>(src);
+                        d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+                    } else {
+                        d[0] = d[1] = d[2] = d[3] = 0u;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) *reinterpret_cast<uint32_t*>(dst + 16 * i) = e[i];
+                        for (int j = 0; j < 16; ++j)
+                            if (k0 + j < K) d[j >> 2] |= (uint32_t)(uint8_t)src[j] << (8 * (j & 3));
+                    }
+                }
+                put_group<ALIGNED>(x_lds, KSP, s_rowsum, m, u, d);
+            }
         }
         __syncthreads();
 
-        // ---- stream the packed weights of this stage ----
-        const int nch = len >> 8;
-        const int64_t stage_off = ks >> 2;
-        constexpr int U = 4;  // chunks in flight per wave
-        for (int c0 = wave; c0 < nch; c0 += kSkWaves * U) {
-            uint4 wv[U][NG];
+        // ---- stream the packed weights of this stage: two register batches in flight ----
+        for (int c0 = wave; c0 < nch; c0 += kSkWaves * kU) {
+            const int c1 = c0 + kSkWaves * kU;
+            if (c1 < nch) load_batch(nxt, c1, nch, stage_off);
+            compute_batch(cur, c0, nch);
+            if (c1 < nch) {
 #pragma unroll
-            for (int uu = 0; uu < U; ++uu) {
-                const int c = c0 + kSkWaves * uu;
+                for (int uu = 0; uu < kU; ++uu)
 #pragma unroll
-                for (int g = 0; g < NG; ++g) {
-                    const int n = n0 + 16 * g + mrow;
-                    wv[uu][g] = (c < nch && n < N)
-                                    ? load_w16<ALIGNED>(p.packed, row_bytes, n,
-                                                        stage_off + c * 64 + 16 * q)
-                                    : make_uint4(0u, 0u, 0u, 0u);
-                }
-            }
-#pragma unroll
-            for (int uu = 0; uu < U; ++uu) {
-                const int c = c0 + kSkWaves * uu;
-                if (c >= nch) break;
-                v4i A[4];
-                if (a_active) {
-                    const unsigned char* src = x_lds + mrow * KSP + (c * 4 + q) * 64;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) A[i] = *reinterpret_cast<const v4i*>(src + 16 * i);
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) A[i] = v4i{0, 0, 0, 0};
-                }
-#pragma unroll
-                for (int g = 0; g < NG; ++g) {
-                    const uint32_t w4[4] = {wv[uu][g].x, wv[uu][g].y, wv[uu][g].z, wv[uu][g].w};
-                    v4i b0, b1, b2, b3;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        b0[r] = (int)(w4[r] & 0x03030303u);
-                        b1[r] = (int)(w4[r] & 0x0C0C0C0Cu);
-                        b2[r] = (int)(w4[r] & 0x30303030u);
-                        b3[r] = (int)((w4[r] >> 2) & 0x30303030u);
-                    }
-                    acc1[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[0], b0, acc1[g], 0, 0, 0);
-                    acc4[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[1], b1, acc4[g], 0, 0, 0);
-                    acc16[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2], b2, acc16[g], 0, 0, 0);
-                    acc16[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[3], b3, acc16[g], 0, 0, 0);
-                }
+                    for (int g = 0; g < NG; ++g) cur[uu][g] = nxt[uu][g];
             }
         }
     }
@@ -269,13 +376,15 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
     }
 }
 
-template <int NG, bool FUSED>
+template <int NG, bool FUSED, int XREG>
 hipError_t dispatch_aligned(const SkinnyArgs& a, bool aligned, dim3 grid, size_t lds,
                             hipStream_t stream) {
     if (aligned)
-        hipLaunchKernelGGL((skinny_kernel<NG, FUSED, true>), grid, dim3(kSkThreads), lds, stream, a);
+        hipLaunchKernelGGL((skinny_kernel<NG, FUSED, true, XREG>), grid, dim3(kSkThreads), lds,
+                           stream, a);
     else
-        hipLaunchKernelGGL((skinny_kernel<NG, FUSED, false>), grid, dim3(kSkThreads), lds, stream, a);
+        hipLaunchKernelGGL((skinny_kernel<NG, FUSED, false, XREG>), grid, dim3(kSkThreads), lds,
+                           stream, a);
     return hipGetLastError();
 }
 
@@ -306,8 +415,14 @@ hipError_t launch_skinny(const int8_t* xq, const float* a_scale, const uint16_t*
     const size_t lds = (size_t)M * (a.KS + 16) + kSkMisc + (size_t)kSkWaves * NG * 4 * 64 * 4;
     const dim3 grid((unsigned)((N + 16 * NG - 1) / (16 * NG)));
     const bool aligned = (K % 256) == 0;
-    if (x_bf16) return dispatch_aligned<NG, true>(a, aligned, grid, lds, stream);
-    return dispatch_aligned<NG, false>(a, aligned, grid, lds, stream);
+    if (x_bf16) {
+        // activations held in registers between the two passes when one K stage covers
+        // the row and the block's groups fit two per thread
+        const bool hold = a.KS >= a.Kp && (int64_t)M * (a.Kp / 16) <= 2 * kSkThreads;
+        if (hold) return dispatch_aligned<NG, true, 2>(a, aligned, grid, lds, stream);
+        return dispatch_aligned<NG, true, 0>(a, aligned, grid, lds, stream);
+    }
+    return dispatch_aligned<NG, false, 0>(a, aligned, grid, lds, stream);
 }
 
 }  // namespace bitnet

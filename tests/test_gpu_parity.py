@@ -210,3 +210,48 @@ def test_tiny_workload_chain(dt):
     for out in (bw.gemv(xq, a, packed, s, dt), bw.gemm(xq, a, packed, s, dt, algo="tiled"),
                 bw.quant_gemv(pb.x_dev, packed, s, dt), bw.bitlinear(pb.x_dev, packed, s, dt)):
         check_out(to_np(out), o["acc"], o["ref"], dt, f"tiny chain {dt}")
+
+
+def test_graph_replay_matches_eager():
+    # The benchmark captures launches in HIP graphs: every replay, with eager work and
+    # synchronizations in between, must reproduce the eager results bit for bit.
+    pb = Problem(1, 640, 2560, seed=3)
+    o = pb.oracle()
+    packed, s = dev(o["packed"]), dev(o["w_scale"])
+    pb2 = Problem(130, 200, 1024, seed=4)
+    o2 = pb2.oracle()
+    xq2, a2, packed2, s2 = dev(o2["xq"]), dev(o2["a_scale"]), dev(o2["packed"]), dev(o2["w_scale"])
+    out = torch.empty((1, 640), dtype=torch.float32, device="cuda")
+    out2 = torch.empty((130, 200), dtype=torch.bfloat16, device="cuda")
+    xq_g = torch.empty((1, 2560), dtype=torch.int8, device="cuda")
+    a_g = torch.empty((1,), dtype=torch.float32, device="cuda")
+
+    def work():
+        bw.quant_gemv(pb.x_dev, packed, s, "f32", out=out)
+        bw.quant_act(pb.x_dev, xq=xq_g, a_scale=a_g)
+        bw.gemm(xq2, a2, packed2, s2, "bf16", algo="tiled", out=out2)
+
+    work()
+    torch.cuda.synchronize()
+    eager = (out.clone(), xq_g.clone(), out2.clone())
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        work()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        work()
+    for rep in range(4):
+        out.zero_()
+        out2.zero_()
+        xq_g.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int32), eager[0].view(torch.int32)), rep
+        assert torch.equal(xq_g, eager[1]), rep
+        assert torch.equal(out2.view(torch.int16), eager[2].view(torch.int16)), rep
+        bw.gemm(xq2, a2, packed2, s2, "f32", algo="tiled")  # unrelated eager work
+    check_out(to_np(out), o["acc"], o["ref"], "f32", "graph replay gemv")
+    check_out(to_np(out2), o2["acc"], o2["ref"], "bf16", "graph replay gemm")
