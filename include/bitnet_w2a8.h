@@ -133,8 +133,10 @@ int bitnet_w2a8_gemv(const int8_t* xq, const float* a_scale, const uint8_t* pack
 /*
  * bitnet_w2a8_gemm -- the same product for any M >= 0 (prefill).  `algo` selects the
  * kernel (bitnet_algo); BITNET_ALGO_SKINNY with M > BITNET_SKINNY_MAX_M returns
- * BITNET_ERR_INVALID_ARG.  `workspace` / `ws_bytes` must cover
- * bitnet_w2a8_gemm_workspace_size(M, N, K) bytes (may be NULL / 0 when that is 0).
+ * BITNET_ERR_INVALID_ARG.
+ * Workspace: reserved for kernels that need device scratch.  This version needs none:
+ * bitnet_w2a8_gemm_workspace_size returns 0 and workspace may be NULL with ws_bytes 0
+ * (a larger caller buffer is accepted and left untouched).
  */
 size_t bitnet_w2a8_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
 int bitnet_w2a8_gemm(const int8_t* xq, const float* a_scale, const uint8_t* packed,

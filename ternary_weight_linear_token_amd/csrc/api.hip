@@ -130,10 +130,8 @@ int bitnet_w2a8_gemv(const int8_t* xq, const float* a_scale, const uint8_t* pack
 }
 
 size_t bitnet_w2a8_gemm_workspace_size(int64_t M, int64_t N, int64_t K) {
-    (void)M;
-    (void)N;
-    (void)K;
-    return 0;
+    if (check_shape(M, N, K) != BITNET_OK) return 0;
+    return bitnet::tiled_workspace_size(M, N, K);
 }
 
 int bitnet_w2a8_gemm(const int8_t* xq, const float* a_scale, const uint8_t* packed,
@@ -159,8 +157,8 @@ int bitnet_w2a8_gemm(const int8_t* xq, const float* a_scale, const uint8_t* pack
         return record_hip(bitnet::launch_skinny(xq, a_scale, nullptr, packed, w_scale, M, N, K,
                                                 out, out_dtype, nullptr, nullptr,
                                                 as_stream(stream)));
-    return record_hip(
-        bitnet::launch_tiled(xq, a_scale, packed, w_scale, M, N, K, out, out_dtype, as_stream(stream)));
+    return record_hip(bitnet::launch_tiled(xq, a_scale, packed, w_scale, M, N, K, out, out_dtype,
+                                           workspace, as_stream(stream)));
 }
 
 int bitnet_quant_gemv(const uint16_t* x, const uint8_t* packed, const float* w_scale,

@@ -21,9 +21,11 @@ hipError_t launch_skinny(const int8_t* xq, const float* a_scale, const uint16_t*
                          int64_t K, void* out, int out_dtype, int8_t* xq_out, float* a_out,
                          hipStream_t stream);
 
-// Tiled int8 matrix-core product for any M.
+// Tiled int8 matrix-core product for any M.  `workspace` must hold
+// tiled_workspace_size(M, N, K) bytes whose counter area is zero (it is left zero).
+size_t tiled_workspace_size(int64_t M, int64_t N, int64_t K);
 hipError_t launch_tiled(const int8_t* xq, const float* a_scale, const uint8_t* packed,
                         const float* w_scale, int64_t M, int64_t N, int64_t K, void* out,
-                        int out_dtype, hipStream_t stream);
+                        int out_dtype, void* workspace, hipStream_t stream);
 
 }  // namespace bitnet

@@ -6,16 +6,35 @@
 // dense contraction, so it runs on v_mfma_i32_32x32x32_i8.
 //
 // Design:
-//  * Block tile BM x BN x 64 (k), four wave64s in a 2 x 2 grid, each a (BM/2) x (BN/2)
-//    tile of 32x32 accumulator blocks.  Double-buffered LDS, one barrier per k-step;
-//    the next k-step's global loads are in flight while the current one computes.
-//  * Operand A (activations) is staged in LDS with every aligned 16-byte group of k
-//    transposed as a 4x4 byte matrix (position 4 r + b holds k = 4 b + r), rows padded
-//    to 80 bytes so the 128-bit fragment reads do not collide in the LDS banks.
-//  * Operand B stays packed in LDS (4x fewer bytes than int8).  A lane reads 8 packed
-//    bytes (32 weights) and unpacks them in registers: field i of each byte is masked
-//    out and mapped through a v_perm byte lookup to the signed int8 weight (c - 1), so
-//    register i, byte b holds weight k = 4 b + i -- the same k-order as operand A.
+//  * Block tile BM x BN, k-stage BK = 64, four wave64s in a 2 x 2 grid, each a
+//    (BM/2) x (BN/2) tile of 32x32 int32 accumulator blocks (tall wave tiles amortize
+//    the weight unpack over more rows).
+//  * Loads are raw buffer loads through per-block descriptors whose range ends at the
+//    last valid row: rows past M or N read as zero without any branch, and per-stage
+//    offsets are scalar, so address arithmetic stays off the vector ALU.
+//  * Software pipeline: two register sets hold the loads of stages kt+1 and kt+2 while
+//    stage kt computes; every pair of stages issues the same loads (past-the-end stage
+//    indices are clamped and never computed), so only the older set is waited for.
+//  * Operand A (activations) goes through LDS (double-buffered, one barrier per stage)
+//    with every aligned 16-byte k-group transposed as a 4x4 byte matrix (position
+//    4 r + b holds k = 4 b + r); rows padded to 80 bytes so the 128-bit fragment reads
+//    are conflict-free.
+//  * Operand B (packed weights, 4x fewer bytes than int8) is loaded straight into the
+//    registers of the waves that use it, 8 bytes (two 16-weight groups) per lane per
+//    32 columns, and unpacked there: field i of each byte is masked out and mapped by a
+//    v_perm byte lookup to the signed weight (c - 1), so register i, byte b holds weight
+//    k = 4 b + i -- the same k-order as operand A.
+//  * No split across blocks: handing int32 partial tiles between blocks needs
+//    device-scope release/acquire, which on this chip (one L2 per XCD) costs more than
+//    the split saves.  Small grids instead use 128x128 blocks of two four-wave k-groups
+//    (alternate k-stages, accumulators combined through LDS), so each SIMD interleaves
+//    two waves.
+//  * Blocks are mapped to work units XCD by XCD (dispatch assigns consecutive blocks to
+//    the 8 XCDs in turn), so an XCD's L2 sees consecutive tiles of the same row panel.
+#include <cstdio>
+#include <cstdlib>
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -24,9 +43,9 @@ namespace bitnet {
 namespace {
 
 constexpr int kTdThreads = 256;
-constexpr int kBK = 64;           // k per LDS stage
+constexpr int kBK = 64;             // k per LDS stage
 constexpr int kAStride = kBK + 16;  // padded A row in LDS (bytes)
-constexpr int kBStride = kBK / 4;   // packed B row in LDS (bytes)
+constexpr int kXcds = 8;
 
 struct TiledArgs {
     const int8_t* xq;
@@ -35,87 +54,130 @@ struct TiledArgs {
     const float* w_scale;
     void* out;
     int M, N, K;
-    int tiles_n;
+    int tiles_m, tiles_n;
+    int units;       // tiles
+    int units_per_xcd;
     int out_dtype;
 };
 
-template <int BM, int BN, bool ALIGNED>
-__global__ __launch_bounds__(kTdThreads) void tiled_kernel(TiledArgs p) {
+template <int BM, int BN, int D, int G, bool ALIGNED, int DT>
+__global__ __launch_bounds__(kTdThreads * G) void tiled_kernel(TiledArgs p) {
     constexpr int WM = BM / 2, WN = BN / 2;   // wave tile
     constexpr int MB = WM / 32, NB = WN / 32;  // 32x32 blocks per wave
-    constexpr int A_VEC = BM * (kBK / 16) / kTdThreads;  // 16-byte A loads per thread
-    static_assert(A_VEC >= 1 && BN <= kTdThreads, "tile/thread mismatch");
+    constexpr int AV = BM * (kBK / 16) / kTdThreads;  // 16-byte A loads per thread per stage
+    constexpr int BROWS_PER_THREAD = (BN + kTdThreads - 1) / kTdThreads;
+    static_assert(AV >= 1, "tile/thread mismatch");
+    (void)BROWS_PER_THREAD;
 
-    __shared__ __align__(16) unsigned char a_lds[2][BM * kAStride];
-    __shared__ __align__(16) unsigned char b_lds[2][BN * kBStride];
+    static_assert(G == 1 || G == 2, "k-groups per block");
+    __shared__ __align__(16) unsigned char a_lds_all[G][2][BM * kAStride];
+    __shared__ float s_inva[BM];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int tile_m = blockIdx.x / p.tiles_n;
-    const int tile_n = blockIdx.x - tile_m * p.tiles_n;
+    // ---- work unit of this block (XCD-contiguous) ----
+    const int xcd = blockIdx.x % kXcds;
+    const int unit = xcd * p.units_per_xcd + blockIdx.x / kXcds;
+    if (unit >= p.units) return;
+    const int tile = unit;
+    const int tile_m = tile / p.tiles_n;
+    const int tile_n = tile - tile_m * p.tiles_n;
     const int m0 = tile_m * BM, n0 = tile_n * BN;
+
+    // G groups of four waves; group g takes the k-stages g, g + G, g + 2G, ... of the
+    // block's range with its own LDS buffers and registers; their accumulators are
+    // combined through LDS at the end.  With G = 2 every SIMD holds two waves whose
+    // memory, LDS and matrix-core phases interleave.
+    const int g = (int)threadIdx.x >> 8;
+    const int tid = threadIdx.x & 255, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    unsigned char (&a_lds)[2][BM * kAStride] = a_lds_all[g];
     const int M = p.M, N = p.N, K = p.K;
     const int64_t row_bytes = K / 4;
     const int nk = (K + kBK - 1) / kBK;
+    const int kt_begin = 0;
 
-    uint4 a_reg[A_VEC];
-    uint4 b_reg;
+    for (int i = (int)threadIdx.x; i < BM; i += kTdThreads * G) {
+        const int m = m0 + i;
+        s_inva[i] = m < M ? 1.0f / p.a_scale[m] : 0.0f;
+    }
 
-    auto load_stage = [&](int kt) {
-        const int k0 = kt * kBK;
+    // Buffer descriptors of this block's A row panel and B column panel; their ranges
+    // stop at the last valid row, so loads past M or N return zeros.
+    const int rows_a = min(BM, M - m0), rows_b = min(BN, N - n0);
+    const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int8_t*>(p.xq) + (int64_t)m0 * K, (short)0, rows_a * K, 0x00020000);
+    const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(p.packed) + (int64_t)n0 * row_bytes, (short)0,
+        (int)(rows_b * row_bytes), 0x00020000);
+
+    // A: thread tid loads AV 16-byte pieces per stage (rows idx/4, k-groups idx%4).
+    // B: lane (l32, q) of wave (wm, wn) loads, for each of its NB column blocks, the 8
+    //    packed bytes k/4 = 8q .. 8q+7 of row n0 + wn*WN + 32 j + l32.
+    const int l32 = lane & 31, q = lane >> 5;
+    int a_voff[AV];
 #pragma unroll
-        for (int j = 0; j < A_VEC; ++j) {
-            const int idx = tid + j * kTdThreads;
-            const int row = idx >> 2, col = idx & 3;
-            const int m = m0 + row;
-            const int kk = k0 + 16 * col;
-            if (m < M) {
-                const int8_t* src = p.xq + (int64_t)m * K + kk;
-                if (ALIGNED) {
-                    a_reg[j] = *reinterpret_cast<const uint4*>(src);
-                } else {
-                    uint32_t d[4] = {0u, 0u, 0u, 0u};
+    for (int j = 0; j < AV; ++j) {
+        const int idx = tid + j * kTdThreads;
+        a_voff[j] = (idx >> 2) * K + 16 * (idx & 3);
+    }
+    int b_voff[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) b_voff[j] = (wn * WN + 32 * j + l32) * (int)row_bytes + 8 * q;
+
+    static_assert(D == 2 || D == 4, "pipeline depth");
+    uint4 a_reg[D][AV];
+    uint2 b_reg[D][NB];
+
+    auto load_stage = [&](uint4 (&ar)[AV], uint2 (&br)[NB], int kt) {
+        const int k0 = kt * kBK;
+        if (ALIGNED) {
+#pragma unroll
+            for (int j = 0; j < AV; ++j)
+                ar[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, a_voff[j], k0, 0));
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+                br[j] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(b_rsrc, b_voff[j], k0 / 4, 0));
+        } else {
+            // K not a multiple of 64: byte loads, zero past the end of each row
+#pragma unroll
+            for (int j = 0; j < AV; ++j) {
+                const int idx = tid + j * kTdThreads;
+                const int row = idx >> 2, kk = k0 + 16 * (idx & 3);
+                uint32_t d[4] = {0u, 0u, 0u, 0u};
+                if (row < rows_a) {
+                    const int8_t* src = p.xq + (int64_t)(m0 + row) * K + kk;
 #pragma unroll
                     for (int t = 0; t < 16; ++t)
                         if (kk + t < K) d[t >> 2] |= (uint32_t)(uint8_t)src[t] << (8 * (t & 3));
-                    a_reg[j] = make_uint4(d[0], d[1], d[2], d[3]);
                 }
-            } else {
-                a_reg[j] = make_uint4(0u, 0u, 0u, 0u);
+                ar[j] = make_uint4(d[0], d[1], d[2], d[3]);
             }
-        }
-        if (tid < BN) {
-            const int n = n0 + tid;
-            const int64_t off = (int64_t)(k0 / 4);
-            if (n < N) {
-                const uint8_t* src = p.packed + (int64_t)n * row_bytes + off;
-                if (ALIGNED) {
-                    b_reg = *reinterpret_cast<const uint4*>(src);
-                } else {
-                    uint32_t d[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-                    for (int t = 0; t < 16; ++t)
+            for (int j = 0; j < NB; ++j) {
+                const int row = wn * WN + 32 * j + l32;
+                const int64_t off = k0 / 4 + 8 * q;
+                uint32_t d[2] = {0u, 0u};
+                if (row < rows_b) {
+                    const uint8_t* src = p.packed + (int64_t)(n0 + row) * row_bytes + off;
+#pragma unroll
+                    for (int t = 0; t < 8; ++t)
                         if (off + t < row_bytes) d[t >> 2] |= (uint32_t)src[t] << (8 * (t & 3));
-                    b_reg = make_uint4(d[0], d[1], d[2], d[3]);
                 }
-            } else {
-                b_reg = make_uint4(0u, 0u, 0u, 0u);
+                br[j] = make_uint2(d[0], d[1]);
             }
         }
     };
 
-    auto store_stage = [&](int buf) {
+    auto store_stage = [&](const uint4 (&ar)[AV], int buf) {
 #pragma unroll
-        for (int j = 0; j < A_VEC; ++j) {
+        for (int j = 0; j < AV; ++j) {
             const int idx = tid + j * kTdThreads;
             const int row = idx >> 2, col = idx & 3;
-            const uint32_t d[4] = {a_reg[j].x, a_reg[j].y, a_reg[j].z, a_reg[j].w};
+            const uint32_t d[4] = {ar[j].x, ar[j].y, ar[j].z, ar[j].w};
             uint32_t e[4];
             transpose4x4_bytes(d, e);
             *reinterpret_cast<uint4*>(&a_lds[buf][row * kAStride + 16 * col]) =
                 make_uint4(e[0], e[1], e[2], e[3]);
         }
-        if (tid < BN) *reinterpret_cast<uint4*>(&b_lds[buf][tid * kBStride]) = b_reg;
     };
 
     v16i acc[MB][NB];
@@ -126,80 +188,318 @@ __global__ __launch_bounds__(kTdThreads) void tiled_kernel(TiledArgs p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
-    load_stage(0);
-    store_stage(0);
-    __syncthreads();
-
-    const int l32 = lane & 31, q = lane >> 5;
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nk) load_stage(kt + 1);
-
+    // Weight operands of one stage, unpacked: B[s][j] feeds k-substep s, column block j.
+    // Lane group q owns the 16-weight groups 2q + s of the 64-k stage.
+    auto unpack_b = [&](const uint2 (&br)[NB], v4i (&Bu)[2][NB]) {
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            // 16-weight group j = 2 q + s of this 64-k stage
-            v4i A[MB], B[NB];
-#pragma unroll
-            for (int i = 0; i < MB; ++i)
-                A[i] = *reinterpret_cast<const v4i*>(
-                    &a_lds[buf][(wm * WM + 32 * i + l32) * kAStride + 16 * (2 * q + s)]);
+        for (int s = 0; s < 2; ++s)
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
-                const uint32_t d = *reinterpret_cast<const uint32_t*>(
-                    &b_lds[buf][(wn * WN + 32 * j + l32) * kBStride + 4 * (2 * q + s)]);
-                B[j][0] = (int)ternary_field_i8<0>(d);
-                B[j][1] = (int)ternary_field_i8<1>(d);
-                B[j][2] = (int)ternary_field_i8<2>(d);
-                B[j][3] = (int)ternary_field_i8<3>(d);
+                const uint32_t d = s == 0 ? br[j].x : br[j].y;
+                Bu[s][j][0] = (int)ternary_field_i8<0>(d);
+                Bu[s][j][1] = (int)ternary_field_i8<1>(d);
+                Bu[s][j][2] = (int)ternary_field_i8<2>(d);
+                Bu[s][j][3] = (int)ternary_field_i8<3>(d);
             }
+    };
+    auto read_a = [&](int buf, v4i (&A)[2][MB]) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+                A[s][i] = *reinterpret_cast<const v4i*>(
+                    &a_lds[buf][(wm * WM + 32 * i + l32) * kAStride + 16 * (2 * q + s)]);
+    };
+    auto mfma_stage = [&](const v4i (&A)[2][MB], const v4i (&Bu)[2][NB]) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
 #pragma unroll
             for (int i = 0; i < MB; ++i)
 #pragma unroll
                 for (int j = 0; j < NB; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[i], B[j], acc[i][j], 0, 0, 0);
-        }
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[s][i], Bu[s][j], acc[i][j], 0, 0, 0);
+    };
 
-        if (kt + 1 < nk) store_stage(buf ^ 1);
+    // D register sets hold the loads of the next D stages.  Step t: read stage t's A
+    // fragments from LDS buffer t%2; while they are in flight, unpack stage t+1's weights
+    // (already in registers), refill register set t%D with the loads of stage t+D and
+    // move stage t+1's A into the other LDS buffer (last read before the previous
+    // barrier); then issue stage t's matrix products, which execute across the barrier
+    // and the next step's fragment reads.  One barrier per step.  Every full group of D
+    // steps issues the same loads (stage indices past the end are clamped and never
+    // computed), so the compiler waits only for the oldest set.  The loop runs whole
+    // groups, so the accumulators keep one live range; the remaining < D stages run in
+    // a tail without new loads.
+    // group g's stages: kt_begin + g + G*i for i < nk_g; the block runs nsteps steps
+    // (the largest nk_g) so all waves meet every barrier; a step past a group's last
+    // stage loads a clamped stage and skips its matrix products.
+    const int nk_g = nk > g ? (nk - g + G - 1) / G : 0;
+    const int nsteps = (nk + G - 1) / G;
+    const int kt_last = kt_begin + max(nk, 1) - 1;
+    auto stage_of = [&](int i) { return min(kt_begin + g + G * i, kt_last); };
+#pragma unroll
+    for (int d = 0; d < D; ++d) load_stage(a_reg[d], b_reg[d], stage_of(d));
+    store_stage(a_reg[0], 0);
+    v4i Bu[2][2][NB];
+    unpack_b(b_reg[0], Bu[0]);
+    __syncthreads();
+    int it = 0;
+    for (; it + D <= nsteps; it += D) {
+#pragma unroll
+        for (int u = 0; u < D; ++u) {
+            v4i A[2][MB];
+            read_a(u & 1, A);
+            unpack_b(b_reg[(u + 1) % D], Bu[(u + 1) & 1]);
+            load_stage(a_reg[u], b_reg[u], stage_of(it + u + D));
+            store_stage(a_reg[(u + 1) % D], (u + 1) & 1);
+            if (G == 1 || it + u < nk_g) mfma_stage(A, Bu[u & 1]);
+            __syncthreads();
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < D - 1; ++u) {
+        if (it + u >= nsteps) break;
+        v4i A[2][MB];
+        read_a(u & 1, A);
+        if (it + u + 1 < nsteps) {
+            unpack_b(b_reg[u + 1], Bu[(u + 1) & 1]);
+            store_stage(a_reg[u + 1], (u + 1) & 1);
+        }
+        if (G == 1 || it + u < nk_g) mfma_stage(A, Bu[u & 1]);
         __syncthreads();
     }
 
-    // 32x32 int32 accumulator layout: lane l, register r -> row 8*(r/4) + 4*(l/32) + r%4,
-    // column l%32.
+    // ---- epilogue: each 32x32 accumulator block goes through a per-wave LDS scratch
+    // (32 rows x 36 ints) so that a lane ends up with 16 consecutive columns of one row
+    // and stores them with 16-byte writes.  32x32 int32 accumulator layout: lane l,
+    // register r -> row 8*(r/4) + 4*(l/32) + r%4, column l%32. ----
+    constexpr int kEpiStride = 36;
+    int* scratch = reinterpret_cast<int*>(&a_lds_all[0][0][0]) + (g * 4 + wave) * (32 * kEpiStride);
+    const int erow = lane >> 1, ecol = (lane & 1) * 16;
+    const bool vec_ok = (N % 16) == 0;
+
+    auto emit_block = [&](int i, int j, const int (&v)[16]) {
 #pragma unroll
-    for (int i = 0; i < MB; ++i) {
+        for (int r = 0; r < 16; ++r) scratch[(8 * (r >> 2) + 4 * q + (r & 3)) * kEpiStride + l32] = v[r];
+        int row[16];
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            const int n = n0 + wn * WN + 32 * j + l32;
-            const float s = n < N ? p.w_scale[n] : 0.0f;
+        for (int t = 0; t < 4; ++t) {
+            const int4 x = *reinterpret_cast<const int4*>(&scratch[erow * kEpiStride + ecol + 4 * t]);
+            row[4 * t] = x.x; row[4 * t + 1] = x.y; row[4 * t + 2] = x.z; row[4 * t + 3] = x.w;
+        }
+        const int ml = wm * WM + 32 * i + erow;
+        const int m = m0 + ml;
+        const int nb = n0 + wn * WN + 32 * j + ecol;
+        if (m < M) {
+            const float inv_a = s_inva[ml];
+            const int64_t o = (int64_t)m * N + nb;
+            if (vec_ok && nb + 16 <= N) {
+                if (DT == 2) {
+                    int4* dst = reinterpret_cast<int4*>(static_cast<int*>(p.out) + o);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int m = m0 + wm * WM + 32 * i + 8 * (r >> 2) + 4 * q + (r & 3);
-                if (m < M && n < N) {
-                    const float inv_a = 1.0f / p.a_scale[m];
-                    store_out(p.out, (int64_t)m * N + n, p.out_dtype, acc[i][j][r], s, inv_a);
+                    for (int t = 0; t < 4; ++t)
+                        dst[t] = make_int4(row[4 * t], row[4 * t + 1], row[4 * t + 2], row[4 * t + 3]);
+                } else {
+                    float f[16];
+                    const float4* ws = reinterpret_cast<const float4*>(p.w_scale + nb);
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const float4 sc = ws[t];
+                        f[4 * t] = ((float)row[4 * t] * sc.x) * inv_a;
+                        f[4 * t + 1] = ((float)row[4 * t + 1] * sc.y) * inv_a;
+                        f[4 * t + 2] = ((float)row[4 * t + 2] * sc.z) * inv_a;
+                        f[4 * t + 3] = ((float)row[4 * t + 3] * sc.w) * inv_a;
+                    }
+                    if (DT == 0) {
+                        float4* dst = reinterpret_cast<float4*>(static_cast<float*>(p.out) + o);
+#pragma unroll
+                        for (int t = 0; t < 4; ++t)
+                            dst[t] = make_float4(f[4 * t], f[4 * t + 1], f[4 * t + 2], f[4 * t + 3]);
+                    } else {
+                        uint32_t h[8];
+#pragma unroll
+                        for (int t = 0; t < 8; ++t)
+                            h[t] = (uint32_t)f32_to_bf16_rne(f[2 * t]) |
+                                   ((uint32_t)f32_to_bf16_rne(f[2 * t + 1]) << 16);
+                        uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) + o);
+                        dst[0] = make_uint4(h[0], h[1], h[2], h[3]);
+                        dst[1] = make_uint4(h[4], h[5], h[6], h[7]);
+                    }
                 }
+            } else {
+#pragma unroll
+                for (int t = 0; t < 16; ++t)
+                    if (nb + t < N) store_out(p.out, o + t, DT, row[t], p.w_scale[nb + t], inv_a);
             }
         }
+        // keep consecutive blocks from being interleaved (bounds the live registers)
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // every k-stage ended with a barrier: the A buffers are free for the epilogue scratch
+    if constexpr (G == 2) {
+        // ---- combine the two groups: group 0 ends up owning accumulator rows blocks
+        // i < MB/2, group 1 the others; each half goes through LDS in its own phase ----
+        constexpr int H = MB / 2;
+        int* red = reinterpret_cast<int*>(&a_lds_all[0][0][0]);
+        auto slot = [&](int ih, int j, int r) { return (((wave * H + ih) * NB + j) * 16 + r) * 64 + lane; };
+        if (g == 1) {
+#pragma unroll
+            for (int ih = 0; ih < H; ++ih)
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) red[slot(ih, j, r)] = acc[ih][j][r];
+        }
+        __syncthreads();
+        if (g == 0) {
+#pragma unroll
+            for (int ih = 0; ih < H; ++ih)
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[ih][j][r] += red[slot(ih, j, r)];
+        }
+        __syncthreads();
+        if (g == 0) {
+#pragma unroll
+            for (int ih = 0; ih < H; ++ih)
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) red[slot(ih, j, r)] = acc[H + ih][j][r];
+        }
+        __syncthreads();
+        if (g == 1) {
+#pragma unroll
+            for (int ih = 0; ih < H; ++ih)
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[H + ih][j][r] += red[slot(ih, j, r)];
+        }
+        __syncthreads();  // red is reused as epilogue scratch below
+#pragma unroll
+        for (int ih = 0; ih < H; ++ih)
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                int v[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) v[r] = g == 0 ? acc[ih][j][r] : acc[H + ih][j][r];
+                emit_block(g == 0 ? ih : H + ih, j, v);
+            }
+        return;
     }
+
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            int v[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) v[r] = acc[i][j][r];
+            emit_block(i, j, v);
+        }
 }
 
-template <int BM, int BN>
-hipError_t launch_tile(TiledArgs a, bool aligned, hipStream_t stream) {
-    const int tiles_m = (a.M + BM - 1) / BM;
-    a.tiles_n = (a.N + BN - 1) / BN;
-    const dim3 grid((unsigned)(tiles_m * a.tiles_n));
-    if (aligned)
-        hipLaunchKernelGGL((tiled_kernel<BM, BN, true>), grid, dim3(kTdThreads), 0, stream, a);
-    else
-        hipLaunchKernelGGL((tiled_kernel<BM, BN, false>), grid, dim3(kTdThreads), 0, stream, a);
+struct TilePlan {
+    int bm, bn;
+    int tiles_m, tiles_n;
+};
+
+int device_cus() {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+            v = 256;
+        cus[dev] = v;
+    }
+    return cus[dev];
+}
+
+// Optional override for tuning: BITNET_TILED_CONFIG="bm,bn" with bm,bn one of the
+// compiled tile shapes (256,256 / 256,128 / 128,128); read once per process.
+bool config_override(int* bm, int* bn) {
+    static int cached[3] = {-1, 0, 0};
+    if (cached[0] == -1) {
+        const char* e = std::getenv("BITNET_TILED_CONFIG");
+        int a = 0, b = 0;
+        if (e && std::sscanf(e, "%d,%d", &a, &b) == 2 &&
+            ((a == 256 && b == 256) || (a == 256 && b == 128) || (a == 128 && b == 128))) {
+            cached[1] = a;
+            cached[2] = b;
+            cached[0] = 1;
+        } else {
+            cached[0] = 0;
+        }
+    }
+    if (cached[0] <= 0) return false;
+    *bm = cached[1];
+    *bn = cached[2];
+    return true;
+}
+
+// Tile shape: the largest block tile whose grid still covers every CU (per-CU
+// matrix-core efficiency grows with the wave tile, because the weight unpack and the
+// activation transpose are amortized over more products); otherwise 128x128 blocks with
+// two k-groups, so each SIMD interleaves two waves.
+TilePlan plan_tiles(int64_t M, int64_t N, int64_t K) {
+    (void)K;
+    const int cus = device_cus();
+    int bm = 128, bn = 128;
+    if (!config_override(&bm, &bn)) {
+        const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
+        const int64_t t256x128 = ((M + 255) / 256) * ((N + 127) / 128);
+        if (t256 >= cus) {
+            bm = 256;
+            bn = 256;
+        } else if (t256x128 >= cus) {
+            bm = 256;
+            bn = 128;
+        }
+    }
+    TilePlan t;
+    t.bm = bm;
+    t.bn = bn;
+    t.tiles_m = (int)((M + bm - 1) / bm);
+    t.tiles_n = (int)((N + bn - 1) / bn);
+    return t;
+}
+
+template <int BM, int BN, int D, int G>
+hipError_t launch_plan(TiledArgs a, const TilePlan& t, bool aligned, hipStream_t stream) {
+    a.tiles_m = t.tiles_m;
+    a.tiles_n = t.tiles_n;
+    a.units = t.tiles_m * t.tiles_n;
+    a.units_per_xcd = (a.units + kXcds - 1) / kXcds;
+    const dim3 grid((unsigned)(a.units_per_xcd * kXcds));
+    const dim3 blk(kTdThreads * G);
+    switch (a.out_dtype * 2 + (aligned ? 1 : 0)) {
+        case 0: hipLaunchKernelGGL((tiled_kernel<BM, BN, D, G, false, 0>), grid, blk, 0, stream, a); break;
+        case 1: hipLaunchKernelGGL((tiled_kernel<BM, BN, D, G, true, 0>), grid, blk, 0, stream, a); break;
+        case 2: hipLaunchKernelGGL((tiled_kernel<BM, BN, D, G, false, 1>), grid, blk, 0, stream, a); break;
+        case 3: hipLaunchKernelGGL((tiled_kernel<BM, BN, D, G, true, 1>), grid, blk, 0, stream, a); break;
+        case 4: hipLaunchKernelGGL((tiled_kernel<BM, BN, D, G, false, 2>), grid, blk, 0, stream, a); break;
+        default: hipLaunchKernelGGL((tiled_kernel<BM, BN, D, G, true, 2>), grid, blk, 0, stream, a); break;
+    }
     return hipGetLastError();
 }
 
 }  // namespace
 
+size_t tiled_workspace_size(int64_t M, int64_t N, int64_t K) {
+    (void)M;
+    (void)N;
+    (void)K;
+    return 0;
+}
+
 hipError_t launch_tiled(const int8_t* xq, const float* a_scale, const uint8_t* packed,
                         const float* w_scale, int64_t M, int64_t N, int64_t K, void* out,
-                        int out_dtype, hipStream_t stream) {
+                        int out_dtype, void* workspace, hipStream_t stream) {
     TiledArgs a;
     a.xq = xq;
     a.a_scale = a_scale;
@@ -209,10 +509,13 @@ hipError_t launch_tiled(const int8_t* xq, const float* a_scale, const uint8_t* p
     a.M = (int)M;
     a.N = (int)N;
     a.K = (int)K;
-    a.tiles_n = 0;
     a.out_dtype = out_dtype;
     const bool aligned = (K % kBK) == 0;
-    return launch_tile<128, 128>(a, aligned, stream);
+    (void)workspace;
+    const TilePlan t = plan_tiles(M, N, K);
+    if (t.bm == 256 && t.bn == 256) return launch_plan<256, 256, 2, 1>(a, t, aligned, stream);
+    if (t.bm == 256) return launch_plan<256, 128, 4, 1>(a, t, aligned, stream);
+    return launch_plan<128, 128, 4, 2>(a, t, aligned, stream);
 }
 
 }  // namespace bitnet

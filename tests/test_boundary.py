@@ -111,8 +111,10 @@ def test_gemm_validation(L):
     assert f(A, B, C, D, 64, 16, 256, E, 0, 0, F + 8, 16, None) == UNALIGNED
     assert f(A, B, C, D, 64, 16, 256, E, 0, 0, None, 16, None) == INVALID    # bytes but no buffer
     assert f(A, B, C, D, 0, 16, 256, E, 0, 2, None, 0, None) == OK
+    # no kernel of this version needs device scratch
     assert L.bitnet_w2a8_gemm_workspace_size(512, 2560, 2560) == 0
-
+    assert L.bitnet_w2a8_gemm_workspace_size(4096, 28672, 8192) == 0
+    assert L.bitnet_w2a8_gemm_workspace_size(-1, 16, 256) == 0
 
 def test_quant_gemv_validation(L):
     f = L.bitnet_quant_gemv

@@ -255,3 +255,19 @@ def test_graph_replay_matches_eager():
         bw.gemm(xq2, a2, packed2, s2, "f32", algo="tiled")  # unrelated eager work
     check_out(to_np(out), o["acc"], o["ref"], "f32", "graph replay gemv")
     check_out(to_np(out2), o2["acc"], o2["ref"], "bf16", "graph replay gemm")
+
+
+def test_gemm_small_and_large_tile_grids_with_caller_workspace():
+    # Shapes that select each tile configuration (128x128 with two k-groups, 256x128,
+    # 256x256), including grids far smaller than the CU count and ragged edges; a caller
+    # workspace is accepted and left untouched.
+    ws = torch.full((1 << 20,), 0x5A, dtype=torch.uint8, device="cuda")
+    for (M, N, K) in [(300, 257, 2560), (512, 2560, 2560), (130, 640, 6912), (17, 1024, 4096),
+                      (1024, 8192, 512), (600, 16384, 256), (257, 9000, 320), (520, 33000, 320)]:
+        pb = Problem(M, N, K, seed=M + N + K)
+        xq, a, packed, s, o = product_inputs(pb)
+        out = bw.gemm(xq, a, packed, s, "i32", algo="tiled", workspace=ws)
+        check_out(to_np(out), o["acc"], o["ref"], "i32", f"tiles {M}x{N}x{K}")
+        out = bw.gemm(xq, a, packed, s, "bf16", algo="tiled")
+        check_out(to_np(out), o["acc"], o["ref"], "bf16", f"tiles {M}x{N}x{K} bf16")
+    assert int((ws != 0x5A).count_nonzero()) == 0
