@@ -11,7 +11,14 @@
 // written for NVIDIA warps and dp4a, none of that is reused here):
 //  * A block (4 wave64s) owns 16 output rows and all of K.  The four waves take
 //    interleaved 256-weight chunks of K; a lane loads 16 packed bytes (64 weights) of
-//    one row per chunk, a wave 16 rows x 64 bytes, with 128-bit loads.
+//    one row per chunk, a wave 16 rows x 64 bytes, with 128-bit buffer loads.
+//  * Latency first: the scales and activations are requested, then the block's weights
+//    (all of them when a wave's share fits in U chunks, else the first of a
+//    double-buffered series of U-chunk batches), and only then does the activation
+//    quantization run, so it overlaps the weights' trip from memory.  The loads are
+//    unconditional: a chunk or row outside the problem gets an offset past the buffer
+//    resource's range, which reads as zeros, so the compiler counts the loads in flight
+//    exactly and never has to drain them all before the first use.
 //  * The activations (M <= 16 rows) sit in LDS; each chunk feeds int8 matrix-core
 //    products v_mfma_i32_16x16x64_i8 with the activations as operand A (rows m) and
 //    the weight codes as operand B (columns n).
@@ -23,6 +30,8 @@
 //  * The activations are stored in LDS in the k-order that makes operand A match: within
 //    every 64-element group, position 16 i + 4 r + b holds k = 16 r + 4 b + i.  Any
 //    common permutation of k on both operands leaves the dot product unchanged.
+//  * Per-row maxima and code sums are reduced per wave (wave reductions at M = 1, atomics
+//    on the wave's own LDS slots otherwise), so no block-wide atomic is contended.
 //  * Per-wave int32 partials are combined through LDS; one pass writes the outputs.
 #include "device_common.hpp"
 #include "kernels.hpp"
@@ -33,8 +42,9 @@ namespace {
 
 constexpr int kSkThreads = 256;
 constexpr int kSkWaves = 4;
-constexpr int kSkXBudget = 48 * 1024;  // LDS bytes for the staged activations
-constexpr int kSkMisc = 256;           // s_amax, s_rowsum, s_a, s_inva (16 entries each)
+constexpr int kSkXBudget = 48 * 1024;   // LDS bytes for the staged activations
+constexpr int kSkMisc = 640;            // per-wave s_wmax, s_wsum [4][16]; s_inva [16]
+constexpr uint32_t kOOB = 0x80000000u;  // buffer offset beyond every resource: reads 0
 
 struct SkinnyArgs {
     const int8_t* xq;
@@ -51,12 +61,41 @@ struct SkinnyArgs {
     int out_dtype;
 };
 
-// 16 packed bytes at byte offset `off` of packed row `n` (zeros past the row end).
-template <bool ALIGNED>
-__device__ __forceinline__ uint4 load_w16(const uint8_t* __restrict__ packed, int64_t row_bytes,
-                                          int n, int64_t off) {
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+__device__ __forceinline__ float buf_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
+// Reductions over the 16 lanes of a DPP row (lanes 16r .. 16r+15): xor 1 and xor 2 by
+// quad permutes, then the 8-lane and 16-lane mirrors; every lane of the row gets the result.
+template <typename Op>
+__device__ __forceinline__ uint32_t row16_reduce(uint32_t v, Op op) {
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // [1,0,3,2]
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // [2,3,0,1]
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // half mirror
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));  // mirror
+    return v;
+}
+__device__ __forceinline__ uint32_t row16_max(uint32_t v) {
+    return row16_reduce(v, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+}
+__device__ __forceinline__ int row16_sum(int v) {
+    return (int)row16_reduce((uint32_t)v, [](uint32_t a, uint32_t b) { return a + b; });
+}
+
+// 16 packed bytes at byte offset `off` of packed row `n`, byte by byte, zeros past the
+// row end (the path for K not a multiple of 64, whose rows are not 16-byte aligned).
+__device__ __forceinline__ uint4 load_w16_bytes(const uint8_t* __restrict__ packed,
+                                                int64_t row_bytes, int n, int64_t off) {
     const uint8_t* src = packed + (int64_t)n * row_bytes + off;
-    if (ALIGNED) return *reinterpret_cast<const uint4*>(src);
     uint32_t d[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int j = 0; j < 16; ++j)
@@ -65,40 +104,32 @@ __device__ __forceinline__ uint4 load_w16(const uint8_t* __restrict__ packed, in
 }
 
 // Quantize 16 bf16 values (h: 8 words, 2 values each, low half first) with scale a into
-// 16 int8 codes d[0..3] (value j in byte j%4 of d[j/4]).
+// 16 int8 codes d[0..3] (value j in byte j%4 of d[j/4]): rint(x*a) clamped to +-127.
 __device__ __forceinline__ void quant16(const uint32_t h[8], float a, uint32_t d[4]) {
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-        uint32_t word = 0;
+        uint32_t v[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const uint32_t hw = h[2 * b + (t >> 1)];
-            const uint32_t bits = (t & 1) ? (hw >> 16) : (hw & 0xFFFFu);
-            float r = rintf(bf16_bits_to_f32(bits) * a);
-            r = fminf(fmaxf(r, -127.0f), 127.0f);
-            word |= ((uint32_t)(int)r & 0xFFu) << (8 * t);
+            const float x = (t & 1) ? __uint_as_float(hw & 0xFFFF0000u) : bf16_bits_to_f32(hw);
+            v[t] = (uint32_t)(int)__builtin_amdgcn_fmed3f(rintf(x * a), -127.0f, 127.0f);
         }
-        d[b] = word;
+        // the low bytes of the four ints -> one word (v_perm selector 0x0c gives 0)
+        d[b] = __builtin_amdgcn_perm(v[1], v[0], 0x0c0c0400u) |
+               __builtin_amdgcn_perm(v[3], v[2], 0x04000c0cu);
     }
 }
 
-// Load 16 bf16 activations x[m][k0 .. k0+15] (zeros past K) as 8 words.
-template <bool ALIGNED>
-__device__ __forceinline__ void load_x16_bf16(const uint16_t* __restrict__ xb, int K, int m,
-                                              int k0, uint32_t h[8]) {
+// 16 bf16 activations x[m][k0 .. k0+15] as 8 words, element by element, zeros past K.
+__device__ __forceinline__ void load_x16_bf16_elems(const uint16_t* __restrict__ xb, int K, int m,
+                                                    int k0, uint32_t h[8]) {
     const uint16_t* src = xb + (int64_t)m * K + k0;
-    if (ALIGNED) {
-        const uint4 v0 = reinterpret_cast<const uint4*>(src)[0];
-        const uint4 v1 = reinterpret_cast<const uint4*>(src)[1];
-        h[0] = v0.x; h[1] = v0.y; h[2] = v0.z; h[3] = v0.w;
-        h[4] = v1.x; h[5] = v1.y; h[6] = v1.z; h[7] = v1.w;
-    } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const uint32_t lo = (k0 + 2 * j < K) ? src[2 * j] : 0u;
-            const uint32_t hi = (k0 + 2 * j + 1 < K) ? src[2 * j + 1] : 0u;
-            h[j] = lo | (hi << 16);
-        }
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t lo = (k0 + 2 * j < K) ? src[2 * j] : 0u;
+        const uint32_t hi = (k0 + 2 * j + 1 < K) ? src[2 * j + 1] : 0u;
+        h[j] = lo | (hi << 16);
     }
 }
 
@@ -112,26 +143,24 @@ __device__ __forceinline__ uint32_t absmax_bits16(const uint32_t h[8]) {
     return mx;
 }
 
-// One 16-element group of activations, quantized (d), into the permuted LDS layout;
-// also adds its code sum to s_rowsum[m] and (block 0, if requested) writes the codes.
-template <bool ALIGNED>
-__device__ __forceinline__ void put_group(unsigned char* x_lds, int KSP, int* s_rowsum, int m,
-                                          int u, const uint32_t d[4]) {
+// One 16-element group of codes d into the permuted LDS layout; returns the codes' sum.
+__device__ __forceinline__ int put_group(unsigned char* x_lds, int KSP, int m, int u,
+                                         const uint32_t d[4]) {
     const int rs = sum_i8x4(d[0], sum_i8x4(d[1], sum_i8x4(d[2], sum_i8x4(d[3], 0))));
-    atomicAdd(&s_rowsum[m], rs);
     uint32_t e[4];
     transpose4x4_bytes(d, e);
     unsigned char* dst = x_lds + m * KSP + (u >> 2) * 64 + 4 * (u & 3);
 #pragma unroll
     for (int i = 0; i < 4; ++i) *reinterpret_cast<uint32_t*>(dst + 16 * i) = e[i];
+    return rs;
 }
 
-template <bool ALIGNED>
+template <bool FAST>
 __device__ __forceinline__ void store_codes16(int8_t* xq_out, int K, int m, int k0,
                                               const uint32_t d[4]) {
     int8_t* dst = xq_out + (int64_t)m * K + k0;
-    if (ALIGNED) {
-        *reinterpret_cast<uint4*>(dst) = make_uint4(d[0], d[1], d[2], d[3]);
+    if (FAST) {
+        if (k0 < K) *reinterpret_cast<uint4*>(dst) = make_uint4(d[0], d[1], d[2], d[3]);
     } else {
 #pragma unroll
         for (int j = 0; j < 16; ++j)
@@ -139,65 +168,80 @@ __device__ __forceinline__ void store_codes16(int8_t* xq_out, int K, int m, int 
     }
 }
 
-constexpr int kU = 4;  // 256-weight chunks per wave per batch (loads in flight per lane)
-
-// XREG > 0: the block's activation groups (at most XREG per thread, single K stage) stay
-// in registers between the max pass and the quantization pass.
-template <int NG, bool FUSED, bool ALIGNED, int XREG>
+// Template parameters:
+//  FUSED  - quantize bf16 activations in the kernel (else read int8 codes + a_scale)
+//  FAST   - K % 64 == 0: rows are 16-byte aligned, buffer loads for the weights
+//  XH     - activation groups held in registers per lane (0: staged in loops instead);
+//           only with a single K stage
+//  U      - weight chunks per wave per batch
+//  SINGLE - one batch covers a wave's whole share of K (single K stage)
+template <bool FUSED, bool FAST, int XH, int U, bool SINGLE>
 __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
     extern __shared__ __align__(16) unsigned char smem[];
     const int KSP = p.KS + 16;  // padded LDS row stride: spreads rows over the banks
     const int M = p.M, N = p.N, K = p.K;
     unsigned char* x_lds = smem;
-    uint32_t* s_amax = reinterpret_cast<uint32_t*>(smem + M * KSP);
-    int* s_rowsum = reinterpret_cast<int*>(s_amax + 16);
-    float* s_a = reinterpret_cast<float*>(s_rowsum + 16);
-    float* s_inva = s_a + 16;
-    int* red = reinterpret_cast<int*>(smem + M * KSP + kSkMisc);  // [waves][NG][4][64]
-
+    // per-wave partial results: s_wmax[w][m] = max |x| bits seen by wave w in row m,
+    // s_wsum[w][m] = sum of the codes of row m staged by wave w
+    uint32_t* s_wmax = reinterpret_cast<uint32_t*>(smem + M * KSP);
+    int* s_wsum = reinterpret_cast<int*>(s_wmax + 64);
+    float* s_inva = reinterpret_cast<float*>(s_wsum + 64);
+    int* red = reinterpret_cast<int*>(smem + M * KSP + kSkMisc);  // [waves][4][64]
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t row_bytes = K / 4;
-    const int n0 = blockIdx.x * (16 * NG);
+    const int row_bytes = K / 4;
+    const int n0 = blockIdx.x * 16;
+    const int rows = min(16, N - n0);
     const int mrow = lane & 15;  // operand-A row (token) and operand-B column of this lane
     const int q = lane >> 4;     // k-group of this lane inside a 256-weight chunk
     const bool a_active = mrow < M;
+    const bool row_leader = (lane & 15) == 0;
 
-    // weights of chunks c0 + 4*uu (uu < kU) of the stage starting at byte stage_off
-    auto load_batch = [&](uint4 (&w)[kU][NG], int c0, int nch, int64_t stage_off) {
+    // scales needed at the end, requested first (threads tid < 16 M write outputs)
+    const float ws_n = buf_load_f32(make_rsrc(p.w_scale + n0, (uint32_t)(rows * 4)),
+                                    tid < 16 * M ? (uint32_t)(4 * (tid & 15)) : kOOB);
+    float a_in = 0.0f;
+    if constexpr (!FUSED)
+        a_in = buf_load_f32(make_rsrc(p.a_scale, (uint32_t)(M * 4)), tid < M ? 4u * tid : kOOB);
+
+    // the block's weight rows (fewer than 16 at the end of N); reads past them give 0
+    const __amdgpu_buffer_rsrc_t w_rsrc =
+        make_rsrc(p.packed + (int64_t)n0 * row_bytes, (uint32_t)(rows * row_bytes));
+    const uint32_t w_lane = (uint32_t)(mrow * row_bytes + 16 * q);
+
+    // chunks c = wave + 4 * (j0 + uu), uu < U, of the stage starting at byte stage_off
+    auto load_batch = [&](uint4 (&w)[U], int j0, int stage_off, int nch) {
 #pragma unroll
-        for (int uu = 0; uu < kU; ++uu) {
-            const int c = c0 + kSkWaves * uu;
-#pragma unroll
-            for (int g = 0; g < NG; ++g) {
-                const int n = n0 + 16 * g + mrow;
-                w[uu][g] = (c < nch && n < N)
-                               ? load_w16<ALIGNED>(p.packed, row_bytes, n, stage_off + c * 64 + 16 * q)
-                               : make_uint4(0u, 0u, 0u, 0u);
+        for (int uu = 0; uu < U; ++uu) {
+            const int c = wave + kSkWaves * (j0 + uu);
+            const int cb = stage_off + c * 64;  // the chunk's first byte in the row
+            if (FAST) {
+                const uint32_t off = (c < nch && cb + 16 * q < row_bytes) ? w_lane + cb : kOOB;
+                w[uu] = buf_load16(w_rsrc, off);
+            } else {
+                const int n = n0 + mrow;
+                w[uu] = (n < N && c < nch) ? load_w16_bytes(p.packed, row_bytes, n, cb + 16 * q)
+                                           : make_uint4(0u, 0u, 0u, 0u);
             }
         }
     };
 
-    v4i acc1[NG], acc4[NG], acc16[NG];
-#pragma unroll
-    for (int g = 0; g < NG; ++g) acc1[g] = acc4[g] = acc16[g] = v4i{0, 0, 0, 0};
+    v4i acc1 = v4i{0, 0, 0, 0}, acc4 = acc1, acc16 = acc1;
 
-    auto compute_batch = [&](const uint4 (&w)[kU][NG], int c0, int nch) {
+    auto compute_batch = [&](const uint4 (&w)[U], int j0, int nch) {
 #pragma unroll
-        for (int uu = 0; uu < kU; ++uu) {
-            const int c = c0 + kSkWaves * uu;
-            if (c >= nch) break;
-            v4i A[4];
-            if (a_active) {
-                const unsigned char* src = x_lds + mrow * KSP + (c * 4 + q) * 64;
+        for (int uu = 0; uu < U; ++uu) {
+            const int c = wave + kSkWaves * (j0 + uu);
+            if (c < nch) {
+                v4i A[4];
+                if (a_active) {
+                    const unsigned char* src = x_lds + mrow * KSP + (c * 4 + q) * 64;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) A[i] = *reinterpret_cast<const v4i*>(src + 16 * i);
-            } else {
+                    for (int i = 0; i < 4; ++i) A[i] = *reinterpret_cast<const v4i*>(src + 16 * i);
+                } else {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) A[i] = v4i{0, 0, 0, 0};
-            }
-#pragma unroll
-            for (int g = 0; g < NG; ++g) {
-                const uint32_t w4[4] = {w[uu][g].x, w[uu][g].y, w[uu][g].z, w[uu][g].w};
+                    for (int i = 0; i < 4; ++i) A[i] = v4i{0, 0, 0, 0};
+                }
+                const uint32_t w4[4] = {w[uu].x, w[uu].y, w[uu].z, w[uu].w};
                 v4i b0, b1, b2, b3;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -206,127 +250,163 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
                     b2[r] = (int)(w4[r] & 0x30303030u);
                     b3[r] = (int)((w4[r] >> 2) & 0x30303030u);
                 }
-                acc1[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[0], b0, acc1[g], 0, 0, 0);
-                acc4[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[1], b1, acc4[g], 0, 0, 0);
-                acc16[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2], b2, acc16[g], 0, 0, 0);
-                acc16[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[3], b3, acc16[g], 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[0], b0, acc1, 0, 0, 0);
+                acc4 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[1], b1, acc4, 0, 0, 0);
+                acc16 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2], b2, acc16, 0, 0, 0);
+                acc16 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[3], b3, acc16, 0, 0, 0);
             }
         }
     };
 
-    // The first weight batch is requested before anything else, so its memory latency
-    // overlaps the activation phases below.
-    uint4 cur[kU][NG], nxt[kU][NG];
-    {
-        const int len0 = min(p.KS, p.Kp);
-        load_batch(cur, wave, len0 >> 8, 0);
+    // each wave clears its own slots (LDS operations of one wave complete in order)
+    if (lane < 16) {
+        s_wmax[wave * 16 + lane] = 0u;
+        s_wsum[wave * 16 + lane] = 0;
     }
+    // the activation scale 127 / max|x| of token m from the four waves' maxima
+    auto fused_scale = [&](int m) -> float {
+        const uint32_t mx = max(max(s_wmax[m], s_wmax[16 + m]), max(s_wmax[32 + m], s_wmax[48 + m]));
+        float amax = bf16_bits_to_f32(mx);
+        amax = amax < 1e-5f ? 1e-5f : amax;
+        return 127.0f / amax;
+    };
 
-    if (tid < 16) {
-        s_amax[tid] = 0u;
-        s_rowsum[tid] = 0;
-    }
-    __syncthreads();
+    // Staging is wave-local: wave w stages exactly the chunks c = w + 4 j it multiplies,
+    // all M rows, so no block barrier separates staging from use.  The wave's 16-element
+    // groups are numbered g = (j * M + m) * 16 + i (activations k = 256 c + 16 i ..
+    // + 15 of row m); lane l takes g = l + 64 t, so the 16 lanes of a DPP row share
+    // (j, m) and reduce their per-row partials with DPP before one LDS atomic.
+    auto group_of = [&](int g, int& m, int& c, int& i) {
+        i = g & 15;
+        const int jm = g >> 4, j = jm / M;
+        m = jm - j * M;
+        c = wave + kSkWaves * j;
+    };
 
-    uint32_t held[XREG > 0 ? XREG : 1][8];
-    if constexpr (FUSED) {
-        if constexpr (XREG > 0) {
-            const int gpr = p.Kp >> 4;
+    uint4 wa[U];
+    const int nch0 = min(p.KS, p.Kp) >> 8;
+    if constexpr (XH > 0) {
+        // ---- single K stage, activations held in registers: requested before weights ----
+        constexpr int XW = FUSED ? 8 : 4;
+        uint32_t held[XH][XW];
 #pragma unroll
-            for (int t = 0; t < XREG; ++t) {
-                const int gi = tid + t * kSkThreads;
-                if (gi < M * gpr) {
-                    const int m = gi / gpr, u = gi - m * gpr;
-                    load_x16_bf16<ALIGNED>(p.xb, K, m, 16 * u, held[t]);
-                }
+        for (int t = 0; t < XH; ++t) {
+            int m, c, i;
+            group_of(lane + 64 * t, m, c, i);
+            const int k0 = 256 * c + 16 * i;
+            const bool ok = c < nch0 && k0 < K;
+            if constexpr (FUSED) {
+                const __amdgpu_buffer_rsrc_t x_rsrc = make_rsrc(p.xb, (uint32_t)(M * K * 2));
+                const uint32_t off = ok ? (uint32_t)((m * K + k0) * 2) : kOOB;
+                const uint4 v0 = buf_load16(x_rsrc, off), v1 = buf_load16(x_rsrc, off + 16);
+                held[t][0] = v0.x; held[t][1] = v0.y; held[t][2] = v0.z; held[t][3] = v0.w;
+                held[t][4] = v1.x; held[t][5] = v1.y; held[t][6] = v1.z; held[t][7] = v1.w;
+            } else {
+                const __amdgpu_buffer_rsrc_t x_rsrc = make_rsrc(p.xq, (uint32_t)(M * K));
+                const uint4 v0 = buf_load16(x_rsrc, ok ? (uint32_t)(m * K + k0) : kOOB);
+                held[t][0] = v0.x; held[t][1] = v0.y; held[t][2] = v0.z; held[t][3] = v0.w;
             }
-            uint32_t mx = 0;
-            int mcur = -1;
-#pragma unroll
-            for (int t = 0; t < XREG; ++t) {
-                const int gi = tid + t * kSkThreads;
-                if (gi < M * gpr) {
-                    const int m = gi / gpr;
-                    if (m != mcur && mcur >= 0) {
-                        atomicMax(&s_amax[mcur], mx);
-                        mx = 0;
-                    }
-                    mcur = m;
-                    mx = max(mx, absmax_bits16(held[t]));
-                }
-            }
+        }
+        load_batch(wa, 0, 0, nch0);  // the weights' memory trip overlaps all that follows
+
+        if constexpr (FUSED) {
             if (M == 1) {
-                mx = wave_max_u32(mx);
-                if (lane == 0) atomicMax(&s_amax[0], mx);
-            } else if (mcur >= 0) {
-                atomicMax(&s_amax[mcur], mx);
-            }
-        } else {
-            // max |x| per token over the whole row, 4 elements per load
-            const int64_t groups = K / 4;
-            for (int m = 0; m < M; ++m) {
-                const uint2* row = reinterpret_cast<const uint2*>(p.xb + (int64_t)m * K);
                 uint32_t mx = 0;
-                for (int64_t g = tid; g < groups; g += kSkThreads) {
-                    const uint2 v = row[g];
-                    const uint32_t a = v.x & 0x7FFF7FFFu, b = v.y & 0x7FFF7FFFu;
-                    mx = max(mx, max(max(a & 0xFFFFu, a >> 16), max(b & 0xFFFFu, b >> 16)));
+#pragma unroll
+                for (int t = 0; t < XH; ++t) mx = max(mx, absmax_bits16(held[t]));  // 0 if unused
+                mx = row16_max(mx);
+                if (row_leader) atomicMax(&s_wmax[wave * 16], mx);
+            } else {
+#pragma unroll
+                for (int t = 0; t < XH; ++t) {
+                    int m, c, i;
+                    group_of(lane + 64 * t, m, c, i);
+                    const uint32_t mx = row16_max(absmax_bits16(held[t]));
+                    if (row_leader && c < nch0) atomicMax(&s_wmax[wave * 16 + m], mx);
                 }
-                mx = wave_max_u32(mx);
-                if (lane == 0) atomicMax(&s_amax[m], mx);
             }
+            __syncthreads();
+        }
+        float a1 = 0.0f;
+        if constexpr (FUSED) a1 = M == 1 ? fused_scale(0) : 0.0f;
+        int rsum = 0;
+#pragma unroll
+        for (int t = 0; t < XH; ++t) {
+            int m, c, i;
+            group_of(lane + 64 * t, m, c, i);
+            uint32_t d[4];
+            if constexpr (FUSED) {
+                quant16(held[t], M == 1 ? a1 : fused_scale(m), d);
+                if (blockIdx.x == 0 && p.xq_out && c < nch0)
+                    store_codes16<FAST>(p.xq_out, K, m, 256 * c + 16 * i, d);
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) d[r] = held[t][r];
+            }
+            int rs = 0;
+            if (c < nch0) rs = put_group(x_lds, KSP, m, 16 * c + i, d);
+            if (M == 1) {
+                rsum += rs;
+            } else {
+                rs = row16_sum(rs);
+                if (row_leader && c < nch0) atomicAdd(&s_wsum[wave * 16 + m], rs);
+            }
+        }
+        if (M == 1) {
+            rsum = row16_sum(rsum);
+            if (row_leader) atomicAdd(&s_wsum[wave * 16], rsum);
+        }
+    } else if constexpr (FUSED) {
+        // ---- max |x| per token over the whole row, 4 elements per load ----
+        const int groups = K / 4;
+        for (int m = 0; m < M; ++m) {
+            const uint2* row = reinterpret_cast<const uint2*>(p.xb + (int64_t)m * K);
+            uint32_t mx = 0;
+            for (int g = tid; g < groups; g += kSkThreads) {
+                const uint2 v = row[g];
+                const uint32_t a = v.x & 0x7FFF7FFFu, b = v.y & 0x7FFF7FFFu;
+                mx = max(mx, max(max(a & 0xFFFFu, a >> 16), max(b & 0xFFFFu, b >> 16)));
+            }
+            mx = row16_max(mx);
+            if (row_leader) atomicMax(&s_wmax[wave * 16 + m], mx);
         }
         __syncthreads();
-    }
-    if (tid < M) {
-        float a;
-        if constexpr (FUSED) {
-            float amax = bf16_bits_to_f32(s_amax[tid]);
-            amax = amax < 1e-5f ? 1e-5f : amax;
-            a = 127.0f / amax;
-            if (blockIdx.x == 0 && p.a_out) p.a_out[tid] = a;
-        } else {
-            a = p.a_scale[tid];
-        }
-        s_a[tid] = a;
-        s_inva[tid] = 1.0f / a;
     }
 
     for (int ks = 0; ks < p.Kp; ks += p.KS) {
         const int len = min(p.KS, p.Kp - ks);
         const int nch = len >> 8;
-        const int64_t stage_off = ks >> 2;
-        if (ks > 0) load_batch(cur, wave, nch, stage_off);
-        __syncthreads();  // previous stage consumed; s_a visible
-
-        // ---- stage activations [ks, ks+len) of all M rows into LDS, permuted ----
-        const int gpr = len >> 4;  // 16-element groups per row
-        if (FUSED && XREG > 0) {
-#pragma unroll
-            for (int t = 0; t < (XREG > 0 ? XREG : 1); ++t) {
-                const int gi = tid + t * kSkThreads;
-                if (gi < M * gpr) {
-                    const int m = gi / gpr, u = gi - m * gpr;
-                    uint32_t d[4];
-                    quant16(held[t], s_a[m], d);
-                    if (blockIdx.x == 0 && p.xq_out) store_codes16<ALIGNED>(p.xq_out, K, m, 16 * u, d);
-                    put_group<ALIGNED>(x_lds, KSP, s_rowsum, m, u, d);
-                }
-            }
-        } else {
-            for (int gi = tid; gi < M * gpr; gi += kSkThreads) {
-                const int m = gi / gpr, u = gi - m * gpr;
-                const int k0 = ks + 16 * u;
+        const int stage_off = ks >> 2;
+        if constexpr (XH == 0) {
+            // ---- stage this wave's chunks of [ks, ks+len), all M rows, into LDS ----
+            const int cnt = M * ((nch - wave + kSkWaves - 1) / kSkWaves) * 16;
+            for (int g = lane; g < cnt; g += 64) {  // the 16 lanes of a row stay together
+                int m, c, i;
+                group_of(g, m, c, i);
+                const int k0 = ks + 256 * c + 16 * i;
                 uint32_t d[4];
                 if constexpr (FUSED) {
                     uint32_t h[8];
-                    load_x16_bf16<ALIGNED>(p.xb, K, m, k0, h);
-                    quant16(h, s_a[m], d);
-                    if (blockIdx.x == 0 && p.xq_out) store_codes16<ALIGNED>(p.xq_out, K, m, k0, d);
+                    if (FAST) {
+                        if (k0 < K) {
+                            const uint4* src = reinterpret_cast<const uint4*>(p.xb + (int64_t)m * K + k0);
+                            const uint4 v0 = src[0], v1 = src[1];
+                            h[0] = v0.x; h[1] = v0.y; h[2] = v0.z; h[3] = v0.w;
+                            h[4] = v1.x; h[5] = v1.y; h[6] = v1.z; h[7] = v1.w;
+                        } else {
+#pragma unroll
+                            for (int j = 0; j < 8; ++j) h[j] = 0u;
+                        }
+                    } else {
+                        load_x16_bf16_elems(p.xb, K, m, k0, h);
+                    }
+                    quant16(h, fused_scale(m), d);
+                    if (blockIdx.x == 0 && p.xq_out) store_codes16<FAST>(p.xq_out, K, m, k0, d);
                 } else {
                     const int8_t* src = p.xq + (int64_t)m * K + k0;
-                    if (ALIGNED) {
-                        const uint4 v = *reinterpret_cast<const uint4*>(src);
+                    if (FAST) {
+                        const uint4 v = k0 < K ? *reinterpret_cast<const uint4*>(src)
+                                               : make_uint4(0u, 0u, 0u, 0u);
                         d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
                     } else {
                         d[0] = d[1] = d[2] = d[3] = 0u;
@@ -335,57 +415,86 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
                             if (k0 + j < K) d[j >> 2] |= (uint32_t)(uint8_t)src[j] << (8 * (j & 3));
                     }
                 }
-                put_group<ALIGNED>(x_lds, KSP, s_rowsum, m, u, d);
+                const int rs = row16_sum(put_group(x_lds, KSP, m, 16 * c + i, d));
+                if (row_leader) atomicAdd(&s_wsum[wave * 16 + m], rs);
             }
+            load_batch(wa, 0, stage_off, nch);
         }
-        __syncthreads();
+        // The activations this wave multiplies are its own LDS writes, and the LDS
+        // operations of a wave complete in order; keep the compiler from hoisting reads.
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        __builtin_amdgcn_wave_barrier();
 
-        // ---- stream the packed weights of this stage: two register batches in flight ----
-        for (int c0 = wave; c0 < nch; c0 += kSkWaves * kU) {
-            const int c1 = c0 + kSkWaves * kU;
-            if (c1 < nch) load_batch(nxt, c1, nch, stage_off);
-            compute_batch(cur, c0, nch);
-            if (c1 < nch) {
-#pragma unroll
-                for (int uu = 0; uu < kU; ++uu)
-#pragma unroll
-                    for (int g = 0; g < NG; ++g) cur[uu][g] = nxt[uu][g];
+        // ---- stream the packed weights of this stage ----
+        if constexpr (SINGLE) {
+            compute_batch(wa, 0, nch);
+        } else {
+            const int cpw = (nch + kSkWaves - 1) / kSkWaves;  // chunks per wave (upper bound)
+            uint4 wb[U];
+            for (int j0 = 0; j0 < cpw; j0 += 2 * U) {
+                load_batch(wb, j0 + U, stage_off, nch);  // zeros when past the stage
+                compute_batch(wa, j0, nch);
+                if (j0 + U >= cpw) break;
+                load_batch(wa, j0 + 2 * U, stage_off, nch);
+                compute_batch(wb, j0 + U, nch);
             }
         }
     }
 
     // ---- combine the four waves' partials and write the outputs ----
+    if (tid < M) {
+        const float a = FUSED ? fused_scale(tid) : a_in;
+        if (FUSED && blockIdx.x == 0 && p.a_out) p.a_out[tid] = a;
+        s_inva[tid] = 1.0f / a;
+    }
+    {
+        const v4i t = acc1 + (acc4 >> 2) + (acc16 >> 4);
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
-        const v4i t = acc1[g] + (acc4[g] >> 2) + (acc16[g] >> 4);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) red[((wave * NG + g) * 4 + r) * 64 + lane] = t[r];
+        for (int r = 0; r < 4; ++r) red[(wave * 4 + r) * 64 + lane] = t[r];
     }
     __syncthreads();
-    for (int idx = tid; idx < NG * 256; idx += kSkThreads) {
-        const int g = idx >> 8, r = (idx >> 6) & 3, l = idx & 63;
+    if (tid < 16 * M) {
         // 16x16 int32 accumulator layout: lane l, register r -> row 4*(l/16)+r, column l%16
-        const int m = 4 * (l >> 4) + r;
-        const int n = n0 + 16 * g + (l & 15);
-        if (m < M && n < N) {
-            int acc = -s_rowsum[m];
+        const int m = tid >> 4, col = tid & 15;
+        const int l = 16 * (m >> 2) + col, r = m & 3;
+        if (col < rows) {
+            int acc = -(s_wsum[m] + s_wsum[16 + m] + s_wsum[32 + m] + s_wsum[48 + m]);
 #pragma unroll
-            for (int w = 0; w < kSkWaves; ++w) acc += red[((w * NG + g) * 4 + r) * 64 + l];
-            store_out(p.out, (int64_t)m * N + n, p.out_dtype, acc, p.w_scale[n], s_inva[m]);
+            for (int w = 0; w < kSkWaves; ++w) acc += red[(w * 4 + r) * 64 + l];
+            store_out(p.out, (int64_t)m * N + n0 + col, p.out_dtype, acc, ws_n, s_inva[m]);
         }
     }
 }
 
-template <int NG, bool FUSED, int XREG>
-hipError_t dispatch_aligned(const SkinnyArgs& a, bool aligned, dim3 grid, size_t lds,
-                            hipStream_t stream) {
-    if (aligned)
-        hipLaunchKernelGGL((skinny_kernel<NG, FUSED, true, XREG>), grid, dim3(kSkThreads), lds,
-                           stream, a);
-    else
-        hipLaunchKernelGGL((skinny_kernel<NG, FUSED, false, XREG>), grid, dim3(kSkThreads), lds,
-                           stream, a);
+template <bool FUSED, bool FAST, int XH, int U, bool SINGLE>
+hipError_t launch_one(const SkinnyArgs& a, dim3 grid, size_t lds, hipStream_t stream) {
+    hipLaunchKernelGGL((skinny_kernel<FUSED, FAST, XH, U, SINGLE>), grid, dim3(kSkThreads), lds,
+                       stream, a);
     return hipGetLastError();
+}
+
+// Batch shape: U = 4 or 8 chunks per wave; SINGLE when one batch holds a wave's share.
+template <bool FUSED, int XH>
+hipError_t launch_fast(const SkinnyArgs& a, dim3 grid, size_t lds, hipStream_t stream) {
+    const int cpw = (a.KS / 256 + kSkWaves - 1) / kSkWaves;
+    const bool one_stage = a.KS >= a.Kp;
+    if (one_stage && cpw <= 4) return launch_one<FUSED, true, XH, 4, true>(a, grid, lds, stream);
+    if (one_stage && cpw <= 8) return launch_one<FUSED, true, XH, 8, true>(a, grid, lds, stream);
+    return launch_one<FUSED, true, XH, 8, false>(a, grid, lds, stream);
+}
+
+// Held activation groups per lane: M * (chunks per wave) * 16 groups over 64 lanes.
+template <bool FUSED>
+hipError_t launch_held(const SkinnyArgs& a, dim3 grid, size_t lds, hipStream_t stream) {
+    const int cpw = (a.Kp / 256 + kSkWaves - 1) / kSkWaves;
+    const int per_lane = (a.M * cpw + 3) / 4;
+    if (a.KS >= a.Kp) {
+        if (per_lane <= 1) return launch_fast<FUSED, 1>(a, grid, lds, stream);
+        if (per_lane <= 2) return launch_fast<FUSED, 2>(a, grid, lds, stream);
+        if (per_lane <= 4) return launch_fast<FUSED, 4>(a, grid, lds, stream);
+        if (per_lane <= 8) return launch_fast<FUSED, 8>(a, grid, lds, stream);
+    }
+    return launch_fast<FUSED, 0>(a, grid, lds, stream);
 }
 
 }  // namespace
@@ -411,18 +520,14 @@ hipError_t launch_skinny(const int8_t* xq, const float* a_scale, const uint16_t*
     if (ks < 256) ks = 256;
     a.KS = ks < a.Kp ? ks : a.Kp;
     a.out_dtype = out_dtype;
-    constexpr int NG = 1;
-    const size_t lds = (size_t)M * (a.KS + 16) + kSkMisc + (size_t)kSkWaves * NG * 4 * 64 * 4;
-    const dim3 grid((unsigned)((N + 16 * NG - 1) / (16 * NG)));
-    const bool aligned = (K % 256) == 0;
-    if (x_bf16) {
-        // activations held in registers between the two passes when one K stage covers
-        // the row and the block's groups fit two per thread
-        const bool hold = a.KS >= a.Kp && (int64_t)M * (a.Kp / 16) <= 2 * kSkThreads;
-        if (hold) return dispatch_aligned<NG, true, 2>(a, aligned, grid, lds, stream);
-        return dispatch_aligned<NG, true, 0>(a, aligned, grid, lds, stream);
+    const size_t lds = (size_t)M * (a.KS + 16) + kSkMisc + (size_t)kSkWaves * 4 * 64 * 4;
+    const dim3 grid((unsigned)((N + 15) / 16));
+    const bool fused = x_bf16 != nullptr;
+    if (K % 64 != 0) {
+        if (fused) return launch_one<true, false, 0, 4, false>(a, grid, lds, stream);
+        return launch_one<false, false, 0, 4, false>(a, grid, lds, stream);
     }
-    return dispatch_aligned<NG, false, 0>(a, aligned, grid, lds, stream);
+    return fused ? launch_held<true>(a, grid, lds, stream) : launch_held<false>(a, grid, lds, stream);
 }
 
 }  // namespace bitnet
