@@ -40,10 +40,13 @@ namespace bitnet {
 
 namespace {
 
-constexpr int kSkThreads = 256;
-constexpr int kSkWaves = 4;
+#ifndef BITNET_SKINNY_WAVES
+#define BITNET_SKINNY_WAVES 4
+#endif
+constexpr int kSkWaves = BITNET_SKINNY_WAVES;
+constexpr int kSkThreads = 64 * kSkWaves;
 constexpr int kSkXBudget = 48 * 1024;   // LDS bytes for the staged activations
-constexpr int kSkMisc = 640;            // per-wave s_wmax, s_wsum [4][16]; s_inva [16]
+constexpr int kSkMisc = kSkWaves * 128 + 64;  // per-wave s_wmax, s_wsum [waves][16]; s_inva [16]
 constexpr uint32_t kOOB = 0x80000000u;  // buffer offset beyond every resource: reads 0
 
 struct SkinnyArgs {
@@ -91,6 +94,20 @@ __device__ __forceinline__ int row16_sum(int v) {
     return (int)row16_reduce((uint32_t)v, [](uint32_t a, uint32_t b) { return a + b; });
 }
 
+// Wave-wide reductions with a uniform (scalar) result: DPP within each row, then the
+// four row results read out with v_readlane.
+__device__ __forceinline__ uint32_t wave_max_uniform(uint32_t v) {
+    v = row16_max(v);
+    const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+    const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+    return max(max(a, b), max(c, d));
+}
+__device__ __forceinline__ int wave_sum_uniform(int v) {
+    v = row16_sum(v);
+    return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
+           __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
+}
+
 // 16 packed bytes at byte offset `off` of packed row `n`, byte by byte, zeros past the
 // row end (the path for K not a multiple of 64, whose rows are not 16-byte aligned).
 __device__ __forceinline__ uint4 load_w16_bytes(const uint8_t* __restrict__ packed,
@@ -104,21 +121,26 @@ __device__ __forceinline__ uint4 load_w16_bytes(const uint8_t* __restrict__ pack
 }
 
 // Quantize 16 bf16 values (h: 8 words, 2 values each, low half first) with scale a into
-// 16 int8 codes d[0..3] (value j in byte j%4 of d[j/4]): rint(x*a) clamped to +-127.
-__device__ __forceinline__ void quant16(const uint32_t h[8], float a, uint32_t d[4]) {
+// 16 int8 codes, packed transposed for the operand layout: byte b of e[i] is the code of
+// element 4 b + i.  The code is rint(fl(x * a)) with ties to even: adding 1.5 * 2^23 to
+// fl(x * a) (|x * a| < 2^22) rounds it to an integer in one fp32 addition, and the low
+// byte of the sum's bit pattern is that integer in two's complement.  The clamp to
+// +-127 of the definition never binds here: a = fl(127 / amax) and |x| <= amax give
+// |fl(x * a)| <= 127 (1 + 2^-23) < 127.5.
+__device__ __forceinline__ void quant16_t(const uint32_t h[8], float a, uint32_t e[4]) {
+    constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
+    uint32_t v[16];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        uint32_t v[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const uint32_t hw = h[2 * b + (t >> 1)];
-            const float x = (t & 1) ? __uint_as_float(hw & 0xFFFF0000u) : bf16_bits_to_f32(hw);
-            v[t] = (uint32_t)(int)__builtin_amdgcn_fmed3f(rintf(x * a), -127.0f, 127.0f);
-        }
-        // the low bytes of the four ints -> one word (v_perm selector 0x0c gives 0)
-        d[b] = __builtin_amdgcn_perm(v[1], v[0], 0x0c0c0400u) |
-               __builtin_amdgcn_perm(v[3], v[2], 0x04000c0cu);
+    for (int j = 0; j < 8; ++j) {
+        v[2 * j] = __float_as_uint(bf16_bits_to_f32(h[j]) * a + kMagic);
+        v[2 * j + 1] = __float_as_uint(__uint_as_float(h[j] & 0xFFFF0000u) * a + kMagic);
     }
+    // low bytes of elements i, 4+i (bytes 0, 1) and 8+i, 12+i (bytes 2, 3); selector 0x0c
+    // gives a zero byte
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        e[i] = __builtin_amdgcn_perm(v[4 + i], v[i], 0x0c0c0400u) |
+               __builtin_amdgcn_perm(v[12 + i], v[8 + i], 0x04000c0cu);
 }
 
 // 16 bf16 activations x[m][k0 .. k0+15] as 8 words, element by element, zeros past K.
@@ -133,26 +155,31 @@ __device__ __forceinline__ void load_x16_bf16_elems(const uint16_t* __restrict__
     }
 }
 
+// max |x| of 16 bf16 values as bf16 bits (a monotone key for non-negative values),
+// two lanes at a time with the packed 16-bit integer max.
 __device__ __forceinline__ uint32_t absmax_bits16(const uint32_t h[8]) {
-    uint32_t mx = 0;
+    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+    u16x2 m = __builtin_bit_cast(u16x2, h[0] & 0x7FFF7FFFu);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const uint32_t a = h[j] & 0x7FFF7FFFu;
-        mx = max(mx, max(a & 0xFFFFu, a >> 16));
-    }
-    return mx;
+    for (int j = 1; j < 8; ++j)
+        m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, h[j] & 0x7FFF7FFFu));
+    return max((uint32_t)m.x, (uint32_t)m.y);
 }
 
-// One 16-element group of codes d into the permuted LDS layout; returns the codes' sum.
-__device__ __forceinline__ int put_group(unsigned char* x_lds, int KSP, int m, int u,
-                                         const uint32_t d[4]) {
-    const int rs = sum_i8x4(d[0], sum_i8x4(d[1], sum_i8x4(d[2], sum_i8x4(d[3], 0))));
-    uint32_t e[4];
-    transpose4x4_bytes(d, e);
+// One 16-element group, already transposed (byte b of e[i] = element 4 b + i), into the
+// permuted LDS layout; returns the sum of its codes.
+__device__ __forceinline__ int put_group_t(unsigned char* x_lds, int KSP, int m, int u,
+                                           const uint32_t e[4]) {
+    const int rs = sum_i8x4(e[0], sum_i8x4(e[1], sum_i8x4(e[2], sum_i8x4(e[3], 0))));
     unsigned char* dst = x_lds + m * KSP + (u >> 2) * 64 + 4 * (u & 3);
 #pragma unroll
     for (int i = 0; i < 4; ++i) *reinterpret_cast<uint32_t*>(dst + 16 * i) = e[i];
     return rs;
+}
+
+// Element-order codes of a transposed group (for the optional copy of the codes).
+__device__ __forceinline__ void untranspose(const uint32_t e[4], uint32_t d[4]) {
+    transpose4x4_bytes(e, d);  // the 4x4 byte transpose is its own inverse
 }
 
 template <bool FAST>
@@ -175,19 +202,22 @@ __device__ __forceinline__ void store_codes16(int8_t* xq_out, int K, int m, int 
 //           only with a single K stage
 //  U      - weight chunks per wave per batch
 //  SINGLE - one batch covers a wave's whole share of K (single K stage)
-template <bool FUSED, bool FAST, int XH, int U, bool SINGLE>
+//  MC     - M fixed at compile time (1), or 0 for M read from the arguments
+template <bool FUSED, bool FAST, int XH, int U, bool SINGLE, int MC>
 __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
     extern __shared__ __align__(16) unsigned char smem[];
     const int KSP = p.KS + 16;  // padded LDS row stride: spreads rows over the banks
-    const int M = p.M, N = p.N, K = p.K;
+    const int M = MC > 0 ? MC : p.M;
+    const int N = p.N, K = p.K;
     unsigned char* x_lds = smem;
     // per-wave partial results: s_wmax[w][m] = max |x| bits seen by wave w in row m,
     // s_wsum[w][m] = sum of the codes of row m staged by wave w
     uint32_t* s_wmax = reinterpret_cast<uint32_t*>(smem + M * KSP);
-    int* s_wsum = reinterpret_cast<int*>(s_wmax + 64);
-    float* s_inva = reinterpret_cast<float*>(s_wsum + 64);
+    int* s_wsum = reinterpret_cast<int*>(s_wmax + 16 * kSkWaves);
+    float* s_inva = reinterpret_cast<float*>(s_wsum + 16 * kSkWaves);
     int* red = reinterpret_cast<int*>(smem + M * KSP + kSkMisc);  // [waves][4][64]
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
     const int row_bytes = K / 4;
     const int n0 = blockIdx.x * 16;
     const int rows = min(16, N - n0);
@@ -199,9 +229,10 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
     // scales needed at the end, requested first (threads tid < 16 M write outputs)
     const float ws_n = buf_load_f32(make_rsrc(p.w_scale + n0, (uint32_t)(rows * 4)),
                                     tid < 16 * M ? (uint32_t)(4 * (tid & 15)) : kOOB);
-    float a_in = 0.0f;
+    float a_in = 0.0f;  // M = 1: every thread holds the token's scale
     if constexpr (!FUSED)
-        a_in = buf_load_f32(make_rsrc(p.a_scale, (uint32_t)(M * 4)), tid < M ? 4u * tid : kOOB);
+        a_in = buf_load_f32(make_rsrc(p.a_scale, (uint32_t)(M * 4)),
+                            MC == 1 ? 0u : (tid < M ? 4u * tid : kOOB));
 
     // the block's weight rows (fewer than 16 at the end of N); reads past them give 0
     const __amdgpu_buffer_rsrc_t w_rsrc =
@@ -231,7 +262,9 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
 #pragma unroll
         for (int uu = 0; uu < U; ++uu) {
             const int c = wave + kSkWaves * (j0 + uu);
-            if (c < nch) {
+            // With M = 1 and one batch, chunks past the stage are multiplied as well: their
+            // weights read as zeros and their operand-A reads stay inside the LDS block.
+            if ((MC == 1 && SINGLE) || c < nch) {
                 v4i A[4];
                 if (a_active) {
                     const unsigned char* src = x_lds + mrow * KSP + (c * 4 + q) * 64;
@@ -263,9 +296,11 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
         s_wmax[wave * 16 + lane] = 0u;
         s_wsum[wave * 16 + lane] = 0;
     }
-    // the activation scale 127 / max|x| of token m from the four waves' maxima
+    // the activation scale 127 / max|x| of token m from the waves' maxima
     auto fused_scale = [&](int m) -> float {
-        const uint32_t mx = max(max(s_wmax[m], s_wmax[16 + m]), max(s_wmax[32 + m], s_wmax[48 + m]));
+        uint32_t mx = s_wmax[m];
+#pragma unroll
+        for (int w = 1; w < kSkWaves; ++w) mx = max(mx, s_wmax[16 * w + m]);
         float amax = bf16_bits_to_f32(mx);
         amax = amax < 1e-5f ? 1e-5f : amax;
         return 127.0f / amax;
@@ -285,6 +320,8 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
 
     uint4 wa[U];
     const int nch0 = min(p.KS, p.Kp) >> 8;
+    float a_m1 = 0.0f;  // M = 1, fused: the token's scale, uniform
+    int wsum_m1 = 0;    // M = 1: code sum of the activations this wave staged, uniform
     if constexpr (XH > 0) {
         // ---- single K stage, activations held in registers: requested before weights ----
         constexpr int XW = FUSED ? 8 : 4;
@@ -310,12 +347,12 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
         load_batch(wa, 0, 0, nch0);  // the weights' memory trip overlaps all that follows
 
         if constexpr (FUSED) {
-            if (M == 1) {
+            if (MC == 1) {
                 uint32_t mx = 0;
 #pragma unroll
                 for (int t = 0; t < XH; ++t) mx = max(mx, absmax_bits16(held[t]));  // 0 if unused
-                mx = row16_max(mx);
-                if (row_leader) atomicMax(&s_wmax[wave * 16], mx);
+                mx = wave_max_uniform(mx);
+                if (lane == 0) s_wmax[wave * 16] = mx;
             } else {
 #pragma unroll
                 for (int t = 0; t < XH; ++t) {
@@ -327,35 +364,33 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
             }
             __syncthreads();
         }
-        float a1 = 0.0f;
-        if constexpr (FUSED) a1 = M == 1 ? fused_scale(0) : 0.0f;
+        if constexpr (FUSED && MC == 1) a_m1 = fused_scale(0);
         int rsum = 0;
 #pragma unroll
         for (int t = 0; t < XH; ++t) {
             int m, c, i;
             group_of(lane + 64 * t, m, c, i);
-            uint32_t d[4];
+            uint32_t e[4];
             if constexpr (FUSED) {
-                quant16(held[t], M == 1 ? a1 : fused_scale(m), d);
-                if (blockIdx.x == 0 && p.xq_out && c < nch0)
+                quant16_t(held[t], MC == 1 ? a_m1 : fused_scale(m), e);
+                if (blockIdx.x == 0 && p.xq_out && c < nch0) {
+                    uint32_t d[4];
+                    untranspose(e, d);
                     store_codes16<FAST>(p.xq_out, K, m, 256 * c + 16 * i, d);
+                }
             } else {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) d[r] = held[t][r];
+                transpose4x4_bytes(held[t], e);
             }
             int rs = 0;
-            if (c < nch0) rs = put_group(x_lds, KSP, m, 16 * c + i, d);
-            if (M == 1) {
+            if (c < nch0) rs = put_group_t(x_lds, KSP, m, 16 * c + i, e);
+            if (MC == 1) {
                 rsum += rs;
             } else {
                 rs = row16_sum(rs);
                 if (row_leader && c < nch0) atomicAdd(&s_wsum[wave * 16 + m], rs);
             }
         }
-        if (M == 1) {
-            rsum = row16_sum(rsum);
-            if (row_leader) atomicAdd(&s_wsum[wave * 16], rsum);
-        }
+        if (MC == 1) wsum_m1 = wave_sum_uniform(rsum);
     } else if constexpr (FUSED) {
         // ---- max |x| per token over the whole row, 4 elements per load ----
         const int groups = K / 4;
@@ -373,7 +408,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
         __syncthreads();
     }
 
-    for (int ks = 0; ks < p.Kp; ks += p.KS) {
+    auto run_stage = [&](int ks) {
         const int len = min(p.KS, p.Kp - ks);
         const int nch = len >> 8;
         const int stage_off = ks >> 2;
@@ -384,7 +419,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
                 int m, c, i;
                 group_of(g, m, c, i);
                 const int k0 = ks + 256 * c + 16 * i;
-                uint32_t d[4];
+                uint32_t e[4];
                 if constexpr (FUSED) {
                     uint32_t h[8];
                     if (FAST) {
@@ -400,9 +435,14 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
                     } else {
                         load_x16_bf16_elems(p.xb, K, m, k0, h);
                     }
-                    quant16(h, fused_scale(m), d);
-                    if (blockIdx.x == 0 && p.xq_out) store_codes16<FAST>(p.xq_out, K, m, k0, d);
+                    quant16_t(h, fused_scale(m), e);
+                    if (blockIdx.x == 0 && p.xq_out) {
+                        uint32_t d[4];
+                        untranspose(e, d);
+                        store_codes16<FAST>(p.xq_out, K, m, k0, d);
+                    }
                 } else {
+                    uint32_t d[4];
                     const int8_t* src = p.xq + (int64_t)m * K + k0;
                     if (FAST) {
                         const uint4 v = k0 < K ? *reinterpret_cast<const uint4*>(src)
@@ -414,8 +454,9 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
                         for (int j = 0; j < 16; ++j)
                             if (k0 + j < K) d[j >> 2] |= (uint32_t)(uint8_t)src[j] << (8 * (j & 3));
                     }
+                    transpose4x4_bytes(d, e);
                 }
-                const int rs = row16_sum(put_group(x_lds, KSP, m, 16 * c + i, d));
+                const int rs = row16_sum(put_group_t(x_lds, KSP, m, 16 * c + i, e));
                 if (row_leader) atomicAdd(&s_wsum[wave * 16 + m], rs);
             }
             load_batch(wa, 0, stage_off, nch);
@@ -439,18 +480,34 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
                 compute_batch(wb, j0 + U, nch);
             }
         }
+    };
+    if constexpr (XH > 0) {
+        run_stage(0);  // a single K stage
+    } else {
+        for (int ks = 0; ks < p.Kp; ks += p.KS) run_stage(ks);
     }
 
     // ---- combine the four waves' partials and write the outputs ----
-    if (tid < M) {
+    // 1/a: v_rcp_f32 is within 1 ulp, and the rescale below stays within 3 ulp
+    if constexpr (MC == 1) {
+        if (FUSED && blockIdx.x == 0 && tid == 0 && p.a_out) p.a_out[0] = a_m1;
+    } else if (tid < M) {
         const float a = FUSED ? fused_scale(tid) : a_in;
         if (FUSED && blockIdx.x == 0 && p.a_out) p.a_out[tid] = a;
-        s_inva[tid] = 1.0f / a;
+        s_inva[tid] = __builtin_amdgcn_rcpf(a);
     }
-    {
+    if constexpr (MC == 1) {
+        // row 0 of the accumulators: register 0 of lanes 0-15
+        if (lane < 16) red[wave * 256 + lane] = acc1[0] + (acc4[0] >> 2) + (acc16[0] >> 4) - wsum_m1;
+    } else {
+        // this wave's partial minus the code sum of the activations it staged (its own
+        // LDS slot, so no barrier is needed to read it)
         const v4i t = acc1 + (acc4 >> 2) + (acc16 >> 4);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) red[(wave * 4 + r) * 64 + lane] = t[r];
+        for (int r = 0; r < 4; ++r) {
+            const int m = 4 * (lane >> 4) + r;
+            if (m < M) red[(wave * 4 + r) * 64 + lane] = t[r] - s_wsum[wave * 16 + m];
+        }
     }
     __syncthreads();
     if (tid < 16 * M) {
@@ -458,18 +515,19 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
         const int m = tid >> 4, col = tid & 15;
         const int l = 16 * (m >> 2) + col, r = m & 3;
         if (col < rows) {
-            int acc = -(s_wsum[m] + s_wsum[16 + m] + s_wsum[32 + m] + s_wsum[48 + m]);
+            int acc = 0;
 #pragma unroll
             for (int w = 0; w < kSkWaves; ++w) acc += red[(w * 4 + r) * 64 + l];
-            store_out(p.out, (int64_t)m * N + n0 + col, p.out_dtype, acc, ws_n, s_inva[m]);
+            const float inv_a = MC == 1 ? __builtin_amdgcn_rcpf(FUSED ? a_m1 : a_in) : s_inva[m];
+            store_out(p.out, (int64_t)m * N + n0 + col, p.out_dtype, acc, ws_n, inv_a);
         }
     }
 }
 
-template <bool FUSED, bool FAST, int XH, int U, bool SINGLE>
+template <bool FUSED, bool FAST, int XH, int U, bool SINGLE, int MC = 0>
 hipError_t launch_one(const SkinnyArgs& a, dim3 grid, size_t lds, hipStream_t stream) {
-    hipLaunchKernelGGL((skinny_kernel<FUSED, FAST, XH, U, SINGLE>), grid, dim3(kSkThreads), lds,
-                       stream, a);
+    hipLaunchKernelGGL((skinny_kernel<FUSED, FAST, XH, U, SINGLE, MC>), grid, dim3(kSkThreads),
+                       lds, stream, a);
     return hipGetLastError();
 }
 
@@ -488,6 +546,13 @@ template <bool FUSED>
 hipError_t launch_held(const SkinnyArgs& a, dim3 grid, size_t lds, hipStream_t stream) {
     const int cpw = (a.Kp / 256 + kSkWaves - 1) / kSkWaves;
     const int per_lane = (a.M * cpw + 3) / 4;
+    if (a.M == 1 && a.KS >= a.Kp) {
+        // one token (decode): the M = 1 specializations, by K
+        if (cpw <= 4) return launch_one<FUSED, true, 1, 4, true, 1>(a, grid, lds, stream);
+        if (cpw <= 8) return launch_one<FUSED, true, 2, 8, true, 1>(a, grid, lds, stream);
+        if (cpw <= 16) return launch_one<FUSED, true, 4, 8, false, 1>(a, grid, lds, stream);
+        if (cpw <= 32) return launch_one<FUSED, true, 8, 8, false, 1>(a, grid, lds, stream);
+    }
     if (a.KS >= a.Kp) {
         if (per_lane <= 1) return launch_fast<FUSED, 1>(a, grid, lds, stream);
         if (per_lane <= 2) return launch_fast<FUSED, 2>(a, grid, lds, stream);
