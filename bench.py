@@ -2,6 +2,7 @@
 """Benchmark of the W2A8 BitLinear hot path on one MI355X.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+python bench.py --traffic-probe   (launch pattern for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)
 
 A step is one BitNet-2B-shaped decode layer set at M = 1: the seven projections
 (q, k, v, o, gate, up, down; (N, K) = (2560,2560) (640,2560) (640,2560) (2560,2560)
@@ -12,9 +13,9 @@ unpack the packed weights, int8 x ternary dot with int32 accumulation, rescale.
 * Inputs are resident in HBM before timing.  The packed weights are replicated into
   enough copies to exceed 1 GiB and every step uses the next copy, so the weights come
   from HBM rather than the 256 MB Infinity Cache.
-* Each step's seven launches are captured in a HIP graph (one graph per weight copy)
-  so host launch overhead does not pace the GPU; W warmup steps, then exactly K steps
-  between two synchronizations timed with events.
+* Steps are captured in HIP graphs, ten consecutive steps (each on the next weight
+  copy) per graph, so host submission does not pace the GPU; W warmup steps, then
+  exactly K steps between two synchronizations timed with events.
 * value = packed-weight bytes of the set / step time (GB/s).
 * roofline: the fused quant+GEMV kernel, algorithmic bytes (N*K/4 packed bytes per
   launch) / its mean launch duration (a graph of back-to-back launches over the weight
@@ -53,6 +54,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--kernel-reps", type=int, default=5)
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="run the counter-collection launch pattern and exit (no timing)")
     return ap.parse_args()
 
 
@@ -108,37 +111,23 @@ def main():
     copies = [packed0] + [[p.clone() for p in packed0] for _ in range(R - 1)]
     torch.cuda.synchronize()
 
+    if args.traffic_probe:
+        traffic_probe(torch, bw, dev, layer, copies, scales, xs, outs)
+        return
+
     def launch_set(r):
         for i in range(len(layer)):
             bw.quant_gemv(xs[i], copies[r][i], scales[i], "f32", out=outs[i])
 
-    # one graph per weight copy: a step is one replay
-    graphs = []
+    # Steps are captured STEPS_PER_GRAPH at a time, each on the next weight copy, so the
+    # host's graph submissions never pace the GPU; one-step graphs cover the remainder.
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
         launch_set(0)  # eager warm-up on the capture stream
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    for r in range(R):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            launch_set(r)
-        graphs.append(g)
-    torch.cuda.synchronize()
-
-    # ---- timed region: W warmup steps, then exactly K steps ----
-    for i in range(args.warmup):
-        graphs[i % R].replay()
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for i in range(args.steps):
-        graphs[(args.warmup + i) % R].replay()
-    t1.record()
-    torch.cuda.synchronize()
-    ms_step = t0.elapsed_time(t1) / args.steps
+    ms_step = run_steps(torch, launch_set, R, args.warmup, args.steps)
     value = set_bytes / (ms_step * 1e-3) / 1e9
 
     # ---- per-launch kernel durations: one graph per shape holding R back-to-back
@@ -148,7 +137,7 @@ def main():
         for i in range(len(layer))]
     kern_us_total = sum(per_shape_us)
     achieved = set_bytes / (kern_us_total * 1e-6) / 1e9
-    kernel_hash = bw_build.source_hash()
+    kernel_hash = bw_build.kernel_hash("skinny.hip")
     traffic_bytes = load_traffic(kernel_hash)
     roofline = {
         "bound": "hbm",
@@ -157,7 +146,7 @@ def main():
         "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBS, 4),
         "traffic": traffic_bytes,
-        "kernel": "skinny_kernel<1,true,true> (fused quant+GEMV)",
+        "kernel": "skinny_kernel, fused quant+GEMV, M=1 specialization",
         "mean_launch_us": round(kern_us_total / len(layer), 3),
         "algorithmic_bytes_per_launch": set_bytes / len(layer),
         "per_shape_us": {name: round(us, 3) for (name, _, _), us in zip(layer, per_shape_us)},
@@ -197,6 +186,73 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)
+
+
+STEPS_PER_GRAPH = 10
+
+
+def run_steps(torch, launch_step, R, warmup, steps):
+    """Run `warmup` untimed steps, then time exactly `steps` steps (ms per step).
+
+    Step s uses weight copy s % R.  Steps run as graph replays: graphs of STEPS_PER_GRAPH
+    consecutive steps, then one-step graphs for what is left of `steps`."""
+    S = STEPS_PER_GRAPH
+
+    def capture(first, count):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for j in range(count):
+                launch_step((first + j) % R)
+        return g
+
+    # the sequence of (first step, count) replays for warmup + timed steps
+    def plan(first, count):
+        out = []
+        while count >= S:
+            out.append((first, S))
+            first += S
+            count -= S
+        out += [(first + j, 1) for j in range(count)]
+        return out
+
+    graphs = {}
+    warm, timed = plan(0, warmup), plan(warmup, steps)
+    for first, count in warm + timed:
+        key = (first % R, count)
+        if key not in graphs:
+            graphs[key] = capture(first % R, count)
+    torch.cuda.synchronize()
+    for first, count in warm:
+        graphs[(first % R, count)].replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for first, count in timed:
+        graphs[(first % R, count)].replay()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
+def traffic_probe(torch, bw, dev, layer, copies, scales, xs, outs):
+    """Launch pattern for the HBM counters: first three calibration launches of a plain
+    elementwise kernel that reads and writes a known number of bytes (torch.neg on int32,
+    profiling.COPY_BYTES each, twice the Infinity Cache), then the decode set once per
+    weight copy (so the weights come from HBM), eagerly."""
+    from ternary_weight_linear_token_amd import profiling
+    n = profiling.COPY_BYTES // 4
+    src = torch.arange(n, dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    for r in range(len(copies)):
+        for i in range(len(layer)):
+            bw.quant_gemv(xs[i], copies[r][i], scales[i], "f32", out=outs[i])
+    torch.cuda.synchronize()
+    print(f"[bench] traffic probe: {len(copies) * len(layer)} decode launches", file=sys.stderr)
 
 
 def graph_launch_us(torch, launch, R, reps):
@@ -254,24 +310,8 @@ def bench_gemm(bw, workloads, torch, np, dev, layer, R_bytes, reps):
     with torch.cuda.stream(side):
         step(0)
     torch.cuda.current_stream().wait_stream(side)
-    graphs = []
-    for r in range(R):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            step(r)
-        graphs.append(g)
-    for r in range(3):
-        graphs[r % R].replay()
     torch.cuda.synchronize()
-    steps = 40
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for i in range(steps):
-        graphs[i % R].replay()
-    t1.record()
-    torch.cuda.synchronize()
-    ms_step = t0.elapsed_time(t1) / steps
+    ms_step = run_steps(torch, step, R, 3, 40)
 
     per_shape_us = [graph_launch_us(torch, lambda r, i=i: bw.gemm(
         xqs[i], avs[i], copies[r][i], scales[i], "bf16", out=outs[i]), R, reps)
@@ -291,7 +331,7 @@ def bench_gemm(bw, workloads, torch, np, dev, layer, R_bytes, reps):
             "unit": "TFLOP/s",
             "frac": round(tops / INT8_MFMA_PEAK_TOPS, 4),
             "traffic": None,
-            "kernel": "tiled_kernel<128,128,true>",
+            "kernel": "tiled_kernel (per-shape tile plan)",
             "per_shape_us": {name: round(us, 3) for (name, _, _), us in zip(layer, per_shape_us)},
         },
     }

@@ -49,6 +49,18 @@ def source_hash() -> str:
     return h.hexdigest()
 
 
+def kernel_hash(*names: str) -> str:
+    """Hash of the named csrc files, the shared device header and the flags: identifies
+    the code of one kernel family (e.g. kernel_hash("skinny.hip"))."""
+    h = hashlib.sha256()
+    for name in list(names) + ["device_common.hpp"]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    h.update(" ".join(FLAGS).encode())
+    return h.hexdigest()
+
+
 def is_current() -> bool:
     if not os.path.exists(LIB_PATH) or not os.path.exists(HASH_PATH):
         return False

@@ -1,0 +1,175 @@
+"""Short text summaries of rocprofv3 runs, as kept next to the measured numbers.
+
+Kernel durations (a `rocprofv3 --kernel-trace --stats --output-format csv` run):
+
+    python -m ternary_weight_linear_token_amd.profiling kernels --dir DIR --out FILE --cmd "..."
+
+HBM traffic of the decode kernel (two `rocprofv3 --pmc` runs of `bench.py --traffic-probe`,
+one with FETCH_SIZE and one with WRITE_SIZE):
+
+    python -m ternary_weight_linear_token_amd.profiling traffic --fetch DIR1 --write DIR2 \
+        --out FILE --cmd "..."
+
+FETCH_SIZE and WRITE_SIZE read in KiB per dispatch.  They are scaled by what the same
+counters read for a plain elementwise kernel of known size that the probe runs first (it
+reads and writes COPY_BYTES each), so the reported bytes are in the units of that copy.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import glob
+import os
+import statistics
+import sys
+
+COPY_BYTES = 512 << 20    # bytes read (and written) by each calibration launch of the probe
+COPY_KERNEL = "elementwise"  # torch's elementwise kernel family (torch.neg on int32)
+COPY_TAG = "neg"
+
+
+def _short(name: str) -> str:
+    n = name.replace("bitnet::(anonymous namespace)::", "").replace("bitnet::", "")
+    n = n.replace("void ", "")
+    return n.split("(")[0] if "(" in n else n
+
+
+def _find(d: str, suffix: str) -> str:
+    hits = sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True))
+    if not hits:
+        raise FileNotFoundError(f"no *{suffix} under {d}")
+    return hits[0]
+
+
+def kernels(d: str, out: str, cmd: str) -> str:
+    trace = list(csv.DictReader(open(_find(d, "kernel_trace.csv"))))
+    stats = list(csv.DictReader(open(_find(d, "kernel_stats.csv"))))
+    lines = ["# rocprofv3 kernel summary", f"# command: {cmd}", "",
+             "## --stats (every dispatch of the run)",
+             f"{'kernel':72s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s}"]
+    for r in stats:
+        lines.append(f"{_short(r['Name'])[:72]:72s} {r['Calls']:>6s} "
+                     f"{float(r['AverageNs']) / 1e3:9.3f} {float(r['MinNs']) / 1e3:9.3f} "
+                     f"{float(r['MaxNs']) / 1e3:9.3f}")
+    lines += ["", "## library kernels per launch shape (kernel trace; grid in work-items)",
+              f"{'kernel':60s} {'grid':>8s} {'lds':>6s} {'n':>5s} {'mean_us':>9s} {'median_us':>9s}"]
+    agg = collections.defaultdict(list)
+    for r in trace:
+        if "bitnet" not in r["Kernel_Name"]:
+            continue
+        key = (_short(r["Kernel_Name"]), int(r["Grid_Size_X"]), int(r["LDS_Block_Size"]))
+        agg[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    for k, ds in sorted(agg.items()):
+        lines.append(f"{k[0][:60]:60s} {k[1]:8d} {k[2]:6d} {len(ds):5d} "
+                     f"{statistics.mean(ds):9.3f} {statistics.median(ds):9.3f}")
+    text = "\n".join(lines) + "\n"
+    with open(out, "w") as f:
+        f.write(text)
+    return text
+
+
+def _counter_rows(d: str, counter: str):
+    rows = []
+    for path in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter:
+                rows.append(r)
+    if not rows:
+        raise FileNotFoundError(f"no {counter} rows under {d}")
+    return rows
+
+
+def _per_dispatch(rows):
+    """{dispatch id: (kernel name, grid, value summed over the counter's instances)}"""
+    acc = {}
+    for r in rows:
+        key = r["Dispatch_Id"]
+        name, grid, val = r["Kernel_Name"], int(r["Grid_Size"]), float(r["Counter_Value"])
+        if key in acc:
+            acc[key] = (name, grid, acc[key][2] + val)
+        else:
+            acc[key] = (name, grid, val)
+    return acc
+
+
+def traffic(fetch_dir: str, write_dir: str, out: str, cmd: str, source_hash: str,
+            algorithmic_bytes: float) -> str:
+    fetch = _per_dispatch(_counter_rows(fetch_dir, "FETCH_SIZE"))
+    write = _per_dispatch(_counter_rows(write_dir, "WRITE_SIZE"))
+
+    def calib(table):
+        vals = [v for n, g, v in table.values()
+                if COPY_KERNEL in n and COPY_TAG in n and "bitnet" not in n]
+        if not vals:
+            raise RuntimeError("the calibration copy was not found in the counter output")
+        vals = vals[1:] if len(vals) > 1 else vals  # the first launch warms up
+        return COPY_BYTES / (statistics.median(vals) * 1024.0), len(vals)
+
+    f_fetch, n_cf = calib(fetch)
+    f_write, n_cw = calib(write)
+
+    def gemv(table):
+        by = collections.defaultdict(list)
+        for n, g, v in table.values():
+            if "skinny_kernel" in n:
+                by[(_short(n), g)].append(v * 1024.0)
+        return by
+
+    fb, wb = gemv(fetch), gemv(write)
+    lines = ["# HBM traffic of the fused quant+GEMV kernel, BitNet-2B decode set at M = 1",
+             f"# command: {cmd}",
+             f"# calibration: {COPY_BYTES} B read and written per copy launch; FETCH_SIZE reads "
+             f"{1 / f_fetch:.4f}x, WRITE_SIZE {1 / f_write:.4f}x of that ({n_cf}, {n_cw} launches)",
+             "# per shape: kernel, grid (work-items), launches, HBM read bytes, HBM write bytes "
+             "per launch (calibrated)"]
+    total_r, total_w, n_all = 0.0, 0.0, 0
+    for key in sorted(fb):
+        r = statistics.mean(fb[key]) * f_fetch
+        w = statistics.mean(wb.get(key, [0.0])) * f_write
+        cnt = len(fb[key])
+        lines.append(f"#   {key[0][:60]:60s} {key[1]:8d} {cnt:5d} {r:12.0f} {w:10.0f}")
+        total_r += r * cnt
+        total_w += w * cnt
+        n_all += cnt
+    per_launch = (total_r + total_w) / n_all
+    lines += [f"kernel_source_sha256 = {source_hash}",
+              f"fetch_calibration = {f_fetch:.6f}",
+              f"write_calibration = {f_write:.6f}",
+              f"hbm_read_bytes_per_launch = {total_r / n_all:.0f}",
+              f"hbm_write_bytes_per_launch = {total_w / n_all:.0f}",
+              f"hbm_bytes_per_launch = {per_launch:.0f}",
+              f"algorithmic_bytes_per_launch = {algorithmic_bytes:.0f}",
+              f"traffic_over_algorithmic = {per_launch / algorithmic_bytes:.4f}"]
+    text = "\n".join(lines) + "\n"
+    with open(out, "w") as f:
+        f.write(text)
+    return text
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(prog="python -m ternary_weight_linear_token_amd.profiling")
+    sub = ap.add_subparsers(dest="what", required=True)
+    k = sub.add_parser("kernels")
+    k.add_argument("--dir", required=True)
+    k.add_argument("--out", required=True)
+    k.add_argument("--cmd", required=True)
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--out", required=True)
+    t.add_argument("--cmd", required=True)
+    a = ap.parse_args(argv)
+    if a.what == "kernels":
+        sys.stdout.write(kernels(a.dir, a.out, a.cmd))
+    else:
+        from . import build
+        sys.path.insert(0, build.ROOT)
+        import workloads
+        layer = workloads.LAYER_2B
+        alg = sum(N * K // 4 for _, N, K in layer) / len(layer)
+        sys.stdout.write(traffic(a.fetch, a.write, a.out, a.cmd, build.kernel_hash("skinny.hip"), alg))
+
+
+if __name__ == "__main__":
+    main()
