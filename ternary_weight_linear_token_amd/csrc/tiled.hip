@@ -12,9 +12,12 @@
 //  * Loads are raw buffer loads through per-block descriptors whose range ends at the
 //    last valid row: rows past M or N read as zero without any branch, and per-stage
 //    offsets are scalar, so address arithmetic stays off the vector ALU.
-//  * Software pipeline: two register sets hold the loads of stages kt+1 and kt+2 while
-//    stage kt computes; every pair of stages issues the same loads (past-the-end stage
-//    indices are clamped and never computed), so only the older set is waited for.
+//  * Software pipeline: D register sets hold the loads of the next D stages; stages past
+//    the end read zeros through out-of-range buffer offsets, so every step issues the
+//    same loads and products and only the oldest set is waited for.  Within a step the
+//    matrix products are interleaved (scheduling-group hints) with the next step's
+//    weight unpack, loads and activation transpose, so the vector ALU work overlaps the
+//    matrix cores.
 //  * Operand A (activations) goes through LDS (double-buffered, one barrier per stage)
 //    with every aligned 16-byte k-group transposed as a 4x4 byte matrix (position
 //    4 r + b holds k = 4 b + r); rows padded to 80 bytes so the 128-bit fragment reads
@@ -86,14 +89,16 @@ __global__ __launch_bounds__(kTdThreads * G) void tiled_kernel(TiledArgs p) {
     // block's range with its own LDS buffers and registers; their accumulators are
     // combined through LDS at the end.  With G = 2 every SIMD holds two waves whose
     // memory, LDS and matrix-core phases interleave.
-    const int g = (int)threadIdx.x >> 8;
-    const int tid = threadIdx.x & 255, lane = tid & 63, wave = tid >> 6;
+    // group and wave indices are uniform per wave; readfirstlane tells the compiler so,
+    // which keeps the per-stage buffer offsets in scalar registers
+    const int g = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 8);
+    const int tid = threadIdx.x & 255, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     unsigned char (&a_lds)[2][BM * kAStride] = a_lds_all[g];
     const int M = p.M, N = p.N, K = p.K;
     const int64_t row_bytes = K / 4;
     const int nk = (K + kBK - 1) / kBK;
-    const int kt_begin = 0;
 
     for (int i = (int)threadIdx.x; i < BM; i += kTdThreads * G) {
         const int m = m0 + i;
@@ -127,15 +132,26 @@ __global__ __launch_bounds__(kTdThreads * G) void tiled_kernel(TiledArgs p) {
     uint4 a_reg[D][AV];
     uint2 b_reg[D][NB];
 
+    // Stage kt of K; a stage past the end (kt >= nk) reads as zeros: its scalar offset
+    // lies beyond both descriptors' ranges (the 32-bit sum with any in-range voffset
+    // cannot wrap), so the products it feeds add nothing.
     auto load_stage = [&](uint4 (&ar)[AV], uint2 (&br)[NB], int kt) {
-        const int k0 = kt * kBK;
+        const bool live = kt < nk;
+        const int k0 = live ? kt * kBK : 0;
         if (ALIGNED) {
+            const uint32_t sa = live ? (uint32_t)k0 : 0x80000000u;
+            const uint32_t sb = live ? (uint32_t)(k0 / 4) : 0x80000000u;
 #pragma unroll
             for (int j = 0; j < AV; ++j)
-                ar[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, a_voff[j], k0, 0));
+                ar[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, a_voff[j], sa, 0));
 #pragma unroll
             for (int j = 0; j < NB; ++j)
-                br[j] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(b_rsrc, b_voff[j], k0 / 4, 0));
+                br[j] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(b_rsrc, b_voff[j], sb, 0));
+        } else if (!live) {
+#pragma unroll
+            for (int j = 0; j < AV; ++j) ar[j] = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+            for (int j = 0; j < NB; ++j) br[j] = make_uint2(0u, 0u);
         } else {
             // K not a multiple of 64: byte loads, zero past the end of each row
 #pragma unroll
@@ -221,22 +237,34 @@ __global__ __launch_bounds__(kTdThreads * G) void tiled_kernel(TiledArgs p) {
     };
 
     // D register sets hold the loads of the next D stages.  Step t: read stage t's A
-    // fragments from LDS buffer t%2; while they are in flight, unpack stage t+1's weights
-    // (already in registers), refill register set t%D with the loads of stage t+D and
-    // move stage t+1's A into the other LDS buffer (last read before the previous
-    // barrier); then issue stage t's matrix products, which execute across the barrier
-    // and the next step's fragment reads.  One barrier per step.  Every full group of D
-    // steps issues the same loads (stage indices past the end are clamped and never
-    // computed), so the compiler waits only for the oldest set.  The loop runs whole
-    // groups, so the accumulators keep one live range; the remaining < D stages run in
-    // a tail without new loads.
-    // group g's stages: kt_begin + g + G*i for i < nk_g; the block runs nsteps steps
-    // (the largest nk_g) so all waves meet every barrier; a step past a group's last
-    // stage loads a clamped stage and skips its matrix products.
-    const int nk_g = nk > g ? (nk - g + G - 1) / G : 0;
+    // fragments from LDS buffer t%2, refill register set t%D with the loads of stage t+D,
+    // unpack stage t+1's weights (already in registers), move stage t+1's A into the
+    // other LDS buffer (last read before the previous barrier) and issue stage t's
+    // matrix products; one barrier per step.  Every full group of D steps issues the same
+    // loads, so the compiler waits only for the oldest set; the loop runs whole groups
+    // (the accumulators keep one live range) and the remaining < D steps run in a tail
+    // without new loads.
+    // Group g's stages are g, g + G, g + 2G, ...; every group runs nsteps steps, and a
+    // step past the group's last stage multiplies zeros (see load_stage), so the matrix
+    // products are unconditional and each step is one scheduling region.
     const int nsteps = (nk + G - 1) / G;
-    const int kt_last = kt_begin + max(nk, 1) - 1;
-    auto stage_of = [&](int i) { return min(kt_begin + g + G * i, kt_last); };
+    auto stage_of = [&](int i) { return g + G * i; };
+    // One step: the A fragments of this step are read first; then this step's matrix
+    // products are interleaved with the next step's weight unpack, the loads D steps
+    // ahead and the transposed store of the next step's activations, so the vector ALU
+    // and LDS work hides under the matrix cores.
+    constexpr int kMf = 2 * MB * NB;                               // products per step
+    constexpr int kVa = (2 * NB * 11 + AV * 8 + kMf - 1) / kMf;    // VALU per product
+    auto schedule_step = [&]() {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * MB, 0);   // A fragment reads
+        __builtin_amdgcn_sched_group_barrier(0x020, AV + NB, 0);  // loads D steps ahead
+#pragma unroll
+        for (int i = 0; i < kMf; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one product
+            __builtin_amdgcn_sched_group_barrier(0x002, kVa, 0);  // unpack / transpose
+        }
+        __builtin_amdgcn_sched_group_barrier(0x200, AV, 0);       // next A into LDS
+    };
 #pragma unroll
     for (int d = 0; d < D; ++d) load_stage(a_reg[d], b_reg[d], stage_of(d));
     store_stage(a_reg[0], 0);
@@ -249,10 +277,11 @@ __global__ __launch_bounds__(kTdThreads * G) void tiled_kernel(TiledArgs p) {
         for (int u = 0; u < D; ++u) {
             v4i A[2][MB];
             read_a(u & 1, A);
-            unpack_b(b_reg[(u + 1) % D], Bu[(u + 1) & 1]);
             load_stage(a_reg[u], b_reg[u], stage_of(it + u + D));
+            unpack_b(b_reg[(u + 1) % D], Bu[(u + 1) & 1]);
             store_stage(a_reg[(u + 1) % D], (u + 1) & 1);
-            if (G == 1 || it + u < nk_g) mfma_stage(A, Bu[u & 1]);
+            mfma_stage(A, Bu[u & 1]);
+            schedule_step();
             __syncthreads();
         }
     }
@@ -265,7 +294,7 @@ __global__ __launch_bounds__(kTdThreads * G) void tiled_kernel(TiledArgs p) {
             unpack_b(b_reg[u + 1], Bu[(u + 1) & 1]);
             store_stage(a_reg[u + 1], (u + 1) & 1);
         }
-        if (G == 1 || it + u < nk_g) mfma_stage(A, Bu[u & 1]);
+        mfma_stage(A, Bu[u & 1]);
         __syncthreads();
     }
 
