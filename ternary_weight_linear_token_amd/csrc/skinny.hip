@@ -45,6 +45,22 @@ namespace {
 #endif
 constexpr int kSkWaves = BITNET_SKINNY_WAVES;
 constexpr int kSkThreads = 64 * kSkWaves;
+#ifndef BITNET_SKINNY_RUN
+#define BITNET_SKINNY_RUN 2
+#endif
+// A wave takes runs of kSkRun consecutive 256-weight chunks (64 bytes of each row per
+// chunk), so its back-to-back loads cover whole 128-byte lines of every row.
+constexpr int kSkRun = BITNET_SKINNY_RUN;
+
+// j-th chunk of wave w: runs of kSkRun chunks, dealt to the waves in turn
+__host__ __device__ constexpr int chunk_of(int w, int j) {
+    return kSkRun * (w + kSkWaves * (j / kSkRun)) + j % kSkRun;
+}
+// number of chunks of a stage of nch chunks that wave w owns, and the largest over waves
+__host__ __device__ constexpr int chunks_of_wave(int w, int nch) {
+    const int span = kSkRun * kSkWaves, r = nch % span - kSkRun * w;
+    return (nch / span) * kSkRun + (r < 0 ? 0 : (r > kSkRun ? kSkRun : r));
+}
 constexpr int kSkXBudget = 48 * 1024;   // LDS bytes for the staged activations
 constexpr int kSkMisc = kSkWaves * 128 + 64;  // per-wave s_wmax, s_wsum [waves][16]; s_inva [16]
 constexpr uint32_t kOOB = 0x80000000u;  // buffer offset beyond every resource: reads 0
@@ -243,7 +259,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
     auto load_batch = [&](uint4 (&w)[U], int j0, int stage_off, int nch) {
 #pragma unroll
         for (int uu = 0; uu < U; ++uu) {
-            const int c = wave + kSkWaves * (j0 + uu);
+            const int c = chunk_of(wave, j0 + uu);
             const int cb = stage_off + c * 64;  // the chunk's first byte in the row
             if (FAST) {
                 const uint32_t off = (c < nch && cb + 16 * q < row_bytes) ? w_lane + cb : kOOB;
@@ -261,7 +277,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
     auto compute_batch = [&](const uint4 (&w)[U], int j0, int nch) {
 #pragma unroll
         for (int uu = 0; uu < U; ++uu) {
-            const int c = wave + kSkWaves * (j0 + uu);
+            const int c = chunk_of(wave, j0 + uu);
             // With M = 1 and one batch, chunks past the stage are multiplied as well: their
             // weights read as zeros and their operand-A reads stay inside the LDS block.
             if ((MC == 1 && SINGLE) || c < nch) {
@@ -315,7 +331,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
         i = g & 15;
         const int jm = g >> 4, j = jm / M;
         m = jm - j * M;
-        c = wave + kSkWaves * j;
+        c = chunk_of(wave, j);
     };
 
     uint4 wa[U];
@@ -414,7 +430,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
         const int stage_off = ks >> 2;
         if constexpr (XH == 0) {
             // ---- stage this wave's chunks of [ks, ks+len), all M rows, into LDS ----
-            const int cnt = M * ((nch - wave + kSkWaves - 1) / kSkWaves) * 16;
+            const int cnt = M * chunks_of_wave(wave, nch) * 16;
             for (int g = lane; g < cnt; g += 64) {  // the 16 lanes of a row stay together
                 int m, c, i;
                 group_of(g, m, c, i);
@@ -470,7 +486,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
         if constexpr (SINGLE) {
             compute_batch(wa, 0, nch);
         } else {
-            const int cpw = (nch + kSkWaves - 1) / kSkWaves;  // chunks per wave (upper bound)
+            const int cpw = chunks_of_wave(0, nch);  // chunks per wave (wave 0 has the most)
             uint4 wb[U];
             for (int j0 = 0; j0 < cpw; j0 += 2 * U) {
                 load_batch(wb, j0 + U, stage_off, nch);  // zeros when past the stage
@@ -534,7 +550,7 @@ hipError_t launch_one(const SkinnyArgs& a, dim3 grid, size_t lds, hipStream_t st
 // Batch shape: U = 4 or 8 chunks per wave; SINGLE when one batch holds a wave's share.
 template <bool FUSED, int XH>
 hipError_t launch_fast(const SkinnyArgs& a, dim3 grid, size_t lds, hipStream_t stream) {
-    const int cpw = (a.KS / 256 + kSkWaves - 1) / kSkWaves;
+    const int cpw = chunks_of_wave(0, a.KS / 256);
     const bool one_stage = a.KS >= a.Kp;
     if (one_stage && cpw <= 4) return launch_one<FUSED, true, XH, 4, true>(a, grid, lds, stream);
     if (one_stage && cpw <= 8) return launch_one<FUSED, true, XH, 8, true>(a, grid, lds, stream);
@@ -544,7 +560,7 @@ hipError_t launch_fast(const SkinnyArgs& a, dim3 grid, size_t lds, hipStream_t s
 // Held activation groups per lane: M * (chunks per wave) * 16 groups over 64 lanes.
 template <bool FUSED>
 hipError_t launch_held(const SkinnyArgs& a, dim3 grid, size_t lds, hipStream_t stream) {
-    const int cpw = (a.Kp / 256 + kSkWaves - 1) / kSkWaves;
+    const int cpw = chunks_of_wave(0, a.Kp / 256);
     const int per_lane = (a.M * cpw + 3) / 4;
     if (a.M == 1 && a.KS >= a.Kp) {
         // one token (decode): the M = 1 specializations, by K
