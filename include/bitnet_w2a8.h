@@ -70,12 +70,12 @@ typedef enum {
 } bitnet_out_dtype;
 
 typedef enum {
-    BITNET_ALGO_AUTO = 0,   /* choose by M                                            */
+    BITNET_ALGO_AUTO = 0,   /* SKINNY for M <= 16 (or M*N small), else TILED          */
     BITNET_ALGO_SKINNY = 1, /* weight-streaming kernel, M <= BITNET_SKINNY_MAX_M      */
     BITNET_ALGO_TILED = 2   /* tiled int8 matrix-core kernel, any M                    */
 } bitnet_algo;
 
-#define BITNET_SKINNY_MAX_M 16
+#define BITNET_SKINNY_MAX_M 64
 #define BITNET_GEMV_MAX_M 16
 
 /* ABI version of the loaded library (BITNET_ABI_VERSION at build time). */

@@ -16,7 +16,7 @@ from . import build as _build
 OUT_F32, OUT_BF16, OUT_I32 = 0, 1, 2
 ALGO_AUTO, ALGO_SKINNY, ALGO_TILED = 0, 1, 2
 GEMV_MAX_M = 16
-SKINNY_MAX_M = 16
+SKINNY_MAX_M = 64
 
 _OUT_TORCH = {OUT_F32: torch.float32, OUT_BF16: torch.bfloat16, OUT_I32: torch.int32}
 _OUT_NAMES = {"f32": OUT_F32, "float32": OUT_F32, "bf16": OUT_BF16, "bfloat16": OUT_BF16,
@@ -242,10 +242,13 @@ def quant_gemv(x, packed, w_scale, out_dtype="f32", out=None, return_quant=False
     return (out, xq, a_scale) if return_quant else out
 
 
+FUSED_MAX_M = 4  # above this, one quantization launch beats requantizing in every block
+
+
 def bitlinear(x, packed, w_scale, out_dtype="f32"):
-    """One BitLinear forward: fused quant+GEMV for M <= 16, else quant + GEMM."""
+    """One BitLinear forward: fused quant+GEMV for a few tokens, else quant + GEMM."""
     M = x.shape[0]
-    if M <= GEMV_MAX_M:
+    if M <= FUSED_MAX_M:
         return quant_gemv(x, packed, w_scale, out_dtype)
     xq, a_scale = quant_act(x)
     return gemm(xq, a_scale, packed, w_scale, out_dtype)

@@ -151,8 +151,10 @@ int bitnet_w2a8_gemm(const int8_t* xq, const float* a_scale, const uint8_t* pack
         !aligned16(out) || !aligned16(workspace))
         return BITNET_ERR_UNALIGNED;
     if ((st = check_device())) return st;
-    const bool skinny =
-        algo == BITNET_ALGO_SKINNY || (algo == BITNET_ALGO_AUTO && M <= BITNET_SKINNY_MAX_M);
+    // Auto: the weight-streaming kernel up to 16 tokens; from 17 to 64 tokens only while
+    // M * N is small, since each of its 16-row blocks stages all M x K activations.
+    const bool skinny_auto = M <= 16 || (M <= BITNET_SKINNY_MAX_M && M * N <= 262144);
+    const bool skinny = algo == BITNET_ALGO_SKINNY || (algo == BITNET_ALGO_AUTO && skinny_auto);
     if (skinny)
         return record_hip(bitnet::launch_skinny(xq, a_scale, nullptr, packed, w_scale, M, N, K,
                                                 out, out_dtype, nullptr, nullptr,

@@ -15,11 +15,18 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
     return __uint_as_float(h << 16);
 }
 
-// fp32 -> bf16 bit pattern, round to nearest, ties to even (finite inputs).
+// fp32 -> bf16 bit pattern, round to nearest, ties to even: the hardware conversion
+// (v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// Two fp32 values -> two bf16 (low half first), one conversion instruction.
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2_rne(float lo, float hi) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    const f2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b2));
 }
 
 // 4x4 byte transpose: d[b] holds bytes (b, 0..3) of a 16-byte group; on return e[i]

@@ -62,7 +62,8 @@ __host__ __device__ constexpr int chunks_of_wave(int w, int nch) {
     return (nch / span) * kSkRun + (r < 0 ? 0 : (r > kSkRun ? kSkRun : r));
 }
 constexpr int kSkXBudget = 48 * 1024;   // LDS bytes for the staged activations
-constexpr int kSkMisc = kSkWaves * 128 + 64;  // per-wave s_wmax, s_wsum [waves][16]; s_inva [16]
+constexpr int kSkMaxM = 64;                    // rows of activations (tokens) per launch
+constexpr int kSkMisc = kSkWaves * kSkMaxM * 8 + kSkMaxM * 4;  // s_wmax, s_wsum [waves][64]; s_inva [64]
 constexpr uint32_t kOOB = 0x80000000u;  // buffer offset beyond every resource: reads 0
 
 struct SkinnyArgs {
@@ -219,7 +220,8 @@ __device__ __forceinline__ void store_codes16(int8_t* xq_out, int K, int m, int 
 //  U      - weight chunks per wave per batch
 //  SINGLE - one batch covers a wave's whole share of K (single K stage)
 //  MC     - M fixed at compile time (1), or 0 for M read from the arguments
-template <bool FUSED, bool FAST, int XH, int U, bool SINGLE, int MC>
+//  MT     - 16-row tiles of tokens (M <= 16 MT); the weights of a chunk feed all of them
+template <bool FUSED, bool FAST, int XH, int U, bool SINGLE, int MC, int MT = 1>
 __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
     extern __shared__ __align__(16) unsigned char smem[];
     const int KSP = p.KS + 16;  // padded LDS row stride: spreads rows over the banks
@@ -229,9 +231,9 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
     // per-wave partial results: s_wmax[w][m] = max |x| bits seen by wave w in row m,
     // s_wsum[w][m] = sum of the codes of row m staged by wave w
     uint32_t* s_wmax = reinterpret_cast<uint32_t*>(smem + M * KSP);
-    int* s_wsum = reinterpret_cast<int*>(s_wmax + 16 * kSkWaves);
-    float* s_inva = reinterpret_cast<float*>(s_wsum + 16 * kSkWaves);
-    int* red = reinterpret_cast<int*>(smem + M * KSP + kSkMisc);  // [waves][4][64]
+    int* s_wsum = reinterpret_cast<int*>(s_wmax + kSkMaxM * kSkWaves);
+    float* s_inva = reinterpret_cast<float*>(s_wsum + kSkMaxM * kSkWaves);
+    int* red = reinterpret_cast<int*>(smem + M * KSP + kSkMisc);  // [waves][MT][4][64]
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
     const int row_bytes = K / 4;
@@ -239,7 +241,6 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
     const int rows = min(16, N - n0);
     const int mrow = lane & 15;  // operand-A row (token) and operand-B column of this lane
     const int q = lane >> 4;     // k-group of this lane inside a 256-weight chunk
-    const bool a_active = mrow < M;
     const bool row_leader = (lane & 15) == 0;
 
     // scales needed at the end, requested first (threads tid < 16 M write outputs)
@@ -272,7 +273,9 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
         }
     };
 
-    v4i acc1 = v4i{0, 0, 0, 0}, acc4 = acc1, acc16 = acc1;
+    v4i acc1[MT], acc4[MT], acc16[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc1[t] = acc4[t] = acc16[t] = v4i{0, 0, 0, 0};
 
     auto compute_batch = [&](const uint4 (&w)[U], int j0, int nch) {
 #pragma unroll
@@ -281,15 +284,6 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
             // With M = 1 and one batch, chunks past the stage are multiplied as well: their
             // weights read as zeros and their operand-A reads stay inside the LDS block.
             if ((MC == 1 && SINGLE) || c < nch) {
-                v4i A[4];
-                if (a_active) {
-                    const unsigned char* src = x_lds + mrow * KSP + (c * 4 + q) * 64;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) A[i] = *reinterpret_cast<const v4i*>(src + 16 * i);
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) A[i] = v4i{0, 0, 0, 0};
-                }
                 const uint32_t w4[4] = {w[uu].x, w[uu].y, w[uu].z, w[uu].w};
                 v4i b0, b1, b2, b3;
 #pragma unroll
@@ -299,24 +293,34 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
                     b2[r] = (int)(w4[r] & 0x30303030u);
                     b3[r] = (int)((w4[r] >> 2) & 0x30303030u);
                 }
-                acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[0], b0, acc1, 0, 0, 0);
-                acc4 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[1], b1, acc4, 0, 0, 0);
-                acc16 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2], b2, acc16, 0, 0, 0);
-                acc16 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[3], b3, acc16, 0, 0, 0);
+#pragma unroll
+                for (int t = 0; t < MT; ++t) {  // the unpacked weights feed every token tile
+                    v4i A[4];
+                    if (16 * t + mrow < M) {
+                        const unsigned char* src = x_lds + (16 * t + mrow) * KSP + (c * 4 + q) * 64;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) A[i] = *reinterpret_cast<const v4i*>(src + 16 * i);
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) A[i] = v4i{0, 0, 0, 0};
+                    }
+                    acc1[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[0], b0, acc1[t], 0, 0, 0);
+                    acc4[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[1], b1, acc4[t], 0, 0, 0);
+                    acc16[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2], b2, acc16[t], 0, 0, 0);
+                    acc16[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[3], b3, acc16[t], 0, 0, 0);
+                }
             }
         }
     };
 
     // each wave clears its own slots (LDS operations of one wave complete in order)
-    if (lane < 16) {
-        s_wmax[wave * 16 + lane] = 0u;
-        s_wsum[wave * 16 + lane] = 0;
-    }
+    s_wmax[wave * kSkMaxM + lane] = 0u;  // one slot per token row (64 = lanes)
+    s_wsum[wave * kSkMaxM + lane] = 0;
     // the activation scale 127 / max|x| of token m from the waves' maxima
     auto fused_scale = [&](int m) -> float {
         uint32_t mx = s_wmax[m];
 #pragma unroll
-        for (int w = 1; w < kSkWaves; ++w) mx = max(mx, s_wmax[16 * w + m]);
+        for (int w = 1; w < kSkWaves; ++w) mx = max(mx, s_wmax[kSkMaxM * w + m]);
         float amax = bf16_bits_to_f32(mx);
         amax = amax < 1e-5f ? 1e-5f : amax;
         return 127.0f / amax;
@@ -368,14 +372,14 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
 #pragma unroll
                 for (int t = 0; t < XH; ++t) mx = max(mx, absmax_bits16(held[t]));  // 0 if unused
                 mx = wave_max_uniform(mx);
-                if (lane == 0) s_wmax[wave * 16] = mx;
+                if (lane == 0) s_wmax[wave * kSkMaxM] = mx;
             } else {
 #pragma unroll
                 for (int t = 0; t < XH; ++t) {
                     int m, c, i;
                     group_of(lane + 64 * t, m, c, i);
                     const uint32_t mx = row16_max(absmax_bits16(held[t]));
-                    if (row_leader && c < nch0) atomicMax(&s_wmax[wave * 16 + m], mx);
+                    if (row_leader && c < nch0) atomicMax(&s_wmax[wave * kSkMaxM + m], mx);
                 }
             }
             __syncthreads();
@@ -403,7 +407,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
                 rsum += rs;
             } else {
                 rs = row16_sum(rs);
-                if (row_leader && c < nch0) atomicAdd(&s_wsum[wave * 16 + m], rs);
+                if (row_leader && c < nch0) atomicAdd(&s_wsum[wave * kSkMaxM + m], rs);
             }
         }
         if (MC == 1) wsum_m1 = wave_sum_uniform(rsum);
@@ -419,7 +423,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
                 mx = max(mx, max(max(a & 0xFFFFu, a >> 16), max(b & 0xFFFFu, b >> 16)));
             }
             mx = row16_max(mx);
-            if (row_leader) atomicMax(&s_wmax[wave * 16 + m], mx);
+            if (row_leader) atomicMax(&s_wmax[wave * kSkMaxM + m], mx);
         }
         __syncthreads();
     }
@@ -430,50 +434,66 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
         const int stage_off = ks >> 2;
         if constexpr (XH == 0) {
             // ---- stage this wave's chunks of [ks, ks+len), all M rows, into LDS ----
+            // SB groups per lane are requested together (unconditional buffer loads, zeros
+            // past K or past the wave's groups) before any of them is used.
             const int cnt = M * chunks_of_wave(wave, nch) * 16;
-            for (int g = lane; g < cnt; g += 64) {  // the 16 lanes of a row stay together
-                int m, c, i;
-                group_of(g, m, c, i);
-                const int k0 = ks + 256 * c + 16 * i;
-                uint32_t e[4];
-                if constexpr (FUSED) {
-                    uint32_t h[8];
+            constexpr int SB = FUSED ? 4 : 8;
+            constexpr int XW = FUSED ? 8 : 4;
+            const __amdgpu_buffer_rsrc_t x_rsrc =
+                FUSED ? make_rsrc(p.xb, (uint32_t)(M * K * 2)) : make_rsrc(p.xq, (uint32_t)(M * K));
+            for (int g0 = lane; g0 < cnt; g0 += 64 * SB) {  // the 16 lanes of a row stay together
+                uint32_t h[SB][XW];
+#pragma unroll
+                for (int b = 0; b < SB; ++b) {
+                    int m, c, i;
+                    group_of(g0 + 64 * b, m, c, i);
+                    const int k0 = ks + 256 * c + 16 * i;
+                    const bool ok = g0 + 64 * b < cnt && k0 < K;
                     if (FAST) {
-                        if (k0 < K) {
-                            const uint4* src = reinterpret_cast<const uint4*>(p.xb + (int64_t)m * K + k0);
-                            const uint4 v0 = src[0], v1 = src[1];
-                            h[0] = v0.x; h[1] = v0.y; h[2] = v0.z; h[3] = v0.w;
-                            h[4] = v1.x; h[5] = v1.y; h[6] = v1.z; h[7] = v1.w;
+                        if constexpr (FUSED) {
+                            const uint32_t off = ok ? (uint32_t)((m * K + k0) * 2) : kOOB;
+                            const uint4 v0 = buf_load16(x_rsrc, off), v1 = buf_load16(x_rsrc, off + 16);
+                            h[b][0] = v0.x; h[b][1] = v0.y; h[b][2] = v0.z; h[b][3] = v0.w;
+                            h[b][4] = v1.x; h[b][5] = v1.y; h[b][6] = v1.z; h[b][7] = v1.w;
                         } else {
-#pragma unroll
-                            for (int j = 0; j < 8; ++j) h[j] = 0u;
+                            const uint4 v = buf_load16(x_rsrc, ok ? (uint32_t)(m * K + k0) : kOOB);
+                            h[b][0] = v.x; h[b][1] = v.y; h[b][2] = v.z; h[b][3] = v.w;
                         }
-                    } else {
-                        load_x16_bf16_elems(p.xb, K, m, k0, h);
-                    }
-                    quant16_t(h, fused_scale(m), e);
-                    if (blockIdx.x == 0 && p.xq_out) {
-                        uint32_t d[4];
-                        untranspose(e, d);
-                        store_codes16<FAST>(p.xq_out, K, m, k0, d);
-                    }
-                } else {
-                    uint32_t d[4];
-                    const int8_t* src = p.xq + (int64_t)m * K + k0;
-                    if (FAST) {
-                        const uint4 v = k0 < K ? *reinterpret_cast<const uint4*>(src)
-                                               : make_uint4(0u, 0u, 0u, 0u);
-                        d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
-                    } else {
-                        d[0] = d[1] = d[2] = d[3] = 0u;
+                    } else if (g0 + 64 * b < cnt) {
+                        if constexpr (FUSED) {
+                            load_x16_bf16_elems(p.xb, K, m, k0, h[b]);
+                        } else {
+                            const int8_t* src = p.xq + (int64_t)m * K + k0;
+                            uint32_t d[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-                        for (int j = 0; j < 16; ++j)
-                            if (k0 + j < K) d[j >> 2] |= (uint32_t)(uint8_t)src[j] << (8 * (j & 3));
+                            for (int j = 0; j < 16; ++j)
+                                if (k0 + j < K) d[j >> 2] |= (uint32_t)(uint8_t)src[j] << (8 * (j & 3));
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) h[b][j] = d[j];
+                        }
                     }
-                    transpose4x4_bytes(d, e);
                 }
-                const int rs = row16_sum(put_group_t(x_lds, KSP, m, 16 * c + i, e));
-                if (row_leader) atomicAdd(&s_wsum[wave * 16 + m], rs);
+#pragma unroll
+                for (int b = 0; b < SB; ++b) {
+                    if (g0 + 64 * b < cnt) {  // uniform over the 16 lanes of a row
+                        int m, c, i;
+                        group_of(g0 + 64 * b, m, c, i);
+                        const int k0 = ks + 256 * c + 16 * i;
+                        uint32_t e[4];
+                        if constexpr (FUSED) {
+                            quant16_t(h[b], fused_scale(m), e);
+                            if (blockIdx.x == 0 && p.xq_out) {
+                                uint32_t d[4];
+                                untranspose(e, d);
+                                store_codes16<FAST>(p.xq_out, K, m, k0, d);
+                            }
+                        } else {
+                            transpose4x4_bytes(h[b], e);
+                        }
+                        const int rs = row16_sum(put_group_t(x_lds, KSP, m, 16 * c + i, e));
+                        if (row_leader) atomicAdd(&s_wsum[wave * kSkMaxM + m], rs);
+                    }
+                }
             }
             load_batch(wa, 0, stage_off, nch);
         }
@@ -514,35 +534,59 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
     }
     if constexpr (MC == 1) {
         // row 0 of the accumulators: register 0 of lanes 0-15
-        if (lane < 16) red[wave * 256 + lane] = acc1[0] + (acc4[0] >> 2) + (acc16[0] >> 4) - wsum_m1;
+        if (lane < 16) red[wave * 256 + lane] = acc1[0][0] + (acc4[0][0] >> 2) + (acc16[0][0] >> 4) - wsum_m1;
     } else {
-        // this wave's partial minus the code sum of the activations it staged (its own
-        // LDS slot, so no barrier is needed to read it)
-        const v4i t = acc1 + (acc4 >> 2) + (acc16 >> 4);
+        // this wave's partials minus the code sums of the activations it staged (its own
+        // LDS slots, so no barrier is needed to read them)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int m = 4 * (lane >> 4) + r;
-            if (m < M) red[(wave * 4 + r) * 64 + lane] = t[r] - s_wsum[wave * 16 + m];
+        for (int t = 0; t < MT; ++t) {
+            const v4i v = acc1[t] + (acc4[t] >> 2) + (acc16[t] >> 4);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = 16 * t + 4 * (lane >> 4) + r;
+                if (m < M) red[((wave * MT + t) * 4 + r) * 64 + lane] = v[r] - s_wsum[wave * kSkMaxM + m];
+            }
         }
     }
     __syncthreads();
-    if (tid < 16 * M) {
+    for (int idx = tid; idx < 16 * M; idx += kSkThreads) {
         // 16x16 int32 accumulator layout: lane l, register r -> row 4*(l/16)+r, column l%16
-        const int m = tid >> 4, col = tid & 15;
-        const int l = 16 * (m >> 2) + col, r = m & 3;
+        const int m = idx >> 4, col = idx & 15;
+        const int t = m >> 4, ml = m & 15;
+        const int l = 16 * (ml >> 2) + col, r = ml & 3;
         if (col < rows) {
             int acc = 0;
 #pragma unroll
-            for (int w = 0; w < kSkWaves; ++w) acc += red[(w * 4 + r) * 64 + l];
+            for (int w = 0; w < kSkWaves; ++w) acc += red[((w * MT + t) * 4 + r) * 64 + l];
             const float inv_a = MC == 1 ? __builtin_amdgcn_rcpf(FUSED ? a_m1 : a_in) : s_inva[m];
-            store_out(p.out, (int64_t)m * N + n0 + col, p.out_dtype, acc, ws_n, inv_a);
+            // the first pass holds its column's weight scale (loaded early); later passes
+            // (M > 16) read it again
+            const float wsc = idx == tid ? ws_n : p.w_scale[n0 + col];
+            store_out(p.out, (int64_t)m * N + n0 + col, p.out_dtype, acc, wsc, inv_a);
         }
     }
 }
 
-template <bool FUSED, bool FAST, int XH, int U, bool SINGLE, int MC = 0>
+// Dynamic LDS beyond the default 64 KB limit must be granted per kernel (once per device).
+template <typename Kernel>
+hipError_t allow_lds(Kernel* kernel, size_t lds) {
+    if (lds <= 65536) return hipSuccess;
+    static int granted[64] = {0};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < 64 && granted[dev]) return hipSuccess;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e == hipSuccess && dev >= 0 && dev < 64) granted[dev] = 1;
+    return e;
+}
+
+template <bool FUSED, bool FAST, int XH, int U, bool SINGLE, int MC = 0, int MT = 1>
 hipError_t launch_one(const SkinnyArgs& a, dim3 grid, size_t lds, hipStream_t stream) {
-    hipLaunchKernelGGL((skinny_kernel<FUSED, FAST, XH, U, SINGLE, MC>), grid, dim3(kSkThreads),
+    const hipError_t e = allow_lds(&skinny_kernel<FUSED, FAST, XH, U, SINGLE, MC, MT>, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((skinny_kernel<FUSED, FAST, XH, U, SINGLE, MC, MT>), grid, dim3(kSkThreads),
                        lds, stream, a);
     return hipGetLastError();
 }
@@ -604,6 +648,26 @@ hipError_t launch_skinny(const int8_t* xq, const float* a_scale, const uint16_t*
     const size_t lds = (size_t)M * (a.KS + 16) + kSkMisc + (size_t)kSkWaves * 4 * 64 * 4;
     const dim3 grid((unsigned)((N + 15) / 16));
     const bool fused = x_bf16 != nullptr;
+    if (M > 16) {
+        if (fused) return hipErrorInvalidValue;  // the fused entry point takes M <= 16
+        // 17..64 tokens (int8 input only): 2 or 4 token tiles per chunk of weights.  The
+        // activations of a K stage sit in LDS (up to 160 KB); a stage holds at least one
+        // full round of chunk runs, so that every wave has work.
+        const int mt = M <= 32 ? 2 : 4;
+        const size_t red_bytes = (size_t)kSkWaves * mt * 4 * 64 * 4;
+        const size_t budget = 160 * 1024 - kSkMisc - red_bytes;
+        constexpr int round = 256 * kSkRun * kSkWaves;  // weights per round of chunk runs
+        int kst = (int)((budget / M - 16) / round) * round;
+        if (kst < round) kst = round;
+        a.KS = kst < a.Kp ? kst : a.Kp;
+        const size_t lds_m = (size_t)M * (a.KS + 16) + kSkMisc + red_bytes;
+        if (K % 64 != 0) {
+            if (mt == 2) return launch_one<false, false, 0, 4, false, 0, 2>(a, grid, lds_m, stream);
+            return launch_one<false, false, 0, 4, false, 0, 4>(a, grid, lds_m, stream);
+        }
+        if (mt == 2) return launch_one<false, true, 0, 4, false, 0, 2>(a, grid, lds_m, stream);
+        return launch_one<false, true, 0, 4, false, 0, 4>(a, grid, lds_m, stream);
+    }
     if (K % 64 != 0) {
         if (fused) return launch_one<true, false, 0, 4, false>(a, grid, lds, stream);
         return launch_one<false, false, 0, 4, false>(a, grid, lds, stream);

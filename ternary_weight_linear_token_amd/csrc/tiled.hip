@@ -347,9 +347,7 @@ __global__ __launch_bounds__(kTdThreads * G) void tiled_kernel(TiledArgs p) {
                     } else {
                         uint32_t h[8];
 #pragma unroll
-                        for (int t = 0; t < 8; ++t)
-                            h[t] = (uint32_t)f32_to_bf16_rne(f[2 * t]) |
-                                   ((uint32_t)f32_to_bf16_rne(f[2 * t + 1]) << 16);
+                        for (int t = 0; t < 8; ++t) h[t] = f32x2_to_bf16x2_rne(f[2 * t], f[2 * t + 1]);
                         uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) + o);
                         dst[0] = make_uint4(h[0], h[1], h[2], h[3]);
                         dst[1] = make_uint4(h[4], h[5], h[6], h[7]);

@@ -106,7 +106,7 @@ def test_gemv_validation(L):
 def test_gemm_validation(L):
     f = L.bitnet_w2a8_gemm
     assert f(A, B, C, D, 64, 16, 256, E, 0, 7, None, 0, None) == INVALID     # bad algo
-    assert f(A, B, C, D, 64, 16, 256, E, 0, 1, None, 0, None) == INVALID     # skinny with M > 16
+    assert f(A, B, C, D, 65, 16, 256, E, 0, 1, None, 0, None) == INVALID     # skinny with M > 64
     assert f(A, B, C, D, 64, 16, 256, E, 5, 0, None, 0, None) == INVALID     # bad dtype
     assert f(A, B, C, D, 64, 16, 256, E, 0, 0, F + 8, 16, None) == UNALIGNED
     assert f(A, B, C, D, 64, 16, 256, E, 0, 0, None, 16, None) == INVALID    # bytes but no buffer

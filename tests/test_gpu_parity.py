@@ -120,6 +120,18 @@ def test_gemm_matches_oracle(algo, M, N, K):
         check_out(to_np(out), o["acc"], o["ref"], dt, f"gemm {algo} M={M} N={N} K={K} {dt}")
 
 
+@pytest.mark.parametrize("M", [17, 31, 32, 33, 48, 64])
+@pytest.mark.parametrize("N,K", [(37, 260), (300, 1024), (129, 6912), (16, 8448)])
+def test_skinny_token_tiles_match_oracle(M, N, K):
+    """17..64 tokens: two or four 16-row token tiles per chunk of weights, K in several
+    LDS stages for the larger M."""
+    pb = Problem(M, N, K, seed=M * 7000 + N + K)
+    xq, a, packed, s, o = product_inputs(pb)
+    for dt in DT:
+        out = bw.gemm(xq, a, packed, s, dt, algo="skinny")
+        check_out(to_np(out), o["acc"], o["ref"], dt, f"skinny M={M} N={N} K={K} {dt}")
+
+
 @pytest.mark.parametrize("M", [1, 3, 16])
 @pytest.mark.parametrize("N,K", [(16, 256), (300, 1024), (37, 260), (50, 6912)])
 def test_quant_gemv_matches_oracle(M, N, K):
@@ -210,6 +222,19 @@ def test_tiny_workload_chain(dt):
     for out in (bw.gemv(xq, a, packed, s, dt), bw.gemm(xq, a, packed, s, dt, algo="tiled"),
                 bw.quant_gemv(pb.x_dev, packed, s, dt), bw.bitlinear(pb.x_dev, packed, s, dt)):
         check_out(to_np(out), o["acc"], o["ref"], dt, f"tiny chain {dt}")
+
+
+@pytest.mark.parametrize("M", [1, 4, 5, 16, 17, 40, 64, 65, 200])
+def test_bitlinear_every_route(M):
+    # bitlinear picks the fused decode launch, or quantization plus the skinny or tiled
+    # product, by M and N; every route must give the oracle's result.
+    for N, K in ((300, 1024), (4096, 256)):
+        pb = Problem(M, N, K, seed=M * 11 + N)
+        o = pb.oracle()
+        packed, s = dev(o["packed"]), dev(o["w_scale"])
+        for dt in DT:
+            out = bw.bitlinear(pb.x_dev, packed, s, dt)
+            check_out(to_np(out), o["acc"], o["ref"], dt, f"bitlinear M={M} N={N} K={K} {dt}")
 
 
 def test_graph_replay_matches_eager():
