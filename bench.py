@@ -25,6 +25,9 @@ unpack the packed weights, int8 x ternary dot with int32 accumulation, rescale.
   GEMM, bf16 out), int8 TOPS against 5.0 POPS dense.
 * cpu_baseline: the CPU oracle on the host cores (test infrastructure, timed only
   here), on the same decode step repeated for ~10 s.
+* extras: the same per-launch rooflines at large shapes, where the bandwidth and
+  matrix-core bars are reachable: the 70B-shaped decode layer set (M = 1) and the
+  8B-shaped prefill MLP GEMMs (M = 2048).
 """
 from __future__ import annotations
 
@@ -54,6 +57,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--kernel-reps", type=int, default=5)
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the 70B-shaped decode and 8B-shaped prefill rooflines")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run the counter-collection launch pattern and exit (no timing)")
     return ap.parse_args()
@@ -159,6 +164,9 @@ def main():
     # ---- CPU oracle baseline ----
     cpu = None if args.no_cpu_baseline else cpu_baseline(workloads, layer, args.cpu_seconds)
 
+    # ---- the shapes where the bandwidth and matrix-core bars are reachable ----
+    extras = None if args.no_extras else bench_extras(bw, workloads, torch, dev, args.kernel_reps)
+
     result = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -184,6 +192,7 @@ def main():
         "roofline": roofline,
         "gemm": gemm,
         "cpu_baseline": cpu,
+        "extras": extras,
     }
     print(json.dumps(result), flush=True)
 
@@ -277,6 +286,58 @@ def graph_launch_us(torch, launch, R, reps):
     t1.record()
     torch.cuda.synchronize()
     return t0.elapsed_time(t1) * 1e3 / (reps * R)
+
+
+def bench_extras(bw, workloads, torch, dev, reps):
+    """Per-launch rooflines at large shapes: the 70B-shaped decode layer set (M = 1, fused
+    quant + GEMV, packed GB/s against 8 TB/s) and the 8B-shaped prefill MLP GEMMs
+    (M = 2048, quant excluded, int8 TOPS against 5.0 POPS).  Same method as the
+    headline: graphs of back-to-back launches over weight copies rotated past 1 GiB."""
+    out = {}
+    print("[bench] 70B-shaped decode set, M=1", file=sys.stderr, flush=True)
+    per, tot_b, tot_us = {}, 0, 0.0
+    for name, N, K in workloads.LAYER_70B:
+        W = workloads.latent_weights(N, K, seed=0).to(dev)
+        p, s = bw.pack_weights(W)
+        del W
+        R = max(2, math.ceil(ROTATE_BYTES / (N * K // 4)))
+        copies = [p] + [p.clone() for _ in range(R - 1)]
+        x = workloads.activations(1, K, seed=0, outliers=True).to(dev)
+        o = torch.empty((1, N), dtype=torch.float32, device=dev)
+        us = graph_launch_us(torch, lambda r: bw.quant_gemv(x, copies[r], s, "f32", out=o), R, reps)
+        per[name] = {"us": round(us, 3), "GB/s": round(N * K / 4 / us / 1e3, 1)}
+        tot_b += N * K // 4
+        tot_us += us
+        del copies, p
+        torch.cuda.empty_cache()
+    out["decode_70b_m1"] = {"bound": "hbm", "achieved": round(tot_b / tot_us / 1e3, 1),
+                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": round(tot_b / tot_us / 1e3 / HBM_PEAK_GBS, 4),
+                            "packed_bytes": tot_b, "per_shape": per}
+    print("[bench] 8B-shaped prefill MLP, M=2048", file=sys.stderr, flush=True)
+    M, per, tot_ops, tot_us = 2048, {}, 0.0, 0.0
+    for name, N, K in workloads.LAYER_8B:
+        if name not in ("gate", "down"):
+            continue
+        W = workloads.latent_weights(N, K, seed=0).to(dev)
+        p, s = bw.pack_weights(W)
+        del W
+        R = max(2, math.ceil(ROTATE_BYTES / (N * K // 4)))
+        copies = [p] + [p.clone() for _ in range(R - 1)]
+        xq, a = bw.quant_act(workloads.activations(M, K, seed=0, outliers=True).to(dev))
+        o = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        us = graph_launch_us(torch, lambda r: bw.gemm(xq, a, copies[r], s, "bf16", out=o), R, reps)
+        ops = 2.0 * M * N * K
+        per[name] = {"us": round(us, 3), "TFLOP/s": round(ops / us / 1e6, 1)}
+        tot_ops += ops
+        tot_us += us
+        del copies, p
+        torch.cuda.empty_cache()
+    out["prefill_8b_m2048"] = {"bound": "mfma", "achieved": round(tot_ops / tot_us / 1e6, 1),
+                               "peak": INT8_MFMA_PEAK_TOPS, "unit": "TFLOP/s",
+                               "frac": round(tot_ops / tot_us / 1e6 / INT8_MFMA_PEAK_TOPS, 4),
+                               "per_shape": per}
+    return out
 
 
 def bench_gemm(bw, workloads, torch, np, dev, layer, R_bytes, reps):
