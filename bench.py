@@ -6,9 +6,11 @@ python bench.py --traffic-probe   (launch pattern for rocprofv3 --pmc FETCH_SIZE
 
 A step is one BitNet-2B-shaped decode layer set at M = 1: the seven projections
 (q, k, v, o, gate, up, down; (N, K) = (2560,2560) (640,2560) (640,2560) (2560,2560)
-(6912,2560) (6912,2560) (2560,6912)), each one fused quant + GEMV launch (bf16
-activations in, fp32 out), i.e. every step of the path: absmax, quantize, stream and
-unpack the packed weights, int8 x ternary dot with int32 accumulation, rescale.
+(6912,2560) (6912,2560) (2560,6912)), bf16 activations in, fp32 out, every step of the
+path: absmax, quantize, stream and unpack the packed weights, int8 x ternary dot with
+int32 accumulation, rescale.  Projections that read the same activations share one
+fused quant + GEMV launch (q|k|v, o, gate|up, down: four launches); the same set with
+one launch per projection is reported beside it (value_ungrouped).
 
 * Inputs are resident in HBM before timing.  The packed weights are replicated into
   enough copies to exceed 1 GiB and every step uses the next copy, so the weights come
@@ -19,8 +21,8 @@ unpack the packed weights, int8 x ternary dot with int32 accumulation, rescale.
 * value = packed-weight bytes of the set / step time (GB/s).
 * roofline: the fused quant+GEMV kernel, algorithmic bytes (N*K/4 packed bytes per
   launch) / its mean launch duration (a graph of back-to-back launches over the weight
-  copies, timed with events), against 8 TB/s; traffic from the committed rocprofv3 counter summary when it matches the
-  current kernel source.
+  copies, timed with events), against 8 TB/s; traffic from the committed rocprofv3
+  counter summary when it matches the current kernel source.
 * gemm: the BitNet-2B-shaped prefill set at M = 512 (quant kernel + tiled int8-MFMA
   GEMM, bf16 out), int8 TOPS against 5.0 POPS dense.
 * cpu_baseline: the CPU oracle on the host cores (test infrastructure, timed only
@@ -103,6 +105,8 @@ def main():
     print(f"[bench] packing {len(layer)} 2B-shaped projections", file=sys.stderr, flush=True)
 
     packed0, scales, xs, outs = [], [], [], []
+    index = {name: i for i, (name, _, _) in enumerate(layer)}
+    groups = [[index[n] for n in grp] for grp in workloads.DECODE_GROUPS]
     for name, N, K in layer:
         W = workloads.latent_weights(N, K, seed=0).to(dev)
         p, s = bw.pack_weights(W)
@@ -116,13 +120,25 @@ def main():
     copies = [packed0] + [[p.clone() for p in packed0] for _ in range(R - 1)]
     torch.cuda.synchronize()
 
-    if args.traffic_probe:
-        traffic_probe(torch, bw, dev, layer, copies, scales, xs, outs)
-        return
+    def launch_group(r, grp):
+        if len(grp) == 1:
+            i = grp[0]
+            bw.quant_gemv(xs[i], copies[r][i], scales[i], "f32", out=outs[i])
+        else:
+            bw.quant_gemv_grouped(xs[grp[0]], [copies[r][i] for i in grp],
+                                  [scales[i] for i in grp], "f32", out=[outs[i] for i in grp])
 
     def launch_set(r):
+        for grp in groups:
+            launch_group(r, grp)
+
+    def launch_set_ungrouped(r):
         for i in range(len(layer)):
             bw.quant_gemv(xs[i], copies[r][i], scales[i], "f32", out=outs[i])
+
+    if args.traffic_probe:
+        traffic_probe(torch, launch_set, R, dev)
+        return
 
     # Steps are captured STEPS_PER_GRAPH at a time, each on the next weight copy, so the
     # host's graph submissions never pace the GPU; one-step graphs cover the remainder.
@@ -134,13 +150,16 @@ def main():
     torch.cuda.synchronize()
     ms_step = run_steps(torch, launch_set, R, args.warmup, args.steps)
     value = set_bytes / (ms_step * 1e-3) / 1e9
+    ms_step_ungrouped = run_steps(torch, launch_set_ungrouped, R, args.warmup, args.steps)
 
-    # ---- per-launch kernel durations: one graph per shape holding R back-to-back
+    # ---- per-launch kernel durations: one graph per launch holding R back-to-back
     # launches (one per weight copy); event time of the replay / R ----
+    per_group_us = [graph_launch_us(torch, lambda r, grp=grp: launch_group(r, grp), R,
+                                    args.kernel_reps) for grp in groups]
     per_shape_us = [graph_launch_us(torch, lambda r, i=i: bw.quant_gemv(
         xs[i], copies[r][i], scales[i], "f32", out=outs[i]), R, args.kernel_reps)
         for i in range(len(layer))]
-    kern_us_total = sum(per_shape_us)
+    kern_us_total = sum(per_group_us)
     achieved = set_bytes / (kern_us_total * 1e-6) / 1e9
     kernel_hash = bw_build.kernel_hash("skinny.hip")
     traffic_bytes = load_traffic(kernel_hash)
@@ -152,9 +171,14 @@ def main():
         "frac": round(achieved / HBM_PEAK_GBS, 4),
         "traffic": traffic_bytes,
         "kernel": "skinny_kernel, fused quant+GEMV, M=1 specialization",
-        "mean_launch_us": round(kern_us_total / len(layer), 3),
-        "algorithmic_bytes_per_launch": set_bytes / len(layer),
-        "per_shape_us": {name: round(us, 3) for (name, _, _), us in zip(layer, per_shape_us)},
+        "launches_per_step": len(groups),
+        "mean_launch_us": round(kern_us_total / len(groups), 3),
+        "algorithmic_bytes_per_launch": set_bytes / len(groups),
+        "per_launch_us": {"|".join(grp): round(us, 3)
+                          for grp, us in zip(workloads.DECODE_GROUPS, per_group_us)},
+        "ungrouped_per_shape_us": {name: round(us, 3)
+                                   for (name, _, _), us in zip(layer, per_shape_us)},
+        "ungrouped_achieved": round(set_bytes / (sum(per_shape_us) * 1e-6) / 1e9, 1),
     }
 
     # ---- prefill GEMM, M = 512 ----
@@ -184,7 +208,11 @@ def main():
             "workload": "bitnet-2b-decode-layer-set",
             "M": 1,
             "shapes_NK": [[N, K] for _, N, K in layer],
-            "entry": "bitnet_quant_gemv (fused quant + GEMV), fp32 out, HIP graph per step",
+            "entry": "bitnet_quant_gemv_grouped / bitnet_quant_gemv (fused quant + GEMV), "
+                     "fp32 out, HIP graphs of steps",
+            "launches": ["|".join(grp) for grp in workloads.DECODE_GROUPS],
+            "value_ungrouped": round(set_bytes / (ms_step_ungrouped * 1e-3) / 1e9, 1),
+            "ms_per_step_ungrouped": round(ms_step_ungrouped, 5),
             "packed_bytes_per_step": set_bytes,
             "weight_copies_rotated": R,
             "frac_hbm_peak": round(value / HBM_PEAK_GBS, 4),
@@ -244,10 +272,10 @@ def run_steps(torch, launch_step, R, warmup, steps):
     return t0.elapsed_time(t1) / steps
 
 
-def traffic_probe(torch, bw, dev, layer, copies, scales, xs, outs):
+def traffic_probe(torch, launch_set, R, dev):
     """Launch pattern for the HBM counters: first three calibration launches of a plain
     elementwise kernel that reads and writes a known number of bytes (torch.neg on int32,
-    profiling.COPY_BYTES each, twice the Infinity Cache), then the decode set once per
+    profiling.COPY_BYTES each, twice the Infinity Cache), then the decode step once per
     weight copy (so the weights come from HBM), eagerly."""
     from ternary_weight_linear_token_amd import profiling
     n = profiling.COPY_BYTES // 4
@@ -257,11 +285,10 @@ def traffic_probe(torch, bw, dev, layer, copies, scales, xs, outs):
         torch.neg(src, out=dst)
     torch.cuda.synchronize()
     del src, dst
-    for r in range(len(copies)):
-        for i in range(len(layer)):
-            bw.quant_gemv(xs[i], copies[r][i], scales[i], "f32", out=outs[i])
+    for r in range(R):
+        launch_set(r)
     torch.cuda.synchronize()
-    print(f"[bench] traffic probe: {len(copies) * len(layer)} decode launches", file=sys.stderr)
+    print(f"[bench] traffic probe: {R} decode steps", file=sys.stderr)
 
 
 def graph_launch_us(torch, launch, R, reps):
@@ -295,25 +322,36 @@ def bench_extras(bw, workloads, torch, dev, reps):
     headline: graphs of back-to-back launches over weight copies rotated past 1 GiB."""
     out = {}
     print("[bench] 70B-shaped decode set, M=1", file=sys.stderr, flush=True)
+    shapes = {name: (N, K) for name, N, K in workloads.LAYER_70B}
     per, tot_b, tot_us = {}, 0, 0.0
-    for name, N, K in workloads.LAYER_70B:
-        W = workloads.latent_weights(N, K, seed=0).to(dev)
-        p, s = bw.pack_weights(W)
-        del W
-        R = max(2, math.ceil(ROTATE_BYTES / (N * K // 4)))
-        copies = [p] + [p.clone() for _ in range(R - 1)]
+    for grp in workloads.DECODE_GROUPS:
+        K = shapes[grp[0]][1]
+        ps, ss = [], []
+        for name in grp:
+            W = workloads.latent_weights(shapes[name][0], K, seed=0).to(dev)
+            p, s = bw.pack_weights(W)
+            del W
+            ps.append(p)
+            ss.append(s)
+        nbytes = sum(shapes[name][0] * K // 4 for name in grp)
+        R = max(2, math.ceil(ROTATE_BYTES / nbytes))
+        copies = [ps] + [[p.clone() for p in ps] for _ in range(R - 1)]
         x = workloads.activations(1, K, seed=0, outliers=True).to(dev)
-        o = torch.empty((1, N), dtype=torch.float32, device=dev)
-        us = graph_launch_us(torch, lambda r: bw.quant_gemv(x, copies[r], s, "f32", out=o), R, reps)
-        per[name] = {"us": round(us, 3), "GB/s": round(N * K / 4 / us / 1e3, 1)}
-        tot_b += N * K // 4
+        os_ = [torch.empty((1, shapes[name][0]), dtype=torch.float32, device=dev) for name in grp]
+        if len(grp) == 1:
+            launch = lambda r: bw.quant_gemv(x, copies[r][0], ss[0], "f32", out=os_[0])
+        else:
+            launch = lambda r: bw.quant_gemv_grouped(x, copies[r], ss, "f32", out=os_)
+        us = graph_launch_us(torch, launch, R, reps)
+        per["|".join(grp)] = {"us": round(us, 3), "GB/s": round(nbytes / us / 1e3, 1)}
+        tot_b += nbytes
         tot_us += us
-        del copies, p
+        del copies, ps
         torch.cuda.empty_cache()
     out["decode_70b_m1"] = {"bound": "hbm", "achieved": round(tot_b / tot_us / 1e3, 1),
                             "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": round(tot_b / tot_us / 1e3 / HBM_PEAK_GBS, 4),
-                            "packed_bytes": tot_b, "per_shape": per}
+                            "packed_bytes": tot_b, "per_launch": per}
     print("[bench] 8B-shaped prefill MLP, M=2048", file=sys.stderr, flush=True)
     M, per, tot_ops, tot_us = 2048, {}, 0.0, 0.0
     for name, N, K in workloads.LAYER_8B:

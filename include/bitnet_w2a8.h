@@ -77,6 +77,8 @@ typedef enum {
 
 #define BITNET_SKINNY_MAX_M 64
 #define BITNET_GEMV_MAX_M 16
+/* Most weight matrices one grouped launch takes (bitnet_quant_gemv_grouped). */
+#define BITNET_MAX_GROUPS 4
 
 /* ABI version of the loaded library (BITNET_ABI_VERSION at build time). */
 int bitnet_abi_version(void);
@@ -155,6 +157,29 @@ int bitnet_w2a8_gemm(const int8_t* xq, const float* a_scale, const uint8_t* pack
 int bitnet_quant_gemv(const uint16_t* x, const uint8_t* packed, const float* w_scale,
                       int64_t M, int64_t N, int64_t K, void* out, int out_dtype,
                       int8_t* xq_out, float* a_scale_out, void* stream);
+
+/*
+ * bitnet_quant_gemv_grouped -- bitnet_quant_gemv for several weight matrices that read
+ * the same activations, in one launch.  In the model of "BitNet 深度实战" §3.2 (a LLaMA
+ * block with every nn.Linear replaced by BitLinear) q, k and v project the same hidden
+ * states, and so do the MLP's gate and up projections.
+ *   x                : bf16 (M, K) as uint16, 1 <= M <= BITNET_GEMV_MAX_M, shared.
+ *   groups           : 1 <= groups <= BITNET_MAX_GROUPS.
+ *   packed, w_scale, N, out : HOST arrays of `groups` entries, read during the call only;
+ *                      entry g describes one product exactly as bitnet_quant_gemv's
+ *                      packed (N[g], K/4), w_scale (N[g]) and out (M, N[g]) arguments
+ *                      (device pointers, caller-owned).  N[g] == 0 is allowed and
+ *                      touches nothing of that entry.
+ *   out_dtype        : one output type for every group.
+ *   xq_out, a_scale_out : optional copies of the quantized activations, as in
+ *                      bitnet_quant_gemv (written once).
+ * Each out[g] is bit-identical to bitnet_quant_gemv on entry g alone.  Output buffers
+ * must not overlap one another or any input.
+ */
+int bitnet_quant_gemv_grouped(const uint16_t* x, int64_t M, int64_t K, int64_t groups,
+                              const uint8_t* const* packed, const float* const* w_scale,
+                              const int64_t* N, void* const* out, int out_dtype,
+                              int8_t* xq_out, float* a_scale_out, void* stream);
 
 #ifdef __cplusplus
 }

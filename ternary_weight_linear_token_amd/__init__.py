@@ -11,6 +11,7 @@ from ._binding import (  # noqa: F401
     ALGO_SKINNY,
     ALGO_TILED,
     GEMV_MAX_M,
+    MAX_GROUPS,
     OUT_BF16,
     OUT_F32,
     OUT_I32,
@@ -25,6 +26,7 @@ from ._binding import (  # noqa: F401
     pack_weights,
     quant_act,
     quant_gemv,
+    quant_gemv_grouped,
     status_str,
     unpack_weights,
 )

@@ -17,6 +17,7 @@ OUT_F32, OUT_BF16, OUT_I32 = 0, 1, 2
 ALGO_AUTO, ALGO_SKINNY, ALGO_TILED = 0, 1, 2
 GEMV_MAX_M = 16
 SKINNY_MAX_M = 64
+MAX_GROUPS = 4
 
 _OUT_TORCH = {OUT_F32: torch.float32, OUT_BF16: torch.bfloat16, OUT_I32: torch.int32}
 _OUT_NAMES = {"f32": OUT_F32, "float32": OUT_F32, "bf16": OUT_BF16, "bfloat16": OUT_BF16,
@@ -61,6 +62,7 @@ def lib():
             "bitnet_w2a8_gemm_workspace_size": ([i64, i64, i64], ctypes.c_size_t),
             "bitnet_w2a8_gemm": ([p, p, p, p, i64, i64, i64, p, i32, i32, p, ctypes.c_size_t, p], i32),
             "bitnet_quant_gemv": ([p, p, p, i64, i64, i64, p, i32, p, p, p], i32),
+            "bitnet_quant_gemv_grouped": ([p, i64, i64, i64, p, p, p, p, i32, p, p, p], i32),
         }
         for name, (args, res) in sigs.items():
             fn = getattr(L, name)
@@ -240,6 +242,43 @@ def quant_gemv(x, packed, w_scale, out_dtype="f32", out=None, return_quant=False
                                    _opt_ptr(a_scale, torch.float32, "a_scale_out", (M,)), _stream(x)),
            "bitnet_quant_gemv")
     return (out, xq, a_scale) if return_quant else out
+
+
+def quant_gemv_grouped(x, packed, w_scale, out_dtype="f32", out=None, return_quant=False):
+    """quant_gemv for up to MAX_GROUPS weight matrices that read the same x, one launch.
+
+    packed / w_scale: sequences of equal length; returns the list of (M, N_g) outputs."""
+    M, K = x.shape
+    G = len(packed)
+    if len(w_scale) != G:
+        raise ValueError("packed and w_scale must have the same length")
+    code = _out_code(out_dtype)
+    Ns = [int(pk.shape[0]) for pk in packed]
+    outs = list(out) if out is not None else [None] * G
+    if len(outs) != G:
+        raise ValueError("out must have one tensor per group")
+    outs = [_alloc_out(o, M, n, code, x.device) for o, n in zip(outs, Ns)]
+    P = (ctypes.c_void_p * max(G, 1))(*[_tensor(pk, torch.uint8, f"packed[{g}]", (Ns[g], K // 4))
+                                        for g, pk in enumerate(packed)])
+    S = (ctypes.c_void_p * max(G, 1))(*[_tensor(sc, torch.float32, f"w_scale[{g}]", (Ns[g],))
+                                        for g, sc in enumerate(w_scale)])
+    O = (ctypes.c_void_p * max(G, 1))(*[_tensor(o, _OUT_TORCH[code], f"out[{g}]", (M, Ns[g]))
+                                        for g, o in enumerate(outs)])
+    NN = (ctypes.c_int64 * max(G, 1))(*Ns)
+    xq = a_scale = None
+    if return_quant:
+        xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
+        a_scale = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _check(lib().bitnet_quant_gemv_grouped(_tensor(x, torch.bfloat16, "x", (M, K)), M, K, G,
+                                           ctypes.cast(P, ctypes.c_void_p),
+                                           ctypes.cast(S, ctypes.c_void_p),
+                                           ctypes.cast(NN, ctypes.c_void_p),
+                                           ctypes.cast(O, ctypes.c_void_p), code,
+                                           _opt_ptr(xq, torch.int8, "xq_out", (M, K)),
+                                           _opt_ptr(a_scale, torch.float32, "a_scale_out", (M,)),
+                                           _stream(x)),
+           "bitnet_quant_gemv_grouped")
+    return (outs, xq, a_scale) if return_quant else outs
 
 
 FUSED_MAX_M = 4  # above this, one quantization launch beats requantizing in every block

@@ -180,4 +180,35 @@ int bitnet_quant_gemv(const uint16_t* x, const uint8_t* packed, const float* w_s
                                             out_dtype, xq_out, a_scale_out, as_stream(stream)));
 }
 
+int bitnet_quant_gemv_grouped(const uint16_t* x, int64_t M, int64_t K, int64_t groups,
+                              const uint8_t* const* packed, const float* const* w_scale,
+                              const int64_t* N, void* const* out, int out_dtype,
+                              int8_t* xq_out, float* a_scale_out, void* stream) {
+    if (!valid_dtype(out_dtype)) return BITNET_ERR_INVALID_ARG;
+    if (groups < 1 || groups > BITNET_MAX_GROUPS) return BITNET_ERR_INVALID_ARG;
+    if (!packed || !w_scale || !N || !out) return BITNET_ERR_INVALID_ARG;
+    int64_t total_n = 0;
+    for (int64_t g = 0; g < groups; ++g) {
+        int st = check_shape(M, N[g], K);
+        if (st) return st;
+        total_n += N[g];
+    }
+    if (M > BITNET_GEMV_MAX_M) return BITNET_ERR_INVALID_ARG;
+    if (total_n > INT32_MAX) return BITNET_ERR_INVALID_ARG;
+    if (M == 0 || total_n == 0) return BITNET_OK;
+    if (!x) return BITNET_ERR_INVALID_ARG;
+    for (int64_t g = 0; g < groups; ++g) {
+        if (N[g] == 0) continue;
+        if (!packed[g] || !w_scale[g] || !out[g]) return BITNET_ERR_INVALID_ARG;
+        if (!aligned16(packed[g]) || !aligned16(w_scale[g]) || !aligned16(out[g]))
+            return BITNET_ERR_UNALIGNED;
+    }
+    if (!aligned16(x) || !aligned16(xq_out) || !aligned16(a_scale_out)) return BITNET_ERR_UNALIGNED;
+    int st = check_device();
+    if (st) return st;
+    return record_hip(bitnet::launch_skinny_grouped(nullptr, nullptr, x, (int)groups, packed,
+                                                    w_scale, N, out, M, K, out_dtype, xq_out,
+                                                    a_scale_out, as_stream(stream)));
+}
+
 }  // extern "C"

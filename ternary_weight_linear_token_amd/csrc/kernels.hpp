@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "bitnet_w2a8.h"
+
 namespace bitnet {
 
 hipError_t launch_pack_weights(const float* w, int64_t N, int64_t K, uint8_t* packed,
@@ -20,6 +22,13 @@ hipError_t launch_skinny(const int8_t* xq, const float* a_scale, const uint16_t*
                          const uint8_t* packed, const float* w_scale, int64_t M, int64_t N,
                          int64_t K, void* out, int out_dtype, int8_t* xq_out, float* a_out,
                          hipStream_t stream);
+// The same product for 1 <= groups <= BITNET_MAX_GROUPS weight matrices (N[g] rows each,
+// all K columns) against the same activations, in one launch.
+hipError_t launch_skinny_grouped(const int8_t* xq, const float* a_scale, const uint16_t* x_bf16,
+                                 int groups, const uint8_t* const* packed,
+                                 const float* const* w_scale, const int64_t* N,
+                                 void* const* out, int64_t M, int64_t K, int out_dtype,
+                                 int8_t* xq_out, float* a_out, hipStream_t stream);
 
 // Tiled int8 matrix-core product for any M.  `workspace` must hold
 // tiled_workspace_size(M, N, K) bytes whose counter area is zero (it is left zero).

@@ -12,19 +12,60 @@
 namespace bitnet {
 
 // ---------------------------------------------------------------- weight scale ---
-// One thread per output row: the absmean is an fp64 sum over k in ascending order
-// (a fixed order, so the scale is reproducible bit for bit), divided by K, rounded
-// once to fp32 and clamped below at 1e-5.  Offline work: simplicity over speed.
+// The absmean of each row is an fp64 sum over k in ascending order (a fixed order, so
+// the scale is reproducible bit for bit), divided by K, rounded once to fp32 and clamped
+// below at 1e-5.  A block owns kScRows rows: its four waves load 64-column tiles of
+// them with coalesced 16-byte reads into LDS, and lane r of the first wave adds row r's
+// 64 values of the tile in order while the next tile is already in flight.
+constexpr int kScRows = 64, kScCols = 64, kScStride = kScCols + 1;
+
 __global__ __launch_bounds__(256) void weight_scale_kernel(const float* __restrict__ w,
                                                            int64_t N, int64_t K,
                                                            float* __restrict__ scale) {
-    int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (n >= N) return;
-    const float* row = w + n * K;
+    __shared__ float tile[kScRows * kScStride];
+    const int tid = threadIdx.x;
+    const int64_t r0 = (int64_t)blockIdx.x * kScRows;
+    const int rows = (int)min((int64_t)kScRows, N - r0);
+    const int64_t ntiles = (K + kScCols - 1) / kScCols;
+    // thread tid moves the 16-byte pieces p = tid + 256 j (row p / 16, columns 4 (p % 16) ..)
+    constexpr int kPieces = kScRows * kScCols / 4 / 256;
+    float4 held[kPieces];
+    auto load = [&](int64_t t) {
+#pragma unroll
+        for (int j = 0; j < kPieces; ++j) {
+            const int piece = tid + 256 * j, row = piece >> 4;
+            const int64_t col = t * kScCols + 4 * (piece & 15);
+            // K % 4 == 0: a piece is either wholly inside the row or wholly past its end
+            held[j] = (row < rows && col < K)
+                          ? *reinterpret_cast<const float4*>(w + (r0 + row) * K + col)
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    };
     double sum = 0.0;
-    for (int64_t k = 0; k < K; ++k) sum += fabs((double)row[k]);
-    float s = (float)(sum / (double)K);
-    scale[n] = s < 1e-5f ? 1e-5f : s;
+    load(0);
+    for (int64_t t = 0; t < ntiles; ++t) {
+        __syncthreads();  // the previous tile has been summed
+#pragma unroll
+        for (int j = 0; j < kPieces; ++j) {
+            const int piece = tid + 256 * j;
+            float* dst = &tile[(piece >> 4) * kScStride + 4 * (piece & 15)];
+            dst[0] = held[j].x;
+            dst[1] = held[j].y;
+            dst[2] = held[j].z;
+            dst[3] = held[j].w;
+        }
+        __syncthreads();
+        if (t + 1 < ntiles) load(t + 1);
+        if (tid < kScRows) {
+            const int cols = (int)min((int64_t)kScCols, K - t * kScCols);
+            const float* src = &tile[tid * kScStride];
+            for (int c = 0; c < cols; ++c) sum += fabs((double)src[c]);
+        }
+    }
+    if (tid < rows) {
+        const float s = (float)(sum / (double)K);
+        scale[r0 + tid] = s < 1e-5f ? 1e-5f : s;
+    }
 }
 
 // ---------------------------------------------------------------- weight codes ---
@@ -137,8 +178,8 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restri
 hipError_t launch_pack_weights(const float* w, int64_t N, int64_t K, uint8_t* packed,
                                float* scale, hipStream_t stream) {
     dim3 blk(256);
-    hipLaunchKernelGGL(weight_scale_kernel, dim3((unsigned)((N + 255) / 256)), blk, 0, stream, w,
-                       N, K, scale);
+    hipLaunchKernelGGL(weight_scale_kernel, dim3((unsigned)((N + kScRows - 1) / kScRows)), blk, 0,
+                       stream, w, N, K, scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     int64_t total = N * (K / 4);

@@ -33,6 +33,11 @@
 //  * Per-row maxima and code sums are reduced per wave (wave reductions at M = 1, atomics
 //    on the wave's own LDS slots otherwise), so no block-wide atomic is contended.
 //  * Per-wave int32 partials are combined through LDS; one pass writes the outputs.
+//  * Grouped launches: up to kSkGroups weight matrices that read the same activations
+//    (q, k and v of an attention block; gate and up of an MLP) share one launch.  The
+//    grid is the concatenation of the groups' row blocks; a block picks its group with
+//    scalar compares of its index, so each group costs exactly what it costs alone,
+//    minus one launch.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -66,16 +71,33 @@ constexpr int kSkMaxM = 64;                    // rows of activations (tokens) p
 constexpr int kSkMisc = kSkWaves * kSkMaxM * 8 + kSkMaxM * 4;  // s_wmax, s_wsum [waves][64]; s_inva [64]
 constexpr uint32_t kOOB = 0x80000000u;  // buffer offset beyond every resource: reads 0
 
+// a[i] for a wave-uniform i < 4, as scalar selects (no indexed copy of the kernel
+// arguments)
+template <typename T>
+__device__ __forceinline__ T pick(const T (&a)[4], int i) {
+    T r = a[0];
+    r = i == 1 ? a[1] : r;
+    r = i == 2 ? a[2] : r;
+    r = i == 3 ? a[3] : r;
+    return r;
+}
+
+constexpr int kSkGroups = BITNET_MAX_GROUPS;
+
 struct SkinnyArgs {
     const int8_t* xq;
     const float* a_scale;
     const uint16_t* xb;
-    const uint8_t* packed;
-    const float* w_scale;
-    void* out;
     int8_t* xq_out;
     float* a_out;
-    int M, N, K;
+    // group g owns the blocks first[g] .. first[g + 1] - 1 (groups with no rows own none)
+    int groups;
+    int first[kSkGroups];
+    int g_N[kSkGroups];
+    const uint8_t* g_packed[kSkGroups];
+    const float* g_wscale[kSkGroups];
+    void* g_out[kSkGroups];
+    int M, K;
     int Kp;  // K rounded up to a multiple of 256
     int KS;  // K-stage length staged in LDS at once (multiple of 256)
     int out_dtype;
@@ -226,7 +248,16 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
     extern __shared__ __align__(16) unsigned char smem[];
     const int KSP = p.KS + 16;  // padded LDS row stride: spreads rows over the banks
     const int M = MC > 0 ? MC : p.M;
-    const int N = p.N, K = p.K;
+    const int K = p.K;
+    // this block's group: uniform, resolved with scalar selects
+    int gi = 0;
+#pragma unroll
+    for (int i = 1; i < kSkGroups; ++i)
+        if (i < p.groups && (int)blockIdx.x >= p.first[i]) gi = i;
+    const int N = pick(p.g_N, gi);
+    const uint8_t* const packed = pick(p.g_packed, gi);
+    const float* const w_scale = pick(p.g_wscale, gi);
+    void* const out = pick(p.g_out, gi);
     unsigned char* x_lds = smem;
     // per-wave partial results: s_wmax[w][m] = max |x| bits seen by wave w in row m,
     // s_wsum[w][m] = sum of the codes of row m staged by wave w
@@ -237,14 +268,14 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
     const int row_bytes = K / 4;
-    const int n0 = blockIdx.x * 16;
+    const int n0 = ((int)blockIdx.x - pick(p.first, gi)) * 16;
     const int rows = min(16, N - n0);
     const int mrow = lane & 15;  // operand-A row (token) and operand-B column of this lane
     const int q = lane >> 4;     // k-group of this lane inside a 256-weight chunk
     const bool row_leader = (lane & 15) == 0;
 
     // scales needed at the end, requested first (threads tid < 16 M write outputs)
-    const float ws_n = buf_load_f32(make_rsrc(p.w_scale + n0, (uint32_t)(rows * 4)),
+    const float ws_n = buf_load_f32(make_rsrc(w_scale + n0, (uint32_t)(rows * 4)),
                                     tid < 16 * M ? (uint32_t)(4 * (tid & 15)) : kOOB);
     float a_in = 0.0f;  // M = 1: every thread holds the token's scale
     if constexpr (!FUSED)
@@ -253,7 +284,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
 
     // the block's weight rows (fewer than 16 at the end of N); reads past them give 0
     const __amdgpu_buffer_rsrc_t w_rsrc =
-        make_rsrc(p.packed + (int64_t)n0 * row_bytes, (uint32_t)(rows * row_bytes));
+        make_rsrc(packed + (int64_t)n0 * row_bytes, (uint32_t)(rows * row_bytes));
     const uint32_t w_lane = (uint32_t)(mrow * row_bytes + 16 * q);
 
     // chunks c = wave + 4 * (j0 + uu), uu < U, of the stage starting at byte stage_off
@@ -267,7 +298,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
                 w[uu] = buf_load16(w_rsrc, off);
             } else {
                 const int n = n0 + mrow;
-                w[uu] = (n < N && c < nch) ? load_w16_bytes(p.packed, row_bytes, n, cb + 16 * q)
+                w[uu] = (n < N && c < nch) ? load_w16_bytes(packed, row_bytes, n, cb + 16 * q)
                                            : make_uint4(0u, 0u, 0u, 0u);
             }
         }
@@ -561,8 +592,8 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
             const float inv_a = MC == 1 ? __builtin_amdgcn_rcpf(FUSED ? a_m1 : a_in) : s_inva[m];
             // the first pass holds its column's weight scale (loaded early); later passes
             // (M > 16) read it again
-            const float wsc = idx == tid ? ws_n : p.w_scale[n0 + col];
-            store_out(p.out, (int64_t)m * N + n0 + col, p.out_dtype, acc, wsc, inv_a);
+            const float wsc = idx == tid ? ws_n : w_scale[n0 + col];
+            store_out(out, (int64_t)m * N + n0 + col, p.out_dtype, acc, wsc, inv_a);
         }
     }
 }
@@ -628,17 +659,36 @@ hipError_t launch_skinny(const int8_t* xq, const float* a_scale, const uint16_t*
                          const uint8_t* packed, const float* w_scale, int64_t M, int64_t N,
                          int64_t K, void* out, int out_dtype, int8_t* xq_out, float* a_out,
                          hipStream_t stream) {
-    SkinnyArgs a;
+    return launch_skinny_grouped(xq, a_scale, x_bf16, 1, &packed, &w_scale, &N, &out, M, K,
+                                 out_dtype, xq_out, a_out, stream);
+}
+
+hipError_t launch_skinny_grouped(const int8_t* xq, const float* a_scale, const uint16_t* x_bf16,
+                                 int groups, const uint8_t* const* packed,
+                                 const float* const* w_scale, const int64_t* N,
+                                 void* const* out, int64_t M, int64_t K, int out_dtype,
+                                 int8_t* xq_out, float* a_out, hipStream_t stream) {
+    if (groups < 1 || groups > kSkGroups) return hipErrorInvalidValue;
+    SkinnyArgs a = {};
     a.xq = xq;
     a.a_scale = a_scale;
     a.xb = x_bf16;
-    a.packed = packed;
-    a.w_scale = w_scale;
-    a.out = out;
     a.xq_out = xq_out;
     a.a_out = a_out;
+    a.groups = groups;
+    int64_t blocks = 0;
+    for (int g = 0; g < kSkGroups; ++g) {
+        const bool live = g < groups;
+        a.first[g] = (int)blocks;
+        a.g_N[g] = live ? (int)N[g] : 0;
+        a.g_packed[g] = live ? packed[g] : nullptr;
+        a.g_wscale[g] = live ? w_scale[g] : nullptr;
+        a.g_out[g] = live ? out[g] : nullptr;
+        if (live) blocks += (N[g] + 15) / 16;
+    }
+    if (blocks == 0) return hipSuccess;
+    if (blocks > INT32_MAX) return hipErrorInvalidValue;
     a.M = (int)M;
-    a.N = (int)N;
     a.K = (int)K;
     a.Kp = (int)((K + 255) / 256 * 256);
     int ks = ((kSkXBudget / (int)M) - 16) / 256 * 256;
@@ -646,7 +696,7 @@ hipError_t launch_skinny(const int8_t* xq, const float* a_scale, const uint16_t*
     a.KS = ks < a.Kp ? ks : a.Kp;
     a.out_dtype = out_dtype;
     const size_t lds = (size_t)M * (a.KS + 16) + kSkMisc + (size_t)kSkWaves * 4 * 64 * 4;
-    const dim3 grid((unsigned)((N + 15) / 16));
+    const dim3 grid((unsigned)blocks);
     const bool fused = x_bf16 != nullptr;
     if (M > 16) {
         if (fused) return hipErrorInvalidValue;  // the fused entry point takes M <= 16

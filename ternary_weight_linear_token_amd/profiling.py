@@ -167,7 +167,8 @@ def main(argv=None):
         sys.path.insert(0, build.ROOT)
         import workloads
         layer = workloads.LAYER_2B
-        alg = sum(N * K // 4 for _, N, K in layer) / len(layer)
+        # one decode step's packed bytes over its launches (grouped projections)
+        alg = sum(N * K // 4 for _, N, K in layer) / len(workloads.DECODE_GROUPS)
         sys.stdout.write(traffic(a.fetch, a.write, a.out, a.cmd, build.kernel_hash("skinny.hip"), alg))
 
 

@@ -126,6 +126,37 @@ def test_quant_gemv_validation(L):
     assert f(A, B, C, 0, 16, 256, D, 0, None, None, None) == OK
 
 
+def test_quant_gemv_grouped_validation(L):
+    f = L.bitnet_quant_gemv_grouped
+    P = ctypes.c_void_p
+
+    def arrs(packed, scales, ns, outs):
+        g = len(ns)
+        return ((P * g)(*packed), (P * g)(*scales), (ctypes.c_int64 * g)(*ns), (P * g)(*outs))
+
+    ok2 = arrs([B, B + 0x100], [C, C + 0x100], [16, 40], [D, D + 0x1000])
+
+    def call(x, M, K, G, a, dt=0, xq=None, sc=None):
+        pk, ws, ns, outs = a
+        return f(x, M, K, G, ctypes.cast(pk, P), ctypes.cast(ws, P), ctypes.cast(ns, P),
+                 ctypes.cast(outs, P), dt, xq, sc, None)
+
+    assert call(A, 1, 256, 0, ok2) == INVALID           # no groups
+    assert call(A, 1, 256, 5, arrs([B] * 5, [C] * 5, [16] * 5, [D] * 5)) == INVALID  # > 4
+    assert f(A, 1, 256, 2, None, None, None, None, 0, None, None, None) == INVALID
+    assert call(None, 1, 256, 2, ok2) == INVALID         # no activations
+    assert call(A, 17, 256, 2, ok2) == INVALID           # M above the GEMV limit
+    assert call(A, 1, 256, 2, ok2, dt=3) == INVALID      # bad dtype
+    assert call(A, 1, 250, 2, ok2) == UNALIGNED          # K % 4
+    assert call(A, 1, 256, 2, arrs([B, B + 4], [C, C], [16, 40], [D, E])) == UNALIGNED
+    assert call(A, 1, 256, 2, arrs([B, None], [C, C], [16, 40], [D, E])) == INVALID
+    assert call(A, 1, 256, 2, arrs([B, B], [C, C], [16, -1], [D, E])) == INVALID
+    assert call(A, 1, 256, 2, ok2, xq=E + 4) == UNALIGNED
+    # nothing to do: M == 0, or every group empty (its pointers are never looked at)
+    assert call(A, 0, 256, 2, ok2) == OK
+    assert call(A, 1, 256, 2, arrs([None, None], [None, None], [0, 0], [None, None])) == OK
+
+
 def test_valid_call_without_gpu_reports_hip_error(L):
     # Arguments pass validation, so the library asks HIP for the device; with no GPU in
     # this container that fails and comes back as BITNET_ERR_HIP with the HIP message.

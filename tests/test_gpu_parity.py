@@ -145,6 +145,31 @@ def test_quant_gemv_matches_oracle(M, N, K):
         check_out(to_np(out), o["acc"], o["ref"], dt, f"quant_gemv M={M} N={N} K={K} {dt}")
 
 
+@pytest.mark.parametrize("M", [1, 3, 16])
+@pytest.mark.parametrize("K,Ns", [(1024, [300, 37, 16]), (2560, [640, 640, 2560]),
+                                  (260, [129, 0, 50]), (256, [16]),
+                                  (6912, [33, 64, 17, 200]), (28672, [7, 20])])
+def test_quant_gemv_grouped_matches_oracle(M, K, Ns):
+    """Several weight matrices against one activation matrix in one launch: each output
+    matches the oracle and is bit-identical to the ungrouped launch."""
+    X = workloads.activations(M, K, seed=M * 9000 + K)
+    pbs = [Problem(M, n, K, seed=M * 9000 + K + 17 * g, X=X) for g, n in enumerate(Ns)]
+    os_ = [pb.oracle() for pb in pbs]
+    packed = [dev(o["packed"]) for o in os_]
+    scales = [dev(o["w_scale"]) for o in os_]
+    for dt in DT:
+        outs, xq, a = bw.quant_gemv_grouped(pbs[0].x_dev, packed, scales, dt, return_quant=True)
+        assert np.array_equal(to_np(a), os_[0]["a_scale"])
+        assert np.array_equal(to_np(xq), os_[0]["xq"])
+        for g, (o, out) in enumerate(zip(os_, outs)):
+            assert tuple(out.shape) == (M, Ns[g])
+            check_out(to_np(out), o["acc"], o["ref"], dt, f"grouped g={g} M={M} N={Ns[g]} K={K} {dt}")
+            if Ns[g]:
+                alone = bw.quant_gemv(pbs[0].x_dev, packed[g], scales[g], dt)
+                assert torch.equal(out.view(torch.int32) if dt != "bf16" else out.view(torch.int16),
+                                   alone.view(torch.int32) if dt != "bf16" else alone.view(torch.int16))
+
+
 def test_extreme_accumulators():
     # every activation at +-127 and every weight +1 / -1: |acc| = 127 K, the largest sums
     M, N, K = 3, 40, 28672

@@ -27,6 +27,12 @@ LAYER_70B = [("q", 8192, 8192), ("k", 1024, 8192), ("v", 1024, 8192), ("o", 8192
              ("gate", 28672, 8192), ("up", 28672, 8192), ("down", 8192, 28672)]
 
 
+# Projections of one layer that read the same activations (the attention block's input
+# feeds q, k and v; the MLP's input feeds gate and up), in the order a decode step runs
+# them: each tuple is one launch.
+DECODE_GROUPS = [("q", "k", "v"), ("o",), ("gate", "up"), ("down",)]
+
+
 def distinct_shapes(layer):
     seen, out = set(), []
     for name, n, k in layer:
