@@ -29,7 +29,9 @@ one launch per projection is reported beside it (value_ungrouped).
   here), on the same decode step repeated for ~10 s.
 * extras: the same per-launch rooflines at large shapes, where the bandwidth and
   matrix-core bars are reachable: the 70B-shaped decode layer set (M = 1) and the
-  8B-shaped prefill MLP GEMMs (M = 2048).
+  8B-shaped prefill MLP GEMMs (M = 2048); and ceilings measured on this chip: an int8
+  matrix-core loop on register operands, a 2 GiB streaming read, and the vendor int8
+  GEMM (hipBLASLt, dense int8 weights) at the prefill shapes.
 """
 from __future__ import annotations
 
@@ -375,6 +377,21 @@ def bench_extras(bw, workloads, torch, dev, reps):
                                "peak": INT8_MFMA_PEAK_TOPS, "unit": "TFLOP/s",
                                "frac": round(tot_ops / tot_us / 1e6 / INT8_MFMA_PEAK_TOPS, 4),
                                "per_shape": per}
+    # what this chip sustains (context for the fractions above)
+    from ternary_weight_linear_token_amd import ceilings
+    print("[bench] ceilings", file=sys.stderr, flush=True)
+    mfma = ceilings.mfma_i8_tops(torch, dev)
+    read = ceilings.hbm_read_gbs(torch, dev)
+    vendor = {f"{M}x{N}x{K}": (None if t is None else round(t, 1)) for (M, N, K), t in
+              (((M, N, K), ceilings.vendor_int8_gemm_tops(torch, dev, M, N, K))
+               for M, N, K in ((2048, 14336, 4096), (2048, 4096, 14336), (512, 6912, 2560)))}
+    out["ceilings"] = {
+        "mfma_i8_register_loop_tops": round(mfma, 1),
+        "mfma_i8_register_loop_frac_of_peak": round(mfma / INT8_MFMA_PEAK_TOPS, 4),
+        "hbm_stream_read_2GiB_gbs": round(read, 1),
+        "hbm_stream_read_frac_of_peak": round(read / HBM_PEAK_GBS, 4),
+        "vendor_int8_gemm_tops_dense_int8_weights": vendor,
+    }
     return out
 
 

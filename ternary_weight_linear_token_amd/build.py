@@ -97,5 +97,23 @@ def build(verbose: bool = False) -> str:
     return LIB_PATH
 
 
+PROBES_SRC = os.path.join(PKG_DIR, "probes", "ceilings.hip")
+PROBES_LIB = os.path.join(PKG_DIR, "libbitnet_probes.so")
+
+
+def build_probes(verbose: bool = False) -> str:
+    """Compile the ceiling microbenchmarks (not part of the BitLinear library)."""
+    tmp = PROBES_LIB + ".tmp%d" % os.getpid()
+    cmd = [HIPCC] + FLAGS + ["-shared", PROBES_SRC, "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {PROBES_SRC}:\n{res.stdout}\n{res.stderr}")
+    os.replace(tmp, PROBES_LIB)
+    if verbose:
+        print(f"built {PROBES_LIB}", file=sys.stderr)
+    return PROBES_LIB
+
+
 if __name__ == "__main__":
     build(verbose=True)
+    build_probes(verbose=True)

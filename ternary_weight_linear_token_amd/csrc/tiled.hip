@@ -6,9 +6,10 @@
 // dense contraction, so it runs on v_mfma_i32_32x32x32_i8.
 //
 // Design:
-//  * Block tile BM x BN, k-stage BK = 64, four wave64s in a 2 x 2 grid, each a
-//    (BM/2) x (BN/2) tile of 32x32 int32 accumulator blocks (tall wave tiles amortize
-//    the weight unpack over more rows).
+//  * Block tile BM x BN, k-stage BK = 64, four wave64s in a (4/WGN) x WGN grid, each a
+//    tile of 32x32 int32 accumulator blocks.  Tall wave tiles amortize the weight
+//    unpack over more rows: the 256x256 blocks use a 1 x 4 grid (256 x 64 per wave,
+//    half the unpack of a 2 x 2 grid for twice the activation fragment reads).
 //  * Loads are raw buffer loads through per-block descriptors whose range ends at the
 //    last valid row: rows past M or N read as zero without any branch, and per-stage
 //    offsets are scalar, so address arithmetic stays off the vector ALU.
@@ -63,9 +64,10 @@ struct TiledArgs {
     int out_dtype;
 };
 
-template <int BM, int BN, int D, int G, bool ALIGNED, int DT>
+template <int BM, int BN, int D, int G, int WGN, bool ALIGNED, int DT>
 __global__ __launch_bounds__(kTdThreads * G) void tiled_kernel(TiledArgs p) {
-    constexpr int WM = BM / 2, WN = BN / 2;   // wave tile
+    constexpr int WGM = 4 / WGN;                 // waves along M and N
+    constexpr int WM = BM / WGM, WN = BN / WGN;  // wave tile
     constexpr int MB = WM / 32, NB = WN / 32;  // 32x32 blocks per wave
     constexpr int AV = BM * (kBK / 16) / kTdThreads;  // 16-byte A loads per thread per stage
     constexpr int BROWS_PER_THREAD = (BN + kTdThreads - 1) / kTdThreads;
@@ -94,7 +96,7 @@ __global__ __launch_bounds__(kTdThreads * G) void tiled_kernel(TiledArgs p) {
     const int g = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 8);
     const int tid = threadIdx.x & 255, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WGN, wn = wave % WGN;
     unsigned char (&a_lds)[2][BM * kAStride] = a_lds_all[g];
     const int M = p.M, N = p.N, K = p.K;
     const int64_t row_bytes = K / 4;
@@ -496,7 +498,7 @@ TilePlan plan_tiles(int64_t M, int64_t N, int64_t K) {
     return t;
 }
 
-template <int BM, int BN, int D, int G>
+template <int BM, int BN, int D, int G, int WGN>
 hipError_t launch_plan(TiledArgs a, const TilePlan& t, bool aligned, hipStream_t stream) {
     a.tiles_m = t.tiles_m;
     a.tiles_n = t.tiles_n;
@@ -505,12 +507,12 @@ hipError_t launch_plan(TiledArgs a, const TilePlan& t, bool aligned, hipStream_t
     const dim3 grid((unsigned)(a.units_per_xcd * kXcds));
     const dim3 blk(kTdThreads * G);
     switch (a.out_dtype * 2 + (aligned ? 1 : 0)) {
-        case 0: hipLaunchKernelGGL((tiled_kernel<BM, BN, D, G, false, 0>), grid, blk, 0, stream, a); break;
-        case 1: hipLaunchKernelGGL((tiled_kernel<BM, BN, D, G, true, 0>), grid, blk, 0, stream, a); break;
-        case 2: hipLaunchKernelGGL((tiled_kernel<BM, BN, D, G, false, 1>), grid, blk, 0, stream, a); break;
-        case 3: hipLaunchKernelGGL((tiled_kernel<BM, BN, D, G, true, 1>), grid, blk, 0, stream, a); break;
-        case 4: hipLaunchKernelGGL((tiled_kernel<BM, BN, D, G, false, 2>), grid, blk, 0, stream, a); break;
-        default: hipLaunchKernelGGL((tiled_kernel<BM, BN, D, G, true, 2>), grid, blk, 0, stream, a); break;
+        case 0: hipLaunchKernelGGL((tiled_kernel<BM, BN, D, G, WGN, false, 0>), grid, blk, 0, stream, a); break;
+        case 1: hipLaunchKernelGGL((tiled_kernel<BM, BN, D, G, WGN, true, 0>), grid, blk, 0, stream, a); break;
+        case 2: hipLaunchKernelGGL((tiled_kernel<BM, BN, D, G, WGN, false, 1>), grid, blk, 0, stream, a); break;
+        case 3: hipLaunchKernelGGL((tiled_kernel<BM, BN, D, G, WGN, true, 1>), grid, blk, 0, stream, a); break;
+        case 4: hipLaunchKernelGGL((tiled_kernel<BM, BN, D, G, WGN, false, 2>), grid, blk, 0, stream, a); break;
+        default: hipLaunchKernelGGL((tiled_kernel<BM, BN, D, G, WGN, true, 2>), grid, blk, 0, stream, a); break;
     }
     return hipGetLastError();
 }
@@ -540,9 +542,9 @@ hipError_t launch_tiled(const int8_t* xq, const float* a_scale, const uint8_t* p
     const bool aligned = (K % kBK) == 0;
     (void)workspace;
     const TilePlan t = plan_tiles(M, N, K);
-    if (t.bm == 256 && t.bn == 256) return launch_plan<256, 256, 2, 1>(a, t, aligned, stream);
-    if (t.bm == 256) return launch_plan<256, 128, 4, 1>(a, t, aligned, stream);
-    return launch_plan<128, 128, 4, 2>(a, t, aligned, stream);
+    if (t.bm == 256 && t.bn == 256) return launch_plan<256, 256, 2, 1, 4>(a, t, aligned, stream);
+    if (t.bm == 256) return launch_plan<256, 128, 4, 1, 2>(a, t, aligned, stream);
+    return launch_plan<128, 128, 4, 2, 2>(a, t, aligned, stream);
 }
 
 }  // namespace bitnet

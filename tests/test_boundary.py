@@ -176,3 +176,21 @@ def test_python_binding_refuses_cpu_tensors():
         bw.quant_act(x)
     with pytest.raises(ValueError, match="device tensor"):
         bw.pack_weights(torch.zeros((4, 8)))
+
+
+def test_ceiling_probes_library_exports():
+    # the microbenchmarks the bench reports beside the roofline fractions
+    from ternary_weight_linear_token_amd import build as b
+    if not os.path.exists(b.PROBES_LIB):
+        b.build_probes()
+    L = ctypes.CDLL(b.PROBES_LIB)
+    for name in ("bitnet_probe_mfma_i8", "bitnet_probe_mfma_i8_ops", "bitnet_probe_read"):
+        assert hasattr(L, name), name
+    L.bitnet_probe_mfma_i8_ops.restype = ctypes.c_double
+    L.bitnet_probe_mfma_i8_ops.argtypes = [ctypes.c_int, ctypes.c_int]
+    assert L.bitnet_probe_mfma_i8_ops(2, 3) == 2.0 * 32 * 32 * 32 * 8 * 3 * 2 * 4
+    # argument checks come before any HIP call
+    L.bitnet_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
+                                    ctypes.c_void_p]
+    assert L.bitnet_probe_read(None, 16, 0x1000, 1, None) != 0
+    assert L.bitnet_probe_read(0x1008, 16, 0x1000, 1, None) != 0

@@ -313,7 +313,8 @@ def test_gemm_small_and_large_tile_grids_with_caller_workspace():
     # workspace is accepted and left untouched.
     ws = torch.full((1 << 20,), 0x5A, dtype=torch.uint8, device="cuda")
     for (M, N, K) in [(300, 257, 2560), (512, 2560, 2560), (130, 640, 6912), (17, 1024, 4096),
-                      (1024, 8192, 512), (600, 16384, 256), (257, 9000, 320), (520, 33000, 320)]:
+                      (1024, 8192, 512), (600, 16384, 256), (257, 9000, 320), (520, 33000, 320),
+                      (520, 33024, 128), (264, 65560, 192)]:
         pb = Problem(M, N, K, seed=M + N + K)
         xq, a, packed, s, o = product_inputs(pb)
         out = bw.gemm(xq, a, packed, s, "i32", algo="tiled", workspace=ws)
