@@ -151,9 +151,10 @@ int bitnet_w2a8_gemm(const int8_t* xq, const float* a_scale, const uint8_t* pack
         !aligned16(out) || !aligned16(workspace))
         return BITNET_ERR_UNALIGNED;
     if ((st = check_device())) return st;
-    // Auto: the weight-streaming kernel up to 16 tokens; from 17 to 64 tokens only while
-    // M * N is small, since each of its 16-row blocks stages all M x K activations.
-    const bool skinny_auto = M <= 16 || (M <= BITNET_SKINNY_MAX_M && M * N <= 262144);
+    // Auto: the weight-streaming kernel while M * N is small (each of its 16-row blocks
+    // stages all M x K activations, so its cost grows with M * N); otherwise the tiled
+    // kernel, whose single-round grids cost about the same for any M up to 64.
+    const bool skinny_auto = (M <= 16 && M * N <= 196608) || (M <= 32 && M * N <= 131072);
     const bool skinny = algo == BITNET_ALGO_SKINNY || (algo == BITNET_ALGO_AUTO && skinny_auto);
     if (skinny)
         return record_hip(bitnet::launch_skinny(xq, a_scale, nullptr, packed, w_scale, M, N, K,

@@ -30,9 +30,10 @@
 //    k = 4 b + i -- the same k-order as operand A.
 //  * No split across blocks: handing int32 partial tiles between blocks needs
 //    device-scope release/acquire, which on this chip (one L2 per XCD) costs more than
-//    the split saves.  Small grids instead use 128x128 blocks of two four-wave k-groups
-//    (alternate k-stages, accumulators combined through LDS), so each SIMD interleaves
-//    two waves.
+//    the split saves.  Small grids instead split K inside the block: 128x128 blocks of
+//    two four-wave k-groups, or, when 64x128 blocks fit the CUs in one round, 64x128
+//    blocks of four k-groups (alternate k-stages, accumulators combined through LDS),
+//    so each SIMD interleaves two or four waves.
 //  * Blocks are mapped to work units XCD by XCD (dispatch assigns consecutive blocks to
 //    the 8 XCDs in turn), so an XCD's L2 sees consecutive tiles of the same row panel.
 #include <cstdio>
@@ -74,8 +75,17 @@ __global__ __launch_bounds__(kTdThreads * G) void tiled_kernel(TiledArgs p) {
     static_assert(AV >= 1, "tile/thread mismatch");
     (void)BROWS_PER_THREAD;
 
-    static_assert(G == 1 || G == 2, "k-groups per block");
-    __shared__ __align__(16) unsigned char a_lds_all[G][2][BM * kAStride];
+    static_assert(G == 1 || G == 2 || G == 4, "k-groups per block");
+    static_assert(G == 1 || MB % 2 == 0, "k-group combine splits the accumulator rows");
+    // LDS: the groups' double-buffered activation stages, reused after the k loop for the
+    // combine of the groups' accumulators and the per-wave epilogue scratch
+    constexpr int kStageBytes = G * 2 * BM * kAStride;
+    constexpr int kGroupAccBytes = 4 * MB * NB * 16 * 64 * 4;  // one group's accumulators
+    constexpr int kRedBytes = G == 4 ? 2 * kGroupAccBytes : (G == 2 ? kGroupAccBytes / 2 : 0);
+    constexpr int kEpiBytes = (G == 1 ? 1 : 2) * 4 * 32 * 36 * 4;
+    constexpr int kLdsBytes = kStageBytes > kRedBytes ? (kStageBytes > kEpiBytes ? kStageBytes : kEpiBytes)
+                                                      : (kRedBytes > kEpiBytes ? kRedBytes : kEpiBytes);
+    __shared__ __align__(16) unsigned char smem[kLdsBytes];
     __shared__ float s_inva[BM];
 
     // ---- work unit of this block (XCD-contiguous) ----
@@ -89,15 +99,16 @@ __global__ __launch_bounds__(kTdThreads * G) void tiled_kernel(TiledArgs p) {
 
     // G groups of four waves; group g takes the k-stages g, g + G, g + 2G, ... of the
     // block's range with its own LDS buffers and registers; their accumulators are
-    // combined through LDS at the end.  With G = 2 every SIMD holds two waves whose
-    // memory, LDS and matrix-core phases interleave.
+    // combined through LDS at the end.  With G = 2 (4) every SIMD holds two (four) waves
+    // whose memory, LDS and matrix-core phases interleave.
     // group and wave indices are uniform per wave; readfirstlane tells the compiler so,
     // which keeps the per-stage buffer offsets in scalar registers
-    const int g = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 8);
+    const int g = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 8);  // 256 threads per group
     const int tid = threadIdx.x & 255, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WGN, wn = wave % WGN;
-    unsigned char (&a_lds)[2][BM * kAStride] = a_lds_all[g];
+    unsigned char (*a_lds)[BM * kAStride] =
+        reinterpret_cast<unsigned char (*)[BM * kAStride]>(smem + g * 2 * BM * kAStride);
     const int M = p.M, N = p.N, K = p.K;
     const int64_t row_bytes = K / 4;
     const int nk = (K + kBK - 1) / kBK;
@@ -305,7 +316,7 @@ __global__ __launch_bounds__(kTdThreads * G) void tiled_kernel(TiledArgs p) {
     // and stores them with 16-byte writes.  32x32 int32 accumulator layout: lane l,
     // register r -> row 8*(r/4) + 4*(l/32) + r%4, column l%32. ----
     constexpr int kEpiStride = 36;
-    int* scratch = reinterpret_cast<int*>(&a_lds_all[0][0][0]) + (g * 4 + wave) * (32 * kEpiStride);
+    int* scratch = reinterpret_cast<int*>(smem) + (g * 4 + wave) * (32 * kEpiStride);
     const int erow = lane >> 1, ecol = (lane & 1) * 16;
     const bool vec_ok = (N % 16) == 0;
 
@@ -366,11 +377,37 @@ __global__ __launch_bounds__(kTdThreads * G) void tiled_kernel(TiledArgs p) {
     };
 
     // every k-stage ended with a barrier: the A buffers are free for the epilogue scratch
-    if constexpr (G == 2) {
-        // ---- combine the two groups: group 0 ends up owning accumulator rows blocks
-        // i < MB/2, group 1 the others; each half goes through LDS in its own phase ----
+    if constexpr (G == 4) {
+        // ---- groups 2 and 3 hand their accumulators to groups 0 and 1 ----
+        int* red4 = reinterpret_cast<int*>(smem);
+        auto slot4 = [&](int gg, int i, int j, int r) {
+            return ((((gg * 4 + wave) * MB + i) * NB + j) * 16 + r) * 64 + lane;
+        };
+        if (g >= 2) {
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) red4[slot4(g - 2, i, j, r)] = acc[i][j][r];
+        }
+        __syncthreads();
+        if (g < 2) {
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[i][j][r] += red4[slot4(g, i, j, r)];
+        }
+        __syncthreads();
+    }
+    if constexpr (G >= 2) {
+        // ---- combine groups 0 and 1: group 0 ends up owning accumulator rows blocks
+        // i < MB/2, group 1 the others; each half goes through LDS in its own phase
+        // (groups 2 and 3, already folded in, only take part in the barriers) ----
         constexpr int H = MB / 2;
-        int* red = reinterpret_cast<int*>(&a_lds_all[0][0][0]);
+        int* red = reinterpret_cast<int*>(smem);
         auto slot = [&](int ih, int j, int r) { return (((wave * H + ih) * NB + j) * 16 + r) * 64 + lane; };
         if (g == 1) {
 #pragma unroll
@@ -408,6 +445,7 @@ __global__ __launch_bounds__(kTdThreads * G) void tiled_kernel(TiledArgs p) {
                     for (int r = 0; r < 16; ++r) acc[H + ih][j][r] += red[slot(ih, j, r)];
         }
         __syncthreads();  // red is reused as epilogue scratch below
+        if (g >= 2) return;
 #pragma unroll
         for (int ih = 0; ih < H; ++ih)
 #pragma unroll
@@ -432,7 +470,7 @@ __global__ __launch_bounds__(kTdThreads * G) void tiled_kernel(TiledArgs p) {
 }
 
 struct TilePlan {
-    int bm, bn;
+    int bm, bn, g;  // block tile and k-groups per block
     int tiles_m, tiles_n;
 };
 
@@ -449,50 +487,62 @@ int device_cus() {
     return cus[dev];
 }
 
-// Optional override for tuning: BITNET_TILED_CONFIG="bm,bn" with bm,bn one of the
-// compiled tile shapes (256,256 / 256,128 / 128,128); read once per process.
-bool config_override(int* bm, int* bn) {
-    static int cached[3] = {-1, 0, 0};
+// Optional override for tuning: BITNET_TILED_CONFIG="bm,bn,g", one of the compiled
+// configurations (256,256,1 / 256,128,1 / 128,128,2 / 64,128,4); read once
+// per process.
+bool config_override(int* bm, int* bn, int* g) {
+    static int cached[4] = {-1, 0, 0, 0};
     if (cached[0] == -1) {
         const char* e = std::getenv("BITNET_TILED_CONFIG");
-        int a = 0, b = 0;
-        if (e && std::sscanf(e, "%d,%d", &a, &b) == 2 &&
-            ((a == 256 && b == 256) || (a == 256 && b == 128) || (a == 128 && b == 128))) {
-            cached[1] = a;
-            cached[2] = b;
-            cached[0] = 1;
-        } else {
-            cached[0] = 0;
-        }
+        int a = 0, b = 0, c = 0;
+        const bool ok = e && std::sscanf(e, "%d,%d,%d", &a, &b, &c) == 3 &&
+                        ((a == 256 && b == 256 && c == 1) || (a == 256 && b == 128 && c == 1) ||
+                         (a == 128 && b == 128 && c == 2) ||
+                         (a == 64 && b == 128 && c == 4));
+        cached[0] = ok ? 1 : 0;
+        cached[1] = a;
+        cached[2] = b;
+        cached[3] = c;
     }
     if (cached[0] <= 0) return false;
     *bm = cached[1];
     *bn = cached[2];
+    *g = cached[3];
     return true;
 }
 
-// Tile shape: the largest block tile whose grid still covers every CU (per-CU
-// matrix-core efficiency grows with the wave tile, because the weight unpack and the
-// activation transpose are amortized over more products); otherwise 128x128 blocks with
-// two k-groups, so each SIMD interleaves two waves.
+// Tile shape.  A grid that 64x128 blocks fit in one round (at most one block per CU)
+// is latency-bound per block: there 64x128 blocks with four k-groups (sixteen waves,
+// four per SIMD) finish each tile soonest.  Otherwise the largest block tile whose grid
+// still covers every CU (per-CU matrix-core efficiency grows with the wave tile, because
+// the weight unpack and the activation transpose are amortized over more products), or
+// else 128x128 blocks with two k-groups, so each SIMD interleaves two waves.
 TilePlan plan_tiles(int64_t M, int64_t N, int64_t K) {
     (void)K;
     const int cus = device_cus();
-    int bm = 128, bn = 128;
-    if (!config_override(&bm, &bn)) {
+    int bm = 128, bn = 128, g = 2;
+    if (!config_override(&bm, &bn, &g)) {
+        const int64_t t64 = ((M + 63) / 64) * ((N + 127) / 128);
         const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
         const int64_t t256x128 = ((M + 255) / 256) * ((N + 127) / 128);
-        if (t256 >= cus) {
+        if (t64 <= cus) {
+            bm = 64;
+            bn = 128;
+            g = 4;
+        } else if (t256 >= cus) {
             bm = 256;
             bn = 256;
+            g = 1;
         } else if (t256x128 >= cus) {
             bm = 256;
             bn = 128;
+            g = 1;
         }
     }
     TilePlan t;
     t.bm = bm;
     t.bn = bn;
+    t.g = g;
     t.tiles_m = (int)((M + bm - 1) / bm);
     t.tiles_n = (int)((N + bn - 1) / bn);
     return t;
@@ -544,6 +594,7 @@ hipError_t launch_tiled(const int8_t* xq, const float* a_scale, const uint8_t* p
     const TilePlan t = plan_tiles(M, N, K);
     if (t.bm == 256 && t.bn == 256) return launch_plan<256, 256, 2, 1, 4>(a, t, aligned, stream);
     if (t.bm == 256) return launch_plan<256, 128, 4, 1, 2>(a, t, aligned, stream);
+    if (t.bm == 64) return launch_plan<64, 128, 4, 4, 4>(a, t, aligned, stream);
     return launch_plan<128, 128, 4, 2, 2>(a, t, aligned, stream);
 }
 

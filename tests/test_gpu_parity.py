@@ -308,13 +308,13 @@ def test_graph_replay_matches_eager():
 
 
 def test_gemm_small_and_large_tile_grids_with_caller_workspace():
-    # Shapes that select each tile configuration (128x128 with two k-groups, 256x128,
-    # 256x256), including grids far smaller than the CU count and ragged edges; a caller
-    # workspace is accepted and left untouched.
+    # Shapes that select each tile configuration (64x128 with four k-groups, 128x128 with
+    # two, 256x128, 256x256), including grids far smaller than the CU count and ragged
+    # edges; a caller workspace is accepted and left untouched.
     ws = torch.full((1 << 20,), 0x5A, dtype=torch.uint8, device="cuda")
     for (M, N, K) in [(300, 257, 2560), (512, 2560, 2560), (130, 640, 6912), (17, 1024, 4096),
                       (1024, 8192, 512), (600, 16384, 256), (257, 9000, 320), (520, 33000, 320),
-                      (520, 33024, 128), (264, 65560, 192)]:
+                      (520, 33024, 128), (264, 65560, 192), (300, 8200, 384), (64, 4096, 1024)]:
         pb = Problem(M, N, K, seed=M + N + K)
         xq, a, packed, s, o = product_inputs(pb)
         out = bw.gemm(xq, a, packed, s, "i32", algo="tiled", workspace=ws)
