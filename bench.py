@@ -23,13 +23,15 @@ one launch per projection is reported beside it (value_ungrouped).
   launch) / its mean launch duration (a graph of back-to-back launches over the weight
   copies, timed with events), against 8 TB/s; traffic from the committed rocprofv3
   counter summary when it matches the current kernel source.
-* gemm: the BitNet-2B-shaped prefill set at M = 512 (quant kernel + tiled int8-MFMA
-  GEMM, bf16 out), int8 TOPS against 5.0 POPS dense.
+* gemm: the BitNet-2B-shaped prefill set at M = 512 (tiled int8-MFMA GEMM, bf16 out),
+  int8 TOPS against 5.0 POPS dense from the per-launch GEMM durations; the step rate
+  with the four quantization launches (one per shared input) is reported beside it.
 * cpu_baseline: the CPU oracle on the host cores (test infrastructure, timed only
   here), on the same decode step repeated for ~10 s.
 * extras: the same per-launch rooflines at large shapes, where the bandwidth and
   matrix-core bars are reachable: the 70B-shaped decode layer set (M = 1) and the
-  8B-shaped prefill MLP GEMMs (M = 2048); and ceilings measured on this chip: an int8
+  8B-shaped prefill MLP GEMMs (M = 2048); the 2B decode MLP as two launches (gate|up
+  with the SwiGLU epilogue, then down); and ceilings measured on this chip: an int8
   matrix-core loop on register operands, a 2 GiB streaming read, and the vendor int8
   GEMM (hipBLASLt, dense int8 weights) at the prefill shapes.
 """
@@ -377,6 +379,33 @@ def bench_extras(bw, workloads, torch, dev, reps):
                                "peak": INT8_MFMA_PEAK_TOPS, "unit": "TFLOP/s",
                                "frac": round(tot_ops / tot_us / 1e6 / INT8_MFMA_PEAK_TOPS, 4),
                                "per_shape": per}
+    # the decode MLP as two launches: gate|up with the SwiGLU epilogue (h in bf16), then
+    # down on h (fused quant + GEMV); 2B shapes, M = 1
+    print("[bench] 2B decode MLP chain, M=1", file=sys.stderr, flush=True)
+    shapes = {name: (N, K) for name, N, K in workloads.LAYER_2B}
+    (Ni, Kh), (Nd, Kd) = shapes["gate"], shapes["down"]
+    mats = {}
+    for seed, name, (N, K) in ((0, "gate", (Ni, Kh)), (1, "up", (Ni, Kh)), (2, "down", (Nd, Kd))):
+        mats[name] = bw.pack_weights(workloads.latent_weights(N, K, seed=seed).to(dev))
+    nbytes = (2 * Ni * Kh + Nd * Kd) // 4
+    R = max(2, math.ceil(ROTATE_BYTES / nbytes))
+    copies = [mats] + [{k: (v[0].clone(), v[1]) for k, v in mats.items()} for _ in range(R - 1)]
+    x = workloads.activations(1, Kh, seed=0, outliers=True).to(dev)
+    h = torch.empty((1, Ni), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((1, Nd), dtype=torch.float32, device=dev)
+
+    def mlp(r):
+        c = copies[r]
+        bw.quant_gemv_swiglu(x, c["gate"][0], c["gate"][1], c["up"][0], c["up"][1], "bf16", out=h)
+        bw.quant_gemv(h, c["down"][0], c["down"][1], "f32", out=y)
+
+    us = graph_launch_us(torch, mlp, R, reps)
+    out["mlp_decode_2b_m1"] = {"launches": 2, "us": round(us, 3),
+                               "packed_GB/s": round(nbytes / us / 1e3, 1),
+                               "packed_bytes": nbytes}
+    del copies, mats
+    torch.cuda.empty_cache()
+
     # what this chip sustains (context for the fractions above)
     from ternary_weight_linear_token_amd import ceilings
     print("[bench] ceilings", file=sys.stderr, flush=True)
@@ -416,10 +445,16 @@ def bench_gemm(bw, workloads, torch, np, dev, layer, R_bytes, reps):
     copies = [packed0] + [[p.clone() for p in packed0] for _ in range(R - 1)]
     ops = sum(2.0 * M * N * K for _, N, K in layer)
 
+    # projections that read the same activations share one quantization (q|k|v, gate|up)
+    index = {name: i for i, (name, _, _) in enumerate(layer)}
+    groups = [[index[n] for n in grp] for grp in workloads.DECODE_GROUPS]
+
     def step(r):
-        for i in range(len(layer)):
-            bw.quant_act(xs[i], xq=xqs[i], a_scale=avs[i])
-            bw.gemm(xqs[i], avs[i], copies[r][i], scales[i], "bf16", out=outs[i])
+        for grp in groups:
+            i0 = grp[0]
+            bw.quant_act(xs[i0], xq=xqs[i0], a_scale=avs[i0])
+            for i in grp:
+                bw.gemm(xqs[i0], avs[i0], copies[r][i], scales[i], "bf16", out=outs[i])
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -439,6 +474,7 @@ def bench_gemm(bw, workloads, torch, np, dev, layer, R_bytes, reps):
         "value": round(tops, 2),
         "unit": "TOPS",
         "step_tops_incl_quant": round(ops / (ms_step * 1e-3) / 1e12, 2),
+        "step": "one quant_act per shared input (q|k|v, o, gate|up, down) + seven GEMMs",
         "ms_per_step_incl_quant": round(ms_step, 4),
         "roofline": {
             "bound": "mfma",

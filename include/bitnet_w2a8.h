@@ -181,6 +181,28 @@ int bitnet_quant_gemv_grouped(const uint16_t* x, int64_t M, int64_t K, int64_t g
                               const int64_t* N, void* const* out, int out_dtype,
                               int8_t* xq_out, float* a_scale_out, void* stream);
 
+/*
+ * bitnet_quant_gemv_swiglu -- the decode MLP's first half in one launch ("BitNet 深度实战"
+ * §3.2: the MLP computes down(silu(gate(x)) * up(x)) with gate, up and down BitLinear
+ * layers).  Both products read the same quantized x; a block multiplies the same rows of
+ * the two matrices and writes
+ *   h[m,n] = silu(g[m,n]) * u[m,n],  silu(g) = g / (1 + exp(-g)),
+ * where g and u are the fp32 outputs bitnet_quant_gemv would write for (packed_gate,
+ * w_scale_gate) and (packed_up, w_scale_up); the SiLU and the product are fp32.
+ *   x                 : bf16 (M, K) as uint16, 1 <= M <= BITNET_GEMV_MAX_M.
+ *   packed_gate/_up   : uint8 (N, K/4) each; w_scale_gate/_up: float (N) each.
+ *   h                 : (M, N), BITNET_OUT_F32 or BITNET_OUT_BF16 (RNE of the fp32 value);
+ *                       BITNET_OUT_I32 is rejected (BITNET_ERR_INVALID_ARG).
+ *   xq_out, a_scale_out : optional copies of the quantized activations, as in
+ *                       bitnet_quant_gemv.
+ * h is what bitnet_quant_gemv_swiglu's caller feeds (as bf16) to the down projection,
+ * e.g. bitnet_quant_gemv with K = N.
+ */
+int bitnet_quant_gemv_swiglu(const uint16_t* x, const uint8_t* packed_gate,
+                             const float* w_scale_gate, const uint8_t* packed_up,
+                             const float* w_scale_up, int64_t M, int64_t N, int64_t K, void* h,
+                             int out_dtype, int8_t* xq_out, float* a_scale_out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

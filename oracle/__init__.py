@@ -17,6 +17,7 @@ Functions and the pages they follow (page titles abbreviated):
                    §3.2: int8 activations, per-token absmax scale 127/max|x|.
   accumulate    -- "BitNet 深度实战" §4.4: int8 x ternary into int32.
   rescale       -- "BitNet 深度实战" §2.4 / §3.2: out = acc * w_scale / a_scale.
+  swiglu        -- "BitNet 深度实战" §3.2: the MLP's silu(gate(x)) * up(x).
 
 Every function is pinned by tests/test_oracle_pins.py (worked example, closed forms,
 invariants, library matmul on unpacked codes, brute force on tiny inputs).
@@ -79,6 +80,7 @@ def _load():
             "oracle_rescale": [p, p, p, i64, i64, p, p, p],
             "oracle_rescale_sampled": [p, p, p, p, p, i64, p, p, p],
             "oracle_f64_to_bf16": [p, i64, p],
+            "oracle_swiglu": [p, p, i64, p],
         }
         for name, args in sig.items():
             fn = getattr(lib, name)
@@ -223,6 +225,18 @@ def rescale_sampled(acc, a_scale, w_scale, ms, ns):
                                           _ptr(ns), ms.size, _ptr(ref), _ptr(f32), _ptr(bf)),
            "rescale_sampled")
     return ref, f32, bf
+
+
+def swiglu(g: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """O5: h = silu(g) * u = g / (1 + exp(-g)) * u in fp64, elementwise ("BitNet 深度实战"
+    §3.2, the MLP's act_fn(gate(x)) * up(x) with act_fn = F.silu)."""
+    g = np.ascontiguousarray(g, dtype=np.float64)
+    u = np.ascontiguousarray(u, dtype=np.float64)
+    if g.shape != u.shape:
+        raise ValueError("g and u must have the same shape")
+    h = np.empty(g.shape, np.float64)
+    _check(_load().oracle_swiglu(_ptr(g), _ptr(u), g.size, _ptr(h)), "swiglu")
+    return h
 
 
 def f64_to_bf16(x: np.ndarray) -> np.ndarray:

@@ -261,6 +261,20 @@ int oracle_rescale_sampled(const int32_t* acc, const float* a_scale, const float
     return 0;
 }
 
+/* ------------------------------------------------------- O5: SwiGLU of the MLP --- */
+
+/*
+ * [Deep] §3.2 (BitLlamaMLP): the MLP's hidden activation is act_fn(gate_proj(x)) *
+ * up_proj(x) with act_fn = F.silu, and silu(g) = g * sigmoid(g) = g / (1 + exp(-g)).
+ * g and u are the two projections' exact outputs (O4's fp64 values); h is evaluated in
+ * fp64.
+ */
+int oracle_swiglu(const double* g, const double* u, int64_t count, double* h) {
+    if (!g || !u || !h || count < 0) return -1;
+    for (int64_t t = 0; t < count; ++t) h[t] = g[t] / (1.0 + exp(-g[t])) * u[t];
+    return 0;
+}
+
 /* fp64 -> bf16 (RNE) exposed for the oracle's own pin tests. */
 void oracle_f64_to_bf16(const double* x, int64_t count, uint16_t* out) {
     for (int64_t t = 0; t < count; ++t) out[t] = f64_to_bf16_rne(x[t]);

@@ -27,6 +27,7 @@ from ._binding import (  # noqa: F401
     quant_act,
     quant_gemv,
     quant_gemv_grouped,
+    quant_gemv_swiglu,
     status_str,
     unpack_weights,
 )

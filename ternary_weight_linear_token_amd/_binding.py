@@ -63,6 +63,7 @@ def lib():
             "bitnet_w2a8_gemm": ([p, p, p, p, i64, i64, i64, p, i32, i32, p, ctypes.c_size_t, p], i32),
             "bitnet_quant_gemv": ([p, p, p, i64, i64, i64, p, i32, p, p, p], i32),
             "bitnet_quant_gemv_grouped": ([p, i64, i64, i64, p, p, p, p, i32, p, p, p], i32),
+            "bitnet_quant_gemv_swiglu": ([p, p, p, p, p, i64, i64, i64, p, i32, p, p, p], i32),
         }
         for name, (args, res) in sigs.items():
             fn = getattr(L, name)
@@ -279,6 +280,32 @@ def quant_gemv_grouped(x, packed, w_scale, out_dtype="f32", out=None, return_qua
                                            _stream(x)),
            "bitnet_quant_gemv_grouped")
     return (outs, xq, a_scale) if return_quant else outs
+
+
+def quant_gemv_swiglu(x, packed_gate, w_scale_gate, packed_up, w_scale_up, out_dtype="bf16",
+                      out=None, return_quant=False):
+    """silu(x W_gate^T) * (x W_up^T) for M <= 16 in one launch (fused quantization)."""
+    M, K = x.shape
+    N = packed_gate.shape[0]
+    code = _out_code(out_dtype)
+    if code == OUT_I32:
+        raise ValueError("the SwiGLU output is fp32 or bf16")
+    out = _alloc_out(out, M, N, code, x.device)
+    xq = a_scale = None
+    if return_quant:
+        xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
+        a_scale = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _check(lib().bitnet_quant_gemv_swiglu(
+        _tensor(x, torch.bfloat16, "x", (M, K)),
+        _tensor(packed_gate, torch.uint8, "packed_gate", (N, K // 4)),
+        _tensor(w_scale_gate, torch.float32, "w_scale_gate", (N,)),
+        _tensor(packed_up, torch.uint8, "packed_up", (N, K // 4)),
+        _tensor(w_scale_up, torch.float32, "w_scale_up", (N,)), M, N, K,
+        _tensor(out, _OUT_TORCH[code], "out", (M, N)), code,
+        _opt_ptr(xq, torch.int8, "xq_out", (M, K)),
+        _opt_ptr(a_scale, torch.float32, "a_scale_out", (M,)), _stream(x)),
+        "bitnet_quant_gemv_swiglu")
+    return (out, xq, a_scale) if return_quant else out
 
 
 FUSED_MAX_M = 4  # above this, one quantization launch beats requantizing in every block

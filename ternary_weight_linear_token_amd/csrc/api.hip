@@ -212,4 +212,25 @@ int bitnet_quant_gemv_grouped(const uint16_t* x, int64_t M, int64_t K, int64_t g
                                                     a_scale_out, as_stream(stream)));
 }
 
+int bitnet_quant_gemv_swiglu(const uint16_t* x, const uint8_t* packed_gate,
+                             const float* w_scale_gate, const uint8_t* packed_up,
+                             const float* w_scale_up, int64_t M, int64_t N, int64_t K, void* h,
+                             int out_dtype, int8_t* xq_out, float* a_scale_out, void* stream) {
+    if (out_dtype != BITNET_OUT_F32 && out_dtype != BITNET_OUT_BF16) return BITNET_ERR_INVALID_ARG;
+    int st = check_shape(M, N, K);
+    if (st) return st;
+    if (M > BITNET_GEMV_MAX_M) return BITNET_ERR_INVALID_ARG;
+    if (M == 0 || N == 0) return BITNET_OK;
+    if (!x || !packed_gate || !w_scale_gate || !packed_up || !w_scale_up || !h)
+        return BITNET_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(packed_gate) || !aligned16(w_scale_gate) ||
+        !aligned16(packed_up) || !aligned16(w_scale_up) || !aligned16(h) || !aligned16(xq_out) ||
+        !aligned16(a_scale_out))
+        return BITNET_ERR_UNALIGNED;
+    if ((st = check_device())) return st;
+    return record_hip(bitnet::launch_skinny_swiglu(x, packed_gate, w_scale_gate, packed_up,
+                                                   w_scale_up, M, N, K, h, out_dtype, xq_out,
+                                                   a_scale_out, as_stream(stream)));
+}
+
 }  // extern "C"

@@ -30,6 +30,15 @@ hipError_t launch_skinny_grouped(const int8_t* xq, const float* a_scale, const u
                                  void* const* out, int64_t M, int64_t K, int out_dtype,
                                  int8_t* xq_out, float* a_out, hipStream_t stream);
 
+// SwiGLU pair for 1 <= M <= 16 (bf16 activations, fused quantization): the same rows of
+// the gate and up matrices in one launch, out = silu(gate product) * (up product), fp32
+// (out_dtype 0) or bf16 (1).
+hipError_t launch_skinny_swiglu(const uint16_t* x_bf16, const uint8_t* packed_gate,
+                                const float* w_scale_gate, const uint8_t* packed_up,
+                                const float* w_scale_up, int64_t M, int64_t N, int64_t K,
+                                void* out, int out_dtype, int8_t* xq_out, float* a_out,
+                                hipStream_t stream);
+
 // Tiled int8 matrix-core product for any M.  `workspace` must hold
 // tiled_workspace_size(M, N, K) bytes whose counter area is zero (it is left zero).
 size_t tiled_workspace_size(int64_t M, int64_t N, int64_t K);

@@ -243,8 +243,11 @@ __device__ __forceinline__ void store_codes16(int8_t* xq_out, int K, int m, int 
 //  SINGLE - one batch covers a wave's whole share of K (single K stage)
 //  MC     - M fixed at compile time (1), or 0 for M read from the arguments
 //  MT     - 16-row tiles of tokens (M <= 16 MT); the weights of a chunk feed all of them
-template <bool FUSED, bool FAST, int XH, int U, bool SINGLE, int MC, int MT = 1>
+//  PAIR   - SwiGLU pair: the block multiplies the same 16 rows of two matrices (gate =
+//           group 0, up = group 1) and writes silu(gate) * up
+template <bool FUSED, bool FAST, int XH, int U, bool SINGLE, int MC, int MT = 1, bool PAIR = false>
 __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
+    constexpr int NW = PAIR ? 2 : 1;  // weight matrices per block
     extern __shared__ __align__(16) unsigned char smem[];
     const int KSP = p.KS + 16;  // padded LDS row stride: spreads rows over the banks
     const int M = MC > 0 ? MC : p.M;
@@ -255,8 +258,14 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
     for (int i = 1; i < kSkGroups; ++i)
         if (i < p.groups && (int)blockIdx.x >= p.first[i]) gi = i;
     const int N = pick(p.g_N, gi);
-    const uint8_t* const packed = pick(p.g_packed, gi);
-    const float* const w_scale = pick(p.g_wscale, gi);
+    const uint8_t* packed_v[NW];
+    const float* w_scale_v[NW];
+    packed_v[0] = pick(p.g_packed, gi);
+    w_scale_v[0] = pick(p.g_wscale, gi);
+    if constexpr (PAIR) {
+        packed_v[1] = p.g_packed[1];
+        w_scale_v[1] = p.g_wscale[1];
+    }
     void* const out = pick(p.g_out, gi);
     unsigned char* x_lds = smem;
     // per-wave partial results: s_wmax[w][m] = max |x| bits seen by wave w in row m,
@@ -275,54 +284,70 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
     const bool row_leader = (lane & 15) == 0;
 
     // scales needed at the end, requested first (threads tid < 16 M write outputs)
-    const float ws_n = buf_load_f32(make_rsrc(w_scale + n0, (uint32_t)(rows * 4)),
-                                    tid < 16 * M ? (uint32_t)(4 * (tid & 15)) : kOOB);
+    float ws_n[NW];
+#pragma unroll
+    for (int v = 0; v < NW; ++v)
+        ws_n[v] = buf_load_f32(make_rsrc(w_scale_v[v] + n0, (uint32_t)(rows * 4)),
+                               tid < 16 * M ? (uint32_t)(4 * (tid & 15)) : kOOB);
     float a_in = 0.0f;  // M = 1: every thread holds the token's scale
     if constexpr (!FUSED)
         a_in = buf_load_f32(make_rsrc(p.a_scale, (uint32_t)(M * 4)),
                             MC == 1 ? 0u : (tid < M ? 4u * tid : kOOB));
 
     // the block's weight rows (fewer than 16 at the end of N); reads past them give 0
-    const __amdgpu_buffer_rsrc_t w_rsrc =
-        make_rsrc(packed + (int64_t)n0 * row_bytes, (uint32_t)(rows * row_bytes));
+    __amdgpu_buffer_rsrc_t w_rsrc[NW];
+#pragma unroll
+    for (int v = 0; v < NW; ++v)
+        w_rsrc[v] = make_rsrc(packed_v[v] + (int64_t)n0 * row_bytes, (uint32_t)(rows * row_bytes));
     const uint32_t w_lane = (uint32_t)(mrow * row_bytes + 16 * q);
 
-    // chunks c = wave + 4 * (j0 + uu), uu < U, of the stage starting at byte stage_off
-    auto load_batch = [&](uint4 (&w)[U], int j0, int stage_off, int nch) {
+    // chunks c = wave + 4 * (j0 + uu), uu < U, of the stage starting at byte stage_off;
+    // w[uu * NW + v] holds chunk uu of matrix v
+    auto load_batch = [&](uint4 (&w)[U * NW], int j0, int stage_off, int nch) {
 #pragma unroll
         for (int uu = 0; uu < U; ++uu) {
             const int c = chunk_of(wave, j0 + uu);
             const int cb = stage_off + c * 64;  // the chunk's first byte in the row
-            if (FAST) {
-                const uint32_t off = (c < nch && cb + 16 * q < row_bytes) ? w_lane + cb : kOOB;
-                w[uu] = buf_load16(w_rsrc, off);
-            } else {
-                const int n = n0 + mrow;
-                w[uu] = (n < N && c < nch) ? load_w16_bytes(packed, row_bytes, n, cb + 16 * q)
-                                           : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+            for (int v = 0; v < NW; ++v) {
+                if (FAST) {
+                    const uint32_t off = (c < nch && cb + 16 * q < row_bytes) ? w_lane + cb : kOOB;
+                    w[uu * NW + v] = buf_load16(w_rsrc[v], off);
+                } else {
+                    const int n = n0 + mrow;
+                    w[uu * NW + v] = (n < N && c < nch)
+                                         ? load_w16_bytes(packed_v[v], row_bytes, n, cb + 16 * q)
+                                         : make_uint4(0u, 0u, 0u, 0u);
+                }
             }
         }
     };
 
-    v4i acc1[MT], acc4[MT], acc16[MT];
+    v4i acc1[NW][MT], acc4[NW][MT], acc16[NW][MT];
 #pragma unroll
-    for (int t = 0; t < MT; ++t) acc1[t] = acc4[t] = acc16[t] = v4i{0, 0, 0, 0};
+    for (int v = 0; v < NW; ++v)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) acc1[v][t] = acc4[v][t] = acc16[v][t] = v4i{0, 0, 0, 0};
 
-    auto compute_batch = [&](const uint4 (&w)[U], int j0, int nch) {
+    auto compute_batch = [&](const uint4 (&w)[U * NW], int j0, int nch) {
 #pragma unroll
         for (int uu = 0; uu < U; ++uu) {
             const int c = chunk_of(wave, j0 + uu);
             // With M = 1 and one batch, chunks past the stage are multiplied as well: their
             // weights read as zeros and their operand-A reads stay inside the LDS block.
             if ((MC == 1 && SINGLE) || c < nch) {
-                const uint32_t w4[4] = {w[uu].x, w[uu].y, w[uu].z, w[uu].w};
-                v4i b0, b1, b2, b3;
+                v4i b0[NW], b1[NW], b2[NW], b3[NW];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    b0[r] = (int)(w4[r] & 0x03030303u);
-                    b1[r] = (int)(w4[r] & 0x0C0C0C0Cu);
-                    b2[r] = (int)(w4[r] & 0x30303030u);
-                    b3[r] = (int)((w4[r] >> 2) & 0x30303030u);
+                for (int v = 0; v < NW; ++v) {
+                    const uint4 wv = w[uu * NW + v];
+                    const uint32_t w4[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        b0[v][r] = (int)(w4[r] & 0x03030303u);
+                        b1[v][r] = (int)(w4[r] & 0x0C0C0C0Cu);
+                        b2[v][r] = (int)(w4[r] & 0x30303030u);
+                        b3[v][r] = (int)((w4[r] >> 2) & 0x30303030u);
+                    }
                 }
 #pragma unroll
                 for (int t = 0; t < MT; ++t) {  // the unpacked weights feed every token tile
@@ -335,10 +360,13 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
 #pragma unroll
                         for (int i = 0; i < 4; ++i) A[i] = v4i{0, 0, 0, 0};
                     }
-                    acc1[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[0], b0, acc1[t], 0, 0, 0);
-                    acc4[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[1], b1, acc4[t], 0, 0, 0);
-                    acc16[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2], b2, acc16[t], 0, 0, 0);
-                    acc16[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[3], b3, acc16[t], 0, 0, 0);
+#pragma unroll
+                    for (int v = 0; v < NW; ++v) {
+                        acc1[v][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[0], b0[v], acc1[v][t], 0, 0, 0);
+                        acc4[v][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[1], b1[v], acc4[v][t], 0, 0, 0);
+                        acc16[v][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2], b2[v], acc16[v][t], 0, 0, 0);
+                        acc16[v][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[3], b3[v], acc16[v][t], 0, 0, 0);
+                    }
                 }
             }
         }
@@ -369,7 +397,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
         c = chunk_of(wave, j);
     };
 
-    uint4 wa[U];
+    uint4 wa[U * NW];
     const int nch0 = min(p.KS, p.Kp) >> 8;
     float a_m1 = 0.0f;  // M = 1, fused: the token's scale, uniform
     int wsum_m1 = 0;    // M = 1: code sum of the activations this wave staged, uniform
@@ -538,7 +566,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
             compute_batch(wa, 0, nch);
         } else {
             const int cpw = chunks_of_wave(0, nch);  // chunks per wave (wave 0 has the most)
-            uint4 wb[U];
+            uint4 wb[U * NW];
             for (int j0 = 0; j0 < cpw; j0 += 2 * U) {
                 load_batch(wb, j0 + U, stage_off, nch);  // zeros when past the stage
                 compute_batch(wa, j0, nch);
@@ -563,19 +591,27 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
         if (FUSED && blockIdx.x == 0 && p.a_out) p.a_out[tid] = a;
         s_inva[tid] = __builtin_amdgcn_rcpf(a);
     }
-    if constexpr (MC == 1) {
-        // row 0 of the accumulators: register 0 of lanes 0-15
-        if (lane < 16) red[wave * 256 + lane] = acc1[0][0] + (acc4[0][0] >> 2) + (acc16[0][0] >> 4) - wsum_m1;
-    } else {
-        // this wave's partials minus the code sums of the activations it staged (its own
-        // LDS slots, so no barrier is needed to read them)
+    constexpr int kRedSet = kSkWaves * MT * 4 * 64;  // ints per matrix in `red`
 #pragma unroll
-        for (int t = 0; t < MT; ++t) {
-            const v4i v = acc1[t] + (acc4[t] >> 2) + (acc16[t] >> 4);
+    for (int v = 0; v < NW; ++v) {
+        if constexpr (MC == 1) {
+            // row 0 of the accumulators: register 0 of lanes 0-15
+            if (lane < 16)
+                red[v * kRedSet + wave * 256 + lane] =
+                    acc1[v][0][0] + (acc4[v][0][0] >> 2) + (acc16[v][0][0] >> 4) - wsum_m1;
+        } else {
+            // this wave's partials minus the code sums of the activations it staged (its
+            // own LDS slots, so no barrier is needed to read them)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = 16 * t + 4 * (lane >> 4) + r;
-                if (m < M) red[((wave * MT + t) * 4 + r) * 64 + lane] = v[r] - s_wsum[wave * kSkMaxM + m];
+            for (int t = 0; t < MT; ++t) {
+                const v4i s4 = acc1[v][t] + (acc4[v][t] >> 2) + (acc16[v][t] >> 4);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = 16 * t + 4 * (lane >> 4) + r;
+                    if (m < M)
+                        red[v * kRedSet + ((wave * MT + t) * 4 + r) * 64 + lane] =
+                            s4[r] - s_wsum[wave * kSkMaxM + m];
+                }
             }
         }
     }
@@ -586,14 +622,31 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
         const int t = m >> 4, ml = m & 15;
         const int l = 16 * (ml >> 2) + col, r = ml & 3;
         if (col < rows) {
-            int acc = 0;
+            int acc[NW];
 #pragma unroll
-            for (int w = 0; w < kSkWaves; ++w) acc += red[((w * MT + t) * 4 + r) * 64 + l];
+            for (int v = 0; v < NW; ++v) {
+                acc[v] = 0;
+#pragma unroll
+                for (int w = 0; w < kSkWaves; ++w) acc[v] += red[v * kRedSet + ((w * MT + t) * 4 + r) * 64 + l];
+            }
             const float inv_a = MC == 1 ? __builtin_amdgcn_rcpf(FUSED ? a_m1 : a_in) : s_inva[m];
             // the first pass holds its column's weight scale (loaded early); later passes
             // (M > 16) read it again
-            const float wsc = idx == tid ? ws_n : w_scale[n0 + col];
-            store_out(out, (int64_t)m * N + n0 + col, p.out_dtype, acc, wsc, inv_a);
+            const int64_t o = (int64_t)m * N + n0 + col;
+            if constexpr (PAIR) {
+                // h = silu(g) * u with g, u the two products rescaled exactly as a plain
+                // output (fp32, same roundings); silu(g) = g / (1 + exp(-g))
+                const float g = ((float)acc[0] * (idx == tid ? ws_n[0] : w_scale_v[0][n0 + col])) * inv_a;
+                const float u = ((float)acc[1] * (idx == tid ? ws_n[1] : w_scale_v[1][n0 + col])) * inv_a;
+                const float h = (g / (1.0f + expf(-g))) * u;
+                if (p.out_dtype == 0)
+                    static_cast<float*>(out)[o] = h;
+                else
+                    static_cast<uint16_t*>(out)[o] = f32_to_bf16_rne(h);
+            } else {
+                const float wsc = idx == tid ? ws_n[0] : w_scale_v[0][n0 + col];
+                store_out(out, o, p.out_dtype, acc[0], wsc, inv_a);
+            }
         }
     }
 }
@@ -613,44 +666,54 @@ hipError_t allow_lds(Kernel* kernel, size_t lds) {
     return e;
 }
 
-template <bool FUSED, bool FAST, int XH, int U, bool SINGLE, int MC = 0, int MT = 1>
+template <bool FUSED, bool FAST, int XH, int U, bool SINGLE, int MC = 0, int MT = 1, bool PAIR = false>
 hipError_t launch_one(const SkinnyArgs& a, dim3 grid, size_t lds, hipStream_t stream) {
-    const hipError_t e = allow_lds(&skinny_kernel<FUSED, FAST, XH, U, SINGLE, MC, MT>, lds);
+    const hipError_t e = allow_lds(&skinny_kernel<FUSED, FAST, XH, U, SINGLE, MC, MT, PAIR>, lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((skinny_kernel<FUSED, FAST, XH, U, SINGLE, MC, MT>), grid, dim3(kSkThreads),
-                       lds, stream, a);
+    hipLaunchKernelGGL((skinny_kernel<FUSED, FAST, XH, U, SINGLE, MC, MT, PAIR>), grid,
+                       dim3(kSkThreads), lds, stream, a);
     return hipGetLastError();
 }
 
 // Batch shape: U = 4 or 8 chunks per wave; SINGLE when one batch holds a wave's share.
-template <bool FUSED, int XH>
+template <bool FUSED, int XH, bool PAIR = false>
 hipError_t launch_fast(const SkinnyArgs& a, dim3 grid, size_t lds, hipStream_t stream) {
     const int cpw = chunks_of_wave(0, a.KS / 256);
     const bool one_stage = a.KS >= a.Kp;
-    if (one_stage && cpw <= 4) return launch_one<FUSED, true, XH, 4, true>(a, grid, lds, stream);
-    if (one_stage && cpw <= 8) return launch_one<FUSED, true, XH, 8, true>(a, grid, lds, stream);
-    return launch_one<FUSED, true, XH, 8, false>(a, grid, lds, stream);
+    if (one_stage && cpw <= 4) return launch_one<FUSED, true, XH, 4, true, 0, 1, PAIR>(a, grid, lds, stream);
+    if (one_stage && cpw <= 8) return launch_one<FUSED, true, XH, 8, true, 0, 1, PAIR>(a, grid, lds, stream);
+    return launch_one<FUSED, true, XH, 8, false, 0, 1, PAIR>(a, grid, lds, stream);
 }
 
 // Held activation groups per lane: M * (chunks per wave) * 16 groups over 64 lanes.
-template <bool FUSED>
+template <bool FUSED, bool PAIR = false>
 hipError_t launch_held(const SkinnyArgs& a, dim3 grid, size_t lds, hipStream_t stream) {
     const int cpw = chunks_of_wave(0, a.Kp / 256);
     const int per_lane = (a.M * cpw + 3) / 4;
     if (a.M == 1 && a.KS >= a.Kp) {
         // one token (decode): the M = 1 specializations, by K
-        if (cpw <= 4) return launch_one<FUSED, true, 1, 4, true, 1>(a, grid, lds, stream);
-        if (cpw <= 8) return launch_one<FUSED, true, 2, 8, true, 1>(a, grid, lds, stream);
-        if (cpw <= 16) return launch_one<FUSED, true, 4, 8, false, 1>(a, grid, lds, stream);
-        if (cpw <= 32) return launch_one<FUSED, true, 8, 8, false, 1>(a, grid, lds, stream);
+        if (cpw <= 4) return launch_one<FUSED, true, 1, 4, true, 1, 1, PAIR>(a, grid, lds, stream);
+        if (cpw <= 8) return launch_one<FUSED, true, 2, 8, true, 1, 1, PAIR>(a, grid, lds, stream);
+        if (cpw <= 16) return launch_one<FUSED, true, 4, 8, false, 1, 1, PAIR>(a, grid, lds, stream);
+        if (cpw <= 32) return launch_one<FUSED, true, 8, 8, false, 1, 1, PAIR>(a, grid, lds, stream);
     }
     if (a.KS >= a.Kp) {
-        if (per_lane <= 1) return launch_fast<FUSED, 1>(a, grid, lds, stream);
-        if (per_lane <= 2) return launch_fast<FUSED, 2>(a, grid, lds, stream);
-        if (per_lane <= 4) return launch_fast<FUSED, 4>(a, grid, lds, stream);
-        if (per_lane <= 8) return launch_fast<FUSED, 8>(a, grid, lds, stream);
+        if (per_lane <= 1) return launch_fast<FUSED, 1, PAIR>(a, grid, lds, stream);
+        if (per_lane <= 2) return launch_fast<FUSED, 2, PAIR>(a, grid, lds, stream);
+        if (per_lane <= 4) return launch_fast<FUSED, 4, PAIR>(a, grid, lds, stream);
+        if (per_lane <= 8) return launch_fast<FUSED, 8, PAIR>(a, grid, lds, stream);
     }
-    return launch_fast<FUSED, 0>(a, grid, lds, stream);
+    return launch_fast<FUSED, 0, PAIR>(a, grid, lds, stream);
+}
+
+// K stage length: the activations of a stage (M rows) fit the LDS budget.
+void set_stage(SkinnyArgs& a, int64_t M, int64_t K) {
+    a.M = (int)M;
+    a.K = (int)K;
+    a.Kp = (int)((K + 255) / 256 * 256);
+    int ks = ((kSkXBudget / (int)M) - 16) / 256 * 256;
+    if (ks < 256) ks = 256;
+    a.KS = ks < a.Kp ? ks : a.Kp;
 }
 
 }  // namespace
@@ -688,12 +751,7 @@ hipError_t launch_skinny_grouped(const int8_t* xq, const float* a_scale, const u
     }
     if (blocks == 0) return hipSuccess;
     if (blocks > INT32_MAX) return hipErrorInvalidValue;
-    a.M = (int)M;
-    a.K = (int)K;
-    a.Kp = (int)((K + 255) / 256 * 256);
-    int ks = ((kSkXBudget / (int)M) - 16) / 256 * 256;
-    if (ks < 256) ks = 256;
-    a.KS = ks < a.Kp ? ks : a.Kp;
+    set_stage(a, M, K);
     a.out_dtype = out_dtype;
     const size_t lds = (size_t)M * (a.KS + 16) + kSkMisc + (size_t)kSkWaves * 4 * 64 * 4;
     const dim3 grid((unsigned)blocks);
@@ -723,6 +781,31 @@ hipError_t launch_skinny_grouped(const int8_t* xq, const float* a_scale, const u
         return launch_one<false, false, 0, 4, false>(a, grid, lds, stream);
     }
     return fused ? launch_held<true>(a, grid, lds, stream) : launch_held<false>(a, grid, lds, stream);
+}
+
+hipError_t launch_skinny_swiglu(const uint16_t* x_bf16, const uint8_t* packed_gate,
+                                const float* w_scale_gate, const uint8_t* packed_up,
+                                const float* w_scale_up, int64_t M, int64_t N, int64_t K,
+                                void* out, int out_dtype, int8_t* xq_out, float* a_out,
+                                hipStream_t stream) {
+    if (M < 1 || M > 16 || N < 1 || out_dtype == 2) return hipErrorInvalidValue;
+    SkinnyArgs a = {};
+    a.xb = x_bf16;
+    a.xq_out = xq_out;
+    a.a_out = a_out;
+    a.groups = 1;  // the blocks cover N rows once; each reads gate (0) and up (1)
+    a.g_N[0] = a.g_N[1] = (int)N;
+    a.g_packed[0] = packed_gate;
+    a.g_packed[1] = packed_up;
+    a.g_wscale[0] = w_scale_gate;
+    a.g_wscale[1] = w_scale_up;
+    a.g_out[0] = out;
+    set_stage(a, M, K);
+    a.out_dtype = out_dtype;
+    const size_t lds = (size_t)M * (a.KS + 16) + kSkMisc + (size_t)2 * kSkWaves * 4 * 64 * 4;
+    const dim3 grid((unsigned)((N + 15) / 16));
+    if (K % 64 != 0) return launch_one<true, false, 0, 4, false, 0, 1, true>(a, grid, lds, stream);
+    return launch_held<true, true>(a, grid, lds, stream);
 }
 
 }  // namespace bitnet

@@ -157,6 +157,19 @@ def test_quant_gemv_grouped_validation(L):
     assert call(A, 1, 256, 2, arrs([None, None], [None, None], [0, 0], [None, None])) == OK
 
 
+def test_quant_gemv_swiglu_validation(L):
+    f = L.bitnet_quant_gemv_swiglu
+    assert f(A, B, C, D, E, 1, 16, 256, F, 2, None, None, None) == INVALID   # int32 output
+    assert f(A, B, C, D, E, 1, 16, 256, F, 7, None, None, None) == INVALID   # bad dtype
+    assert f(None, B, C, D, E, 1, 16, 256, F, 0, None, None, None) == INVALID
+    assert f(A, B, C, None, E, 1, 16, 256, F, 0, None, None, None) == INVALID
+    assert f(A, B, C, D, E, 17, 16, 256, F, 0, None, None, None) == INVALID  # M above 16
+    assert f(A, B, C, D + 4, E, 1, 16, 256, F, 1, None, None, None) == UNALIGNED
+    assert f(A, B, C, D, E, 1, 16, 250, F, 0, None, None, None) == UNALIGNED  # K % 4
+    assert f(A, B, C, D, E, 0, 16, 256, F, 0, None, None, None) == OK
+    assert f(A, B, C, D, E, 1, 0, 256, F, 0, None, None, None) == OK
+
+
 def test_valid_call_without_gpu_reports_hip_error(L):
     # Arguments pass validation, so the library asks HIP for the device; with no GPU in
     # this container that fails and comes back as BITNET_ERR_HIP with the HIP message.

@@ -170,6 +170,38 @@ def test_quant_gemv_grouped_matches_oracle(M, K, Ns):
                                    alone.view(torch.int32) if dt != "bf16" else alone.view(torch.int16))
 
 
+def swiglu_tolerance(g_ref, u_ref, h_ref):
+    """fp32 bound for h = silu(g) * u: g and u are each within 3 ulp of exact (see
+    gpu_helpers); silu scales g's relative error by at most 1 + |g|; exp, the division
+    and the two products add one rounding each.  An absolute floor of the smallest normal
+    times |u| covers exp(-g) overflowing to inf for g < -88 (h then underflows to 0)."""
+    return (12.0 + 6.0 * np.abs(g_ref)) * 2.0 ** -23 * np.abs(h_ref) + 2.0 ** -126 * np.abs(u_ref)
+
+
+@pytest.mark.parametrize("M", [1, 3, 16])
+@pytest.mark.parametrize("N,K", [(16, 256), (300, 1024), (37, 260), (129, 2560), (50, 6912),
+                                 (20, 28672)])
+def test_quant_gemv_swiglu_matches_oracle(M, N, K):
+    """gate and up in one launch with h = silu(g) * u written out, against the oracle's
+    swiglu of its exact products."""
+    X = workloads.activations(M, K, seed=M * 11000 + N + K)
+    pg = Problem(M, N, K, seed=M * 11000 + N + K + 1, X=X)
+    pu = Problem(M, N, K, seed=M * 11000 + N + K + 2, X=X)
+    og, ou = pg.oracle(), pu.oracle()
+    h_ref = oracle.swiglu(og["ref"], ou["ref"])
+    lim = swiglu_tolerance(og["ref"], ou["ref"], h_ref)
+    pk_g, s_g, pk_u, s_u = dev(og["packed"]), dev(og["w_scale"]), dev(ou["packed"]), dev(ou["w_scale"])
+    h, xq, a = bw.quant_gemv_swiglu(pg.x_dev, pk_g, s_g, pk_u, s_u, "f32", return_quant=True)
+    assert np.array_equal(to_np(a), og["a_scale"]) and np.array_equal(to_np(xq), og["xq"])
+    err = np.abs(to_np(h).astype(np.float64) - h_ref)
+    bad = np.flatnonzero((err > lim).reshape(-1))
+    assert bad.size == 0, f"swiglu M={M} N={N} K={K}: {bad.size} fp32 outputs beyond the bound"
+    hb = to_np(bw.quant_gemv_swiglu(pg.x_dev, pk_g, s_g, pk_u, s_u, "bf16"))
+    from gpu_helpers import bf16_key
+    d = np.abs(bf16_key(hb) - bf16_key(oracle.f64_to_bf16(h_ref)))
+    assert d.max(initial=0) <= 1, f"swiglu bf16 M={M} N={N} K={K}: off by {d.max()} ulp"
+
+
 def test_extreme_accumulators():
     # every activation at +-127 and every weight +1 / -1: |acc| = 127 K, the largest sums
     M, N, K = 3, 40, 28672

@@ -40,6 +40,12 @@ MUTATIONS = {
                    "double r = floor(x / quantum) * quantum;"),
     "bf16_double_rounding": ("double r = nearbyint(x / quantum) * quantum;",
                              "double r = nearbyint((double)(float)x / quantum) * quantum;"),
+    "swiglu_sign_of_exp": ("h[t] = g[t] / (1.0 + exp(-g[t])) * u[t];",
+                           "h[t] = g[t] / (1.0 + exp(g[t])) * u[t];"),
+    "swiglu_sigmoid_only": ("h[t] = g[t] / (1.0 + exp(-g[t])) * u[t];",
+                            "h[t] = 1.0 / (1.0 + exp(-g[t])) * u[t];"),
+    "swiglu_swapped_operands": ("h[t] = g[t] / (1.0 + exp(-g[t])) * u[t];",
+                                "h[t] = u[t] / (1.0 + exp(-u[t])) * g[t];"),
 }
 
 

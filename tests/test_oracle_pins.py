@@ -306,3 +306,37 @@ def test_tiny_workload_end_to_end_brute_force():
     assert np.allclose(out["ref"], deq, rtol=1e-12, atol=1e-12)
     frac0 = float(np.mean(q == 0))
     assert 0.25 < frac0 < 0.37
+
+
+# ------------------------------------------------------------------- O5 swiglu
+
+
+def test_swiglu_closed_forms():
+    """silu(g) = g * sigmoid(g): sigmoid(ln 3) = 3/4 and sigmoid(-ln 3) = 1/4 exactly, so
+    h(ln 3, u) = 0.75 ln 3 u and h(-ln 3, u) = -0.25 ln 3 u; the gate is the SiLU's
+    argument (swapping g and u gives 2 sigmoid(2) ln 3, not 1.5 ln 3)."""
+    L3 = math.log(3.0)
+    h = oracle.swiglu(np.array([L3, -L3, L3, 0.0, 2.0]), np.array([1.0, 1.0, 2.0, 5.0, L3]))
+    assert abs(h[0] - 0.75 * L3) <= 1e-15
+    assert abs(h[1] + 0.25 * L3) <= 1e-15
+    assert abs(h[2] - 1.5 * L3) <= 2e-15
+    assert h[3] == 0.0
+    assert abs(h[4] - 1.5 * L3) > 0.1
+
+
+def test_swiglu_invariants():
+    """silu(x) - silu(-x) = x; silu(x) -> x for large x and -> x e^x for very negative x;
+    linear in u; odd in u."""
+    rng = np.random.default_rng(5)
+    x = rng.normal(0, 4, 1000)
+    ones = np.ones_like(x)
+    d = oracle.swiglu(x, ones) - oracle.swiglu(-x, ones)
+    assert np.max(np.abs(d - x)) <= 1e-12
+    big = np.array([40.0, 60.0])
+    assert np.allclose(oracle.swiglu(big, np.ones(2)), big, rtol=1e-15, atol=0)
+    neg = np.array([-40.0, -60.0])
+    assert np.allclose(oracle.swiglu(neg, np.ones(2)), neg * np.exp(neg), rtol=1e-12, atol=0)
+    u = rng.normal(0, 1, 1000)
+    h1 = oracle.swiglu(x, u)
+    assert np.max(np.abs(oracle.swiglu(x, 3.0 * u) - 3.0 * h1)) <= 1e-12 * np.max(np.abs(h1))
+    assert np.array_equal(oracle.swiglu(x, -u), -h1)
