@@ -119,6 +119,35 @@ int bitnet_quant_act(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float*
                      void* stream);
 
 /*
+ * bitnet_quant_act_per_tensor -- the same quantization with one scale for the whole
+ * tensor ("BitNet 1-bit LLM推理优化" §2.2: the I2_S kernel keeps the per-tensor int8
+ * activation quantization used in training; §3.2: per-tensor or per-channel scales):
+ *   a = 127 / max(max_{m,k} |x[m,k]|, 1e-5), written to every a_scale[m] (so the product
+ *   entry points take it unchanged); xq[m,k] = clamp(round_half_even(x * a), -127, 127).
+ * At M = 1 it equals bitnet_quant_act.  Three launches (row maxima, which use a_scale as
+ * scratch; the tensor scale; the codes).
+ */
+int bitnet_quant_act_per_tensor(const uint16_t* x, int64_t M, int64_t K, int8_t* xq,
+                                float* a_scale, void* stream);
+
+/* 2-bit code tables for bitnet_repack_codes. */
+typedef enum {
+    BITNET_CODES_OFFSET = 0, /* this library: code = w + 1 (00 -1, 01 0, 10 +1, 11 unused) */
+    BITNET_CODES_SIGN = 1    /* "BitNet 深度实战" §4.3: 00 0, 01 -1, 11 +1, 10 unused         */
+} bitnet_code_table;
+
+/*
+ * bitnet_repack_codes -- rewrite a packed (N, K/4) array from one code table to the
+ * other (same bit positions: weight 4j+i in bits 2i..2i+1 of byte j).  Converts weights
+ * packed with the page's table for use here, and back.  in and out may be the same
+ * buffer.  A field holding its table's unused code becomes weight 0; when
+ * invalid_count (a device int32, caller-zeroed) is given, the number of such fields is
+ * added to it.
+ */
+int bitnet_repack_codes(const uint8_t* in, int64_t N, int64_t K, int from_table, int to_table,
+                        uint8_t* out, int32_t* invalid_count, void* stream);
+
+/*
  * bitnet_w2a8_gemv -- decode-sized product, 1 <= M <= BITNET_GEMV_MAX_M
  * ("BitNet 深度实战" §4.4; "BitNet-Triton" 技术架构 §1).
  *   xq, a_scale       : as produced by bitnet_quant_act.

@@ -15,6 +15,8 @@ Functions and the pages they follow (page titles abbreviated):
                    §4.3: four weights per byte, first weight in bits 0-1.
   act_quant     -- "BitNet-Triton" 技术架构 §3 / "BitNet 1-bit LLM推理优化" (blog.hotdry.top)
                    §3.2: int8 activations, per-token absmax scale 127/max|x|.
+  act_quant_per_tensor -- "BitNet 1-bit LLM推理优化" §2.2 / §3.2: one scale per tensor.
+  repack        -- "BitNet 深度实战" §4.3: the page's 00/01/11 code table <-> code = w + 1.
   accumulate    -- "BitNet 深度实战" §4.4: int8 x ternary into int32.
   rescale       -- "BitNet 深度实战" §2.4 / §3.2: out = acc * w_scale / a_scale.
   swiglu        -- "BitNet 深度实战" §3.2: the MLP's silu(gate(x)) * up(x).
@@ -81,11 +83,14 @@ def _load():
             "oracle_rescale_sampled": [p, p, p, p, p, i64, p, p, p],
             "oracle_f64_to_bf16": [p, i64, p],
             "oracle_swiglu": [p, p, i64, p],
+            "oracle_act_quant_per_tensor": [p, i64, i64, p, p],
         }
         for name, args in sig.items():
             fn = getattr(lib, name)
             fn.argtypes = args
             fn.restype = ctypes.c_int if name != "oracle_f64_to_bf16" else None
+        lib.oracle_repack.argtypes = [p, i64, i64, ctypes.c_int, ctypes.c_int, p]
+        lib.oracle_repack.restype = i64
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
         _lib = lib
@@ -169,6 +174,38 @@ def act_quant(x_bf16_bits: np.ndarray):
 
 
 # --------------------------------------------------------------------------- O3
+
+
+def act_quant_per_tensor(x_bf16_bits: np.ndarray):
+    """One int8 scale for the whole (M, K) tensor ("BitNet 1-bit LLM推理优化" §2.2, §3.2).
+
+    Returns (xq int8 (M, K), a_scale float32 (M,), every entry 127 / max|x|)."""
+    x = np.ascontiguousarray(x_bf16_bits, dtype=np.uint16)
+    M, K = x.shape
+    xq = np.empty((M, K), np.int8)
+    a = np.empty((M,), np.float32)
+    rc = _load().oracle_act_quant_per_tensor(_ptr(x), M, K, _ptr(xq), _ptr(a))
+    if rc == 1:
+        raise OracleError("act_quant_per_tensor: the +-127 clamp fired, which the definition "
+                          "rules out")
+    _check(rc, "act_quant_per_tensor")
+    return xq, a
+
+
+CODES_OFFSET, CODES_SIGN = 0, 1
+
+
+def repack(packed: np.ndarray, K: int, from_table: int, to_table: int):
+    """Rewrite packed (N, K/4) bytes between the code tables ("BitNet 深度实战" §4.3).
+
+    Returns (out uint8 (N, K/4), number of fields that held the source's unused code)."""
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    N = packed.shape[0]
+    out = np.empty_like(packed)
+    bad = _load().oracle_repack(_ptr(packed), N, K, int(from_table), int(to_table), _ptr(out))
+    if bad < 0:
+        raise OracleError("repack: bad arguments")
+    return out, int(bad)
 
 
 def accumulate(xq: np.ndarray, packed: np.ndarray, K: int) -> np.ndarray:

@@ -169,6 +169,35 @@ int oracle_act_quant(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float*
     return clamped;
 }
 
+/*
+ * Per-tensor variant. [Layout] §2.2 (I2_S): the MAD kernel keeps the per-tensor int8
+ * activation quantization of training; [Layout] §3.2: per-tensor or per-channel scales.
+ * amax is the max |x| over the whole (M, K) tensor (clamped below at 1e-5), scale =
+ * 127 / amax for every row, codes as above.
+ */
+int oracle_act_quant_per_tensor(const uint16_t* x, int64_t M, int64_t K, int8_t* xq,
+                                float* a_scale) {
+    if (!x || !xq || !a_scale || M < 0 || K < 1) return -1;
+    float amax = 0.0f;
+    for (int64_t i = 0; i < M * K; ++i) {
+        float v = fabsf(bf16_to_f32(x[i]));
+        if (v > amax) amax = v;
+    }
+    const float amax_t = amax < 1e-5f ? 1e-5f : amax;
+    const float a_t = 127.0f / amax_t;
+    int clamped = 0;
+    for (int64_t m = 0; m < M; ++m) {
+        a_scale[m] = a_t;
+        for (int64_t k = 0; k < K; ++k) {
+            float r = nearbyintf(bf16_to_f32(x[m * K + k]) * a_t);
+            if (r > 127.0f) { r = 127.0f; clamped = 1; }
+            if (r < -127.0f) { r = -127.0f; clamped = 1; }
+            xq[m * K + k] = (int8_t)r;
+        }
+    }
+    return clamped;
+}
+
 /* -------------------------------------------------- O3: exact int accumulation --- */
 
 /* Decode weight (n, k) from the packed array: the inverse of the byte layout above. */
@@ -259,6 +288,42 @@ int oracle_rescale_sampled(const int32_t* acc, const float* a_scale, const float
         rescale_one(acc[t], w_scale[ns[t]], a_scale[ms[t]], ref ? ref + t : NULL,
                     out_f32 ? out_f32 + t : NULL, out_bf16 ? out_bf16 + t : NULL);
     return 0;
+}
+
+/* ------------------------------------------------------ code table conversion --- */
+
+/*
+ * [Deep] §4.3 (位打包) prints a second 2-bit code table: 11 -> +1, 00 -> 0, 01 -> -1, 10
+ * never used, with the same bit positions (weight 4j+i in bits 2i..2i+1).  Table 0 is
+ * this library's code = w + 1 (11 never used).  Each field is decoded with the source
+ * table and encoded with the destination table; a field holding the unused code is
+ * counted and written as weight 0.  Returns the count (or -1 on bad arguments).
+ */
+static int table_weight(int table, unsigned c) {
+    static const int offset_table[4] = {-1, 0, 1, 99};
+    static const int sign_table[4] = {0, -1, 99, 1};
+    return table == 0 ? offset_table[c] : sign_table[c];
+}
+
+static unsigned table_code(int table, int w) {
+    if (table == 0) return (unsigned)(w + 1);
+    return w == 1 ? 3u : (w == -1 ? 1u : 0u);
+}
+
+int64_t oracle_repack(const uint8_t* in, int64_t N, int64_t K, int from, int to, uint8_t* out) {
+    if (!in || !out || N < 0 || K < 4 || K % 4 || from < 0 || from > 1 || to < 0 || to > 1)
+        return -1;
+    int64_t bad = 0;
+    for (int64_t j = 0; j < N * (K / 4); ++j) {
+        unsigned byte = 0;
+        for (int i = 0; i < 4; ++i) {
+            int w = table_weight(from, (in[j] >> (2 * i)) & 3u);
+            if (w == 99) { ++bad; w = 0; }
+            byte |= table_code(to, w) << (2 * i);
+        }
+        out[j] = (uint8_t)byte;
+    }
+    return bad;
 }
 
 /* ------------------------------------------------------- O5: SwiGLU of the MLP --- */

@@ -25,9 +25,13 @@ from ._binding import (  # noqa: F401
     library_path,
     pack_weights,
     quant_act,
+    quant_act_per_tensor,
     quant_gemv,
     quant_gemv_grouped,
     quant_gemv_swiglu,
     status_str,
     unpack_weights,
+    repack_codes,
+    CODES_OFFSET,
+    CODES_SIGN,
 )

@@ -64,6 +64,8 @@ def lib():
             "bitnet_quant_gemv": ([p, p, p, i64, i64, i64, p, i32, p, p, p], i32),
             "bitnet_quant_gemv_grouped": ([p, i64, i64, i64, p, p, p, p, i32, p, p, p], i32),
             "bitnet_quant_gemv_swiglu": ([p, p, p, p, p, i64, i64, i64, p, i32, p, p, p], i32),
+            "bitnet_quant_act_per_tensor": ([p, i64, i64, p, p, p], i32),
+            "bitnet_repack_codes": ([p, i64, i64, i32, i32, p, p, p], i32),
         }
         for name, (args, res) in sigs.items():
             fn = getattr(L, name)
@@ -157,6 +159,40 @@ def quant_act(x: torch.Tensor, xq: torch.Tensor | None = None,
                                   _tensor(a_scale, torch.float32, "a_scale", (M,)), _stream(x)),
            "bitnet_quant_act")
     return xq, a_scale
+
+
+def quant_act_per_tensor(x: torch.Tensor, xq: torch.Tensor | None = None,
+                         a_scale: torch.Tensor | None = None):
+    """bf16 (M, K) -> (int8 (M, K), fp32 (M,)) with one scale for the whole tensor."""
+    M, K = x.shape
+    if xq is None:
+        xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if a_scale is None:
+        a_scale = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _check(lib().bitnet_quant_act_per_tensor(_tensor(x, torch.bfloat16, "x", (M, K)), M, K,
+                                             _tensor(xq, torch.int8, "xq", (M, K)),
+                                             _tensor(a_scale, torch.float32, "a_scale", (M,)),
+                                             _stream(x)),
+           "bitnet_quant_act_per_tensor")
+    return xq, a_scale
+
+
+CODES_OFFSET, CODES_SIGN = 0, 1
+
+
+def repack_codes(packed: torch.Tensor, K: int, from_table: int, to_table: int,
+                 out: torch.Tensor | None = None, invalid_count: torch.Tensor | None = None):
+    """Rewrite a packed (N, K/4) array from one 2-bit code table to the other."""
+    N = packed.shape[0]
+    if out is None:
+        out = torch.empty_like(packed)
+    _check(lib().bitnet_repack_codes(_tensor(packed, torch.uint8, "packed", (N, K // 4)), N, K,
+                                     int(from_table), int(to_table),
+                                     _tensor(out, torch.uint8, "out", (N, K // 4)),
+                                     _opt_ptr(invalid_count, torch.int32, "invalid_count", (1,)),
+                                     _stream(packed)),
+           "bitnet_repack_codes")
+    return out
 
 
 def _alloc_out(out, M, N, code, device):

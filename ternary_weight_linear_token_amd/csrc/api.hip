@@ -212,6 +212,30 @@ int bitnet_quant_gemv_grouped(const uint16_t* x, int64_t M, int64_t K, int64_t g
                                                     a_scale_out, as_stream(stream)));
 }
 
+int bitnet_quant_act_per_tensor(const uint16_t* x, int64_t M, int64_t K, int8_t* xq,
+                                float* a_scale, void* stream) {
+    int st = check_shape(M, 0, K);
+    if (st) return st;
+    if (M == 0) return BITNET_OK;
+    if (!x || !xq || !a_scale) return BITNET_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(xq) || !aligned16(a_scale)) return BITNET_ERR_UNALIGNED;
+    if ((st = check_device())) return st;
+    return record_hip(bitnet::launch_quant_act_per_tensor(x, M, K, xq, a_scale, as_stream(stream)));
+}
+
+int bitnet_repack_codes(const uint8_t* in, int64_t N, int64_t K, int from_table, int to_table,
+                        uint8_t* out, int32_t* invalid_count, void* stream) {
+    const auto valid_table = [](int t) { return t == BITNET_CODES_OFFSET || t == BITNET_CODES_SIGN; };
+    if (!valid_table(from_table) || !valid_table(to_table)) return BITNET_ERR_INVALID_ARG;
+    int st = check_shape(0, N, K);
+    if (st) return st;
+    if (N == 0) return BITNET_OK;
+    if (!in || !out) return BITNET_ERR_INVALID_ARG;
+    if ((st = check_device())) return st;
+    return record_hip(bitnet::launch_repack_codes(in, N, K, from_table, to_table, out,
+                                                  invalid_count, as_stream(stream)));
+}
+
 int bitnet_quant_gemv_swiglu(const uint16_t* x, const uint8_t* packed_gate,
                              const float* w_scale_gate, const uint8_t* packed_up,
                              const float* w_scale_up, int64_t M, int64_t N, int64_t K, void* h,

@@ -15,6 +15,13 @@ hipError_t launch_unpack_weights(const uint8_t* packed, int64_t N, int64_t K, in
                                  hipStream_t stream);
 hipError_t launch_quant_act(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float* a_scale,
                             hipStream_t stream);
+// One activation scale for the whole (M, K) tensor, written to every a_scale[m].
+hipError_t launch_quant_act_per_tensor(const uint16_t* x, int64_t M, int64_t K, int8_t* xq,
+                                       float* a_scale, hipStream_t stream);
+// Rewrite packed weights from one 2-bit code table to another (0: code = w + 1; 1: the
+// 00/01/11 table); fields holding an unused code become 0 and are counted in *invalid.
+hipError_t launch_repack_codes(const uint8_t* in, int64_t N, int64_t K, int from, int to,
+                               uint8_t* out, int* invalid, hipStream_t stream);
 
 // Weight-streaming product for 1 <= M <= 16.  When x_bf16 is non-null the activations
 // are quantized inside the kernel (xq / a_scale ignored; xq_out / a_out optional copies).

@@ -111,7 +111,11 @@ __global__ __launch_bounds__(256) void unpack_kernel(const uint8_t* __restrict__
 // Pass 2: a = 127 / max(amax, 1e-5) (IEEE division), q = clamp(rne(x * a), +-127).
 // Rows up to G*1024 elements keep their loads in registers between the passes; longer
 // rows (G == 0) read the row twice.
-template <int G>
+// MODE 0: per-token scale (both passes).  Per-tensor scale, three launches: MODE 1 runs
+// pass 1 only and leaves the row's max magnitude bits in a_scale[m]; tensor_scale_kernel
+// reduces them and writes the common scale to every a_scale[m]; MODE 2 runs pass 2 with
+// the scale read from a_scale[m].
+template <int G, int MODE = 0>
 __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restrict__ x,
                                                         int64_t K, int8_t* __restrict__ xq,
                                                         float* __restrict__ a_scale) {
@@ -123,7 +127,15 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restri
 
     uint2 held[G > 0 ? G : 1];
     uint32_t mx = 0;
-    if (G > 0) {
+    if (MODE == 2) {
+        if (G > 0) {
+#pragma unroll
+            for (int i = 0; i < G; ++i) {
+                int64_t g = tid + (int64_t)i * 256;
+                held[i] = g < groups ? row[g] : make_uint2(0u, 0u);
+            }
+        }
+    } else if (G > 0) {
 #pragma unroll
         for (int i = 0; i < G; ++i) {
             int64_t g = tid + (int64_t)i * 256;
@@ -141,14 +153,23 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restri
             mx = max(mx, max(max(a & 0xFFFFu, a >> 16), max(b & 0xFFFFu, b >> 16)));
         }
     }
-    mx = wave_max_u32(mx);
-    if ((tid & 63) == 0) s_max[tid >> 6] = mx;
-    __syncthreads();
-    mx = max(max(s_max[0], s_max[1]), max(s_max[2], s_max[3]));
-    float amax = bf16_bits_to_f32(mx);
-    amax = amax < 1e-5f ? 1e-5f : amax;
-    const float a = 127.0f / amax;
-    if (tid == 0) a_scale[m] = a;
+    float a;
+    if constexpr (MODE == 2) {
+        a = a_scale[m];
+    } else {
+        mx = wave_max_u32(mx);
+        if ((tid & 63) == 0) s_max[tid >> 6] = mx;
+        __syncthreads();
+        mx = max(max(s_max[0], s_max[1]), max(s_max[2], s_max[3]));
+        if constexpr (MODE == 1) {
+            if (tid == 0) reinterpret_cast<uint32_t*>(a_scale)[m] = mx;  // bits of max |x|
+            return;
+        }
+        float amax = bf16_bits_to_f32(mx);
+        amax = amax < 1e-5f ? 1e-5f : amax;
+        a = 127.0f / amax;
+        if (tid == 0) a_scale[m] = a;
+    }
 
     uint32_t* orow = reinterpret_cast<uint32_t*>(xq + m * K);
     auto quant4 = [&](uint2 v) -> uint32_t {
@@ -171,6 +192,64 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restri
     } else {
         for (int64_t g = tid; g < groups; g += 256) orow[g] = quant4(row[g]);
     }
+}
+
+// One block: the tensor's max magnitude from the rows' (a_scale[m] holds the bits of the
+// bf16 max |x| of row m), then a = 127 / max(amax, 1e-5) into every a_scale[m].
+__global__ __launch_bounds__(256) void tensor_scale_kernel(int64_t M, float* __restrict__ a_scale) {
+    __shared__ uint32_t s_max[4];
+    const int tid = threadIdx.x;
+    uint32_t mx = 0;
+    const uint32_t* bits = reinterpret_cast<const uint32_t*>(a_scale);
+    for (int64_t m = tid; m < M; m += 256) mx = max(mx, bits[m]);
+    mx = wave_max_u32(mx);
+    if ((tid & 63) == 0) s_max[tid >> 6] = mx;
+    __syncthreads();
+    mx = max(max(s_max[0], s_max[1]), max(s_max[2], s_max[3]));
+    float amax = bf16_bits_to_f32(mx);
+    amax = amax < 1e-5f ? 1e-5f : amax;
+    const float a = 127.0f / amax;
+    for (int64_t m = tid; m < M; m += 256) a_scale[m] = a;
+}
+
+// ------------------------------------------------------------- code tables ---
+// Field value -> weight for a table, -2 for a code the table leaves unused.
+//   table 0 (this library): code = w + 1  (00 -> -1, 01 -> 0, 10 -> +1, 11 unused)
+//   table 1 ("BitNet 深度实战" §4.3):      (00 -> 0, 01 -> -1, 11 -> +1, 10 unused)
+__device__ __forceinline__ int code_to_weight(int table, uint32_t c) {
+    if (table == 0) return c == 3u ? -2 : (int)c - 1;
+    return c == 0u ? 0 : (c == 1u ? -1 : (c == 3u ? 1 : -2));
+}
+__device__ __forceinline__ uint32_t weight_to_code(int table, int w) {
+    if (table == 0) return (uint32_t)(w + 1);
+    return w == 0 ? 0u : (w < 0 ? 1u : 3u);
+}
+
+// One thread per 4 packed bytes (16 weights); fields keep their positions.  A field
+// holding its table's unused code becomes weight 0 and is counted in *invalid (if
+// given).
+__global__ __launch_bounds__(256) void repack_kernel(const uint8_t* in,
+                                                     int64_t bytes, int from, int to,
+                                                     uint8_t* out,  // may alias in
+                                                     int* __restrict__ invalid) {
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i >= bytes) return;
+    const int n = bytes - i < 4 ? (int)(bytes - i) : 4;
+    uint32_t d = 0;
+    for (int b = 0; b < n; ++b) d |= (uint32_t)in[i + b] << (8 * b);
+    uint32_t r = 0;
+    int bad = 0;
+#pragma unroll
+    for (int f = 0; f < 16; ++f) {
+        int w = code_to_weight(from, (d >> (2 * f)) & 3u);
+        if (w == -2) {
+            ++bad;
+            w = 0;
+        }
+        r |= weight_to_code(to, w) << (2 * f);
+    }
+    for (int b = 0; b < n; ++b) out[i + b] = (uint8_t)(r >> (8 * b));
+    if (bad && invalid) atomicAdd(invalid, bad);
 }
 
 // ------------------------------------------------------------------ launchers ---
@@ -196,25 +275,49 @@ hipError_t launch_unpack_weights(const uint8_t* packed, int64_t N, int64_t K, in
     return hipGetLastError();
 }
 
-hipError_t launch_quant_act(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float* a_scale,
-                            hipStream_t stream) {
+template <int MODE>
+hipError_t launch_quant_rows(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float* a_scale,
+                             hipStream_t stream) {
     const int64_t groups = K / 4;
     const int64_t per_thread = (groups + 255) / 256;
     dim3 grid((unsigned)M), blk(256);
     if (per_thread <= 1)
-        hipLaunchKernelGGL(quant_act_kernel<1>, grid, blk, 0, stream, x, K, xq, a_scale);
+        hipLaunchKernelGGL((quant_act_kernel<1, MODE>), grid, blk, 0, stream, x, K, xq, a_scale);
     else if (per_thread <= 2)
-        hipLaunchKernelGGL(quant_act_kernel<2>, grid, blk, 0, stream, x, K, xq, a_scale);
+        hipLaunchKernelGGL((quant_act_kernel<2, MODE>), grid, blk, 0, stream, x, K, xq, a_scale);
     else if (per_thread <= 4)
-        hipLaunchKernelGGL(quant_act_kernel<4>, grid, blk, 0, stream, x, K, xq, a_scale);
+        hipLaunchKernelGGL((quant_act_kernel<4, MODE>), grid, blk, 0, stream, x, K, xq, a_scale);
     else if (per_thread <= 8)
-        hipLaunchKernelGGL(quant_act_kernel<8>, grid, blk, 0, stream, x, K, xq, a_scale);
+        hipLaunchKernelGGL((quant_act_kernel<8, MODE>), grid, blk, 0, stream, x, K, xq, a_scale);
     else if (per_thread <= 16)
-        hipLaunchKernelGGL(quant_act_kernel<16>, grid, blk, 0, stream, x, K, xq, a_scale);
+        hipLaunchKernelGGL((quant_act_kernel<16, MODE>), grid, blk, 0, stream, x, K, xq, a_scale);
     else if (per_thread <= 32)
-        hipLaunchKernelGGL(quant_act_kernel<32>, grid, blk, 0, stream, x, K, xq, a_scale);
+        hipLaunchKernelGGL((quant_act_kernel<32, MODE>), grid, blk, 0, stream, x, K, xq, a_scale);
     else
-        hipLaunchKernelGGL(quant_act_kernel<0>, grid, blk, 0, stream, x, K, xq, a_scale);
+        hipLaunchKernelGGL((quant_act_kernel<0, MODE>), grid, blk, 0, stream, x, K, xq, a_scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_act(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float* a_scale,
+                            hipStream_t stream) {
+    return launch_quant_rows<0>(x, M, K, xq, a_scale, stream);
+}
+
+hipError_t launch_quant_act_per_tensor(const uint16_t* x, int64_t M, int64_t K, int8_t* xq,
+                                       float* a_scale, hipStream_t stream) {
+    hipError_t e = launch_quant_rows<1>(x, M, K, xq, a_scale, stream);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(tensor_scale_kernel, dim3(1), dim3(256), 0, stream, M, a_scale);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return launch_quant_rows<2>(x, M, K, xq, a_scale, stream);
+}
+
+hipError_t launch_repack_codes(const uint8_t* in, int64_t N, int64_t K, int from, int to,
+                               uint8_t* out, int* invalid, hipStream_t stream) {
+    const int64_t bytes = N * (K / 4);
+    const int64_t threads = (bytes + 3) / 4;
+    hipLaunchKernelGGL(repack_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                       stream, in, bytes, from, to, out, invalid);
     return hipGetLastError();
 }
 

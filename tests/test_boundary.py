@@ -170,6 +170,21 @@ def test_quant_gemv_swiglu_validation(L):
     assert f(A, B, C, D, E, 1, 0, 256, F, 0, None, None, None) == OK
 
 
+def test_per_tensor_and_repack_validation(L):
+    f = L.bitnet_quant_act_per_tensor
+    assert f(None, 1, 256, B, C, None) == INVALID
+    assert f(A, 1, 250, B, C, None) == UNALIGNED
+    assert f(A, 1, 256, B + 4, C, None) == UNALIGNED
+    assert f(A, -1, 256, B, C, None) == INVALID
+    assert f(A, 0, 256, B, C, None) == OK
+    g = L.bitnet_repack_codes
+    assert g(A, 4, 256, 0, 2, B, None, None) == INVALID   # unknown table
+    assert g(A, 4, 256, -1, 1, B, None, None) == INVALID
+    assert g(None, 4, 256, 0, 1, B, None, None) == INVALID
+    assert g(A, 4, 254, 0, 1, B, None, None) == UNALIGNED
+    assert g(A, 0, 256, 0, 1, B, None, None) == OK
+
+
 def test_valid_call_without_gpu_reports_hip_error(L):
     # Arguments pass validation, so the library asks HIP for the device; with no GPU in
     # this container that fails and comes back as BITNET_ERR_HIP with the HIP message.

@@ -63,6 +63,56 @@ def test_quant_act_special_rows():
     assert to_np(xq)[1, :8].tolist() == [127, 62, 2, 0, 0, -2, 0, -127]
 
 
+@pytest.mark.parametrize("M,K", [(1, 2560), (4, 256), (3, 260), (512, 2560), (7, 28672),
+                                 (64, 14336), (2, 4), (300, 1028)])
+def test_quant_act_per_tensor_matches_oracle(M, K):
+    X = workloads.activations(M, K, seed=M * 13 + K)
+    xq_ref, a_ref = oracle.act_quant_per_tensor(workloads.bf16_bits(X))
+    xq, a = bw.quant_act_per_tensor(X.cuda())
+    assert np.array_equal(to_np(a), a_ref)
+    assert np.array_equal(to_np(xq), xq_ref)
+    if M == 1:
+        xq1, a1 = bw.quant_act(X.cuda())
+        assert torch.equal(xq1, xq) and torch.equal(a1, a)
+
+
+def test_per_tensor_scales_feed_the_products():
+    """The product entry points take a per-tensor scale as M equal per-row scales."""
+    M, N, K = 40, 300, 1024
+    pb = Problem(M, N, K, seed=77)
+    o = pb.oracle(full=False)
+    xq_ref, a_ref = oracle.act_quant_per_tensor(pb.xbits)
+    acc = oracle.accumulate(xq_ref, o["packed"], K)
+    ref, _, _ = oracle.rescale(acc, a_ref, o["w_scale"])
+    xq, a = bw.quant_act_per_tensor(pb.x_dev)
+    for algo in ("tiled", "skinny"):
+        out = bw.gemm(xq, a, dev(o["packed"]), dev(o["w_scale"]), "f32", algo=algo)
+        check_out(to_np(out), acc, ref, "f32", f"per-tensor {algo}")
+
+
+# ---------------------------------------------------------------- code tables
+
+
+@pytest.mark.parametrize("N,K", [(1, 4), (3, 12), (129, 260), (640, 2560)])
+def test_repack_codes_matches_oracle(N, K):
+    rng = np.random.default_rng(N + K)
+    raw = rng.integers(0, 256, size=(N, K // 4), dtype=np.uint8)  # includes unused codes
+    for src, dst in ((bw.CODES_OFFSET, bw.CODES_SIGN), (bw.CODES_SIGN, bw.CODES_OFFSET),
+                     (bw.CODES_OFFSET, bw.CODES_OFFSET)):
+        ref, bad = oracle.repack(raw, K, src, dst)
+        cnt = torch.zeros((1,), dtype=torch.int32, device="cuda")
+        out = bw.repack_codes(dev(raw), K, src, dst, invalid_count=cnt)
+        assert np.array_equal(to_np(out), ref), f"repack {src}->{dst} N={N} K={K}"
+        assert int(cnt.item()) == bad
+    # in place, and a round trip of valid weights restores them
+    p, _ = oracle.pack_weights(workloads.latent_weights(N, K, seed=3).numpy())
+    buf = dev(p)
+    bw.repack_codes(buf, K, bw.CODES_OFFSET, bw.CODES_SIGN, out=buf)
+    assert np.array_equal(to_np(buf), oracle.repack(p, K, 0, 1)[0])
+    bw.repack_codes(buf, K, bw.CODES_SIGN, bw.CODES_OFFSET, out=buf)
+    assert np.array_equal(to_np(buf), p)
+
+
 # ---------------------------------------------------------------- weight packing
 
 

@@ -40,6 +40,14 @@ MUTATIONS = {
                    "double r = floor(x / quantum) * quantum;"),
     "bf16_double_rounding": ("double r = nearbyint(x / quantum) * quantum;",
                              "double r = nearbyint((double)(float)x / quantum) * quantum;"),
+    "per_tensor_scale_constant": ("const float a_t = 127.0f / amax_t;",
+                                  "const float a_t = 128.0f / amax_t;"),
+    "per_tensor_uses_first_row": ("for (int64_t i = 0; i < M * K; ++i) {\n        float v = fabsf",
+                                  "for (int64_t i = 0; i < K; ++i) {\n        float v = fabsf"),
+    "repack_sign_table_minus_one": ("return w == 1 ? 3u : (w == -1 ? 1u : 0u);",
+                                    "return w == 1 ? 3u : (w == -1 ? 2u : 0u);"),
+    "repack_field_order": ("byte |= table_code(to, w) << (2 * i);",
+                           "byte |= table_code(to, w) << (2 * (3 - i));"),
     "swiglu_sign_of_exp": ("h[t] = g[t] / (1.0 + exp(-g[t])) * u[t];",
                            "h[t] = g[t] / (1.0 + exp(g[t])) * u[t];"),
     "swiglu_sigmoid_only": ("h[t] = g[t] / (1.0 + exp(-g[t])) * u[t];",

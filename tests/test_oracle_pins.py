@@ -340,3 +340,70 @@ def test_swiglu_invariants():
     h1 = oracle.swiglu(x, u)
     assert np.max(np.abs(oracle.swiglu(x, 3.0 * u) - 3.0 * h1)) <= 1e-12 * np.max(np.abs(h1))
     assert np.array_equal(oracle.swiglu(x, -u), -h1)
+
+
+# ------------------------------------------------ per-tensor activation scale
+
+
+def _bits(rows):
+    return workloads.bf16_bits(torch.tensor(rows, dtype=torch.float32).to(torch.bfloat16))
+
+
+def test_act_quant_per_tensor_worked_values():
+    """amax over the tensor is 8, so a = 127/8 = 15.875 for both rows: 1 -> 16 (15.875),
+    -2 -> -32 (-31.75), 0.5 -> 8 (7.9375), 4 -> 64 (63.5, tie to even), 8 -> 127,
+    -8 -> -127, 1 -> 16."""
+    xq, a = oracle.act_quant_per_tensor(_bits([[1.0, -2.0, 0.5, 0.0], [4.0, 8.0, -8.0, 1.0]]))
+    assert a.tolist() == [15.875, 15.875]
+    assert xq.tolist() == [[16, -32, 8, 0], [64, 127, -127, 16]]
+
+
+def test_act_quant_per_tensor_reduces_to_per_token_for_one_row():
+    X = workloads.activations(1, 777 * 4, seed=3)
+    b = workloads.bf16_bits(X)
+    xq1, a1 = oracle.act_quant(b)
+    xq2, a2 = oracle.act_quant_per_tensor(b)
+    assert np.array_equal(xq1, xq2) and np.array_equal(a1, a2)
+
+
+def test_act_quant_per_tensor_invariants():
+    X = workloads.activations(6, 256, seed=9)
+    b = workloads.bf16_bits(X)
+    xq, a = oracle.act_quant_per_tensor(b)
+    assert np.all(a == a[0])
+    amax = np.max(np.abs(X.to(torch.bfloat16).to(torch.float32).numpy()))
+    assert a[0] == np.float32(127.0) / np.float32(amax)
+    perm = np.array([3, 0, 5, 1, 4, 2])
+    xq_p, a_p = oracle.act_quant_per_tensor(b[perm])
+    assert np.array_equal(xq_p, xq[perm]) and np.array_equal(a_p, a)
+    # the row holding the tensor's max is coded exactly as by the per-token quantizer
+    r = int(np.argmax(np.max(np.abs(X.to(torch.bfloat16).to(torch.float32).numpy()), axis=1)))
+    xq_r, _ = oracle.act_quant(b[r:r + 1])
+    assert np.array_equal(xq[r:r + 1], xq_r)
+
+
+# ------------------------------------------------------------- code tables
+
+
+def test_repack_page_table_example():
+    """Weights (+1, 0, -1, +1): with code = w + 1 the byte is 10 00 01 10 (high to low
+    field order 3..0) = 0x86; with the page's table (11 +1, 00 0, 01 -1) it is
+    11 01 00 11 = 0xD3."""
+    out, bad = oracle.repack(np.array([[0x86]], np.uint8), 4, oracle.CODES_OFFSET, oracle.CODES_SIGN)
+    assert bad == 0 and out.tolist() == [[0xD3]]
+    back, bad = oracle.repack(out, 4, oracle.CODES_SIGN, oracle.CODES_OFFSET)
+    assert bad == 0 and back.tolist() == [[0x86]]
+
+
+def test_repack_unused_codes_and_roundtrip():
+    out, bad = oracle.repack(np.array([[0xFF, 0x55]], np.uint8), 8, oracle.CODES_OFFSET, oracle.CODES_SIGN)
+    assert bad == 4 and out.tolist() == [[0x00, 0x00]]   # 11 unused -> weight 0; 01 = 0 -> 00
+    out, bad = oracle.repack(np.array([[0xAA, 0x44]], np.uint8), 8, oracle.CODES_SIGN, oracle.CODES_OFFSET)
+    # 10 unused -> 0 (offset code 01); 0x44 holds fields (00, 01, 00, 01) = (0, -1, 0, -1)
+    # -> offset codes (01, 00, 01, 00) = 0x11
+    assert bad == 4 and out.tolist() == [[0x55, 0x11]]
+    p, _ = oracle.pack_weights(workloads.latent_weights(5, 64, seed=2).numpy())
+    q, bad1 = oracle.repack(p, 64, oracle.CODES_OFFSET, oracle.CODES_SIGN)
+    r, bad2 = oracle.repack(q, 64, oracle.CODES_SIGN, oracle.CODES_OFFSET)
+    assert bad1 == 0 and bad2 == 0 and np.array_equal(r, p)
+    assert not np.array_equal(q, p)
