@@ -31,7 +31,8 @@ one launch per projection is reported beside it (value_ungrouped).
 * extras: the same per-launch rooflines at large shapes, where the bandwidth and
   matrix-core bars are reachable: the 70B-shaped decode layer set (M = 1) and the
   8B-shaped prefill MLP GEMMs (M = 2048); the 2B decode MLP as two launches (gate|up
-  with the SwiGLU epilogue, then down); and ceilings measured on this chip: an int8
+  with the SwiGLU epilogue, then down); the 2B decode set with bf16 activations and no
+  activation quantization (W1.58A16); and ceilings measured on this chip: an int8
   matrix-core loop on register operands, a 2 GiB streaming read, and the vendor int8
   GEMM (hipBLASLt, dense int8 weights) at the prefill shapes.
 """
@@ -405,6 +406,24 @@ def bench_extras(bw, workloads, torch, dev, reps):
                                "packed_bytes": nbytes}
     del copies, mats
     torch.cuda.empty_cache()
+
+    # bf16 activations times ternary weights (no activation quantization), 2B set at M = 1
+    print("[bench] 2B decode set with bf16 activations, M=1", file=sys.stderr, flush=True)
+    per, tot_b, tot_us = {}, 0, 0.0
+    for name, N, K in workloads.LAYER_2B:
+        p, sc = bw.pack_weights(workloads.latent_weights(N, K, seed=0).to(dev))
+        R = max(2, math.ceil(ROTATE_BYTES / (N * K // 4)))
+        copies = [p] + [p.clone() for _ in range(R - 1)]
+        x = workloads.activations(1, K, seed=0, outliers=True).to(dev)
+        o = torch.empty((1, N), dtype=torch.float32, device=dev)
+        us = graph_launch_us(torch, lambda r: bw.a16_gemv(x, copies[r], sc, "f32", out=o), R, reps)
+        per[name] = round(us, 3)
+        tot_b += N * K // 4
+        tot_us += us
+        del copies, p
+    torch.cuda.empty_cache()
+    out["a16_decode_2b_m1"] = {"achieved_GB/s": round(tot_b / tot_us / 1e3, 1),
+                               "per_shape_us": per}
 
     # what this chip sustains (context for the fractions above)
     from ternary_weight_linear_token_amd import ceilings

@@ -232,6 +232,23 @@ int bitnet_quant_gemv_swiglu(const uint16_t* x, const uint8_t* packed_gate,
                              const float* w_scale_up, int64_t M, int64_t N, int64_t K, void* h,
                              int out_dtype, int8_t* xq_out, float* a_scale_out, void* stream);
 
+/*
+ * bitnet_a16_gemv -- the ternary weights times bf16 activations with no activation
+ * quantization (W1.58A16): "将 BitNet 三元查找表集成到自定义 Triton 内核中" serves ternary
+ * weights with 16-bit activations and an fp32 accumulator; "BitNet 深度实战" §2.2: the
+ * product needs only additions and subtractions.
+ *   out[m,n] = w_scale[n] * sum_k x[m,k] * w[n,k]
+ *   x               : bf16 (M, K) as uint16, 1 <= M <= BITNET_GEMV_MAX_M.
+ *   packed, w_scale : as produced by bitnet_pack_weights; K % 64 == 0 (else
+ *                     BITNET_ERR_UNALIGNED).
+ *   out             : (M, N), BITNET_OUT_F32 or BITNET_OUT_BF16 (RNE of the fp32 value);
+ *                     BITNET_OUT_I32 is rejected.
+ * Each product x * w is exact; the sum is accumulated in fp32 (any order), so
+ * |out - exact| <= (K + 2) * 2^-24 * w_scale[n] * sum_k |x[m,k] * w[n,k]|.
+ */
+int bitnet_a16_gemv(const uint16_t* x, const uint8_t* packed, const float* w_scale, int64_t M,
+                    int64_t N, int64_t K, void* out, int out_dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

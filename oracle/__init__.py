@@ -20,6 +20,8 @@ Functions and the pages they follow (page titles abbreviated):
   accumulate    -- "BitNet 深度实战" §4.4: int8 x ternary into int32.
   rescale       -- "BitNet 深度实战" §2.4 / §3.2: out = acc * w_scale / a_scale.
   swiglu        -- "BitNet 深度实战" §3.2: the MLP's silu(gate(x)) * up(x).
+  a16           -- "将 BitNet 三元查找表集成到自定义 Triton 内核中" / "BitNet 深度实战" §2.2:
+                   16-bit activations times ternary weights, no activation quantization.
 
 Every function is pinned by tests/test_oracle_pins.py (worked example, closed forms,
 invariants, library matmul on unpacked codes, brute force on tiny inputs).
@@ -84,6 +86,7 @@ def _load():
             "oracle_f64_to_bf16": [p, i64, p],
             "oracle_swiglu": [p, p, i64, p],
             "oracle_act_quant_per_tensor": [p, i64, i64, p, p],
+            "oracle_a16": [p, p, p, i64, i64, i64, p, p],
         }
         for name, args in sig.items():
             fn = getattr(lib, name)
@@ -262,6 +265,23 @@ def rescale_sampled(acc, a_scale, w_scale, ms, ns):
                                           _ptr(ns), ms.size, _ptr(ref), _ptr(f32), _ptr(bf)),
            "rescale_sampled")
     return ref, f32, bf
+
+
+def a16(x_bf16_bits: np.ndarray, packed: np.ndarray, w_scale: np.ndarray, K: int):
+    """O6: bf16 activations times the packed ternary weights, no activation quantization
+    ("将 BitNet 三元查找表集成到自定义 Triton 内核中", mixed-precision serving; "BitNet 深度实战"
+    §2.2).  Returns (ref fp64 (M, N) = w_scale[n] * sum_k x w, sumabs fp64 (M, N) =
+    w_scale[n] * sum_k |x w|)."""
+    x = np.ascontiguousarray(x_bf16_bits, dtype=np.uint16)
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    w_scale = np.ascontiguousarray(w_scale, dtype=np.float32)
+    M = x.shape[0]
+    N = packed.shape[0]
+    ref = np.empty((M, N), np.float64)
+    sa = np.empty((M, N), np.float64)
+    _check(_load().oracle_a16(_ptr(x), _ptr(packed), _ptr(w_scale), M, N, K, _ptr(ref), _ptr(sa)),
+           "a16")
+    return ref, sa
 
 
 def swiglu(g: np.ndarray, u: np.ndarray) -> np.ndarray:

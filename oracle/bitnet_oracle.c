@@ -326,6 +326,38 @@ int64_t oracle_repack(const uint8_t* in, int64_t N, int64_t K, int from, int to,
     return bad;
 }
 
+/* -------------------------------------- O6: bf16 activations x ternary (W1.58A16) --- */
+
+/*
+ * [LUT] (introduction and its precision settings): mixed-precision serving multiplies
+ * ternary weights with 16-bit activations and accumulates in fp32; [Deep] §2.2: with
+ * W in {-1, 0, +1}, Y = X @ W needs only additions and subtractions.  No activation
+ * quantization: out[m,n] = w_scale[n] * sum_k x[m,k] * w[n,k], w from the packed codes.
+ * Evaluated in fp64 (every product x * w is exact); sumabs[m,n] = w_scale[n] *
+ * sum_k |x[m,k] * w[n,k]| is returned for the error bound of a float32 sum.
+ */
+int oracle_a16(const uint16_t* x, const uint8_t* packed, const float* w_scale, int64_t M,
+               int64_t N, int64_t K, double* ref, double* sumabs) {
+    if (!x || !packed || !w_scale || !ref || !sumabs || M < 0 || N < 0 || K < 4 || K % 4)
+        return -1;
+    const int64_t KB = K / 4;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static)
+#endif
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t m = 0; m < M; ++m) {
+            double s = 0.0, sa = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const double t = (double)bf16_to_f32(x[m * K + k]) * weight_at(packed, KB, n, k);
+                s += t;
+                sa += fabs(t);
+            }
+            ref[m * N + n] = s * (double)w_scale[n];
+            sumabs[m * N + n] = sa * (double)w_scale[n];
+        }
+    return 0;
+}
+
 /* ------------------------------------------------------- O5: SwiGLU of the MLP --- */
 
 /*

@@ -17,6 +17,7 @@ from ._binding import (  # noqa: F401
     OUT_I32,
     SKINNY_MAX_M,
     BitnetError,
+    a16_gemv,
     abi_version,
     bitlinear,
     gemm,

@@ -65,6 +65,7 @@ def lib():
             "bitnet_quant_gemv_grouped": ([p, i64, i64, i64, p, p, p, p, i32, p, p, p], i32),
             "bitnet_quant_gemv_swiglu": ([p, p, p, p, p, i64, i64, i64, p, i32, p, p, p], i32),
             "bitnet_quant_act_per_tensor": ([p, i64, i64, p, p, p], i32),
+            "bitnet_a16_gemv": ([p, p, p, i64, i64, i64, p, i32, p], i32),
             "bitnet_repack_codes": ([p, i64, i64, i32, i32, p, p, p], i32),
         }
         for name, (args, res) in sigs.items():
@@ -342,6 +343,23 @@ def quant_gemv_swiglu(x, packed_gate, w_scale_gate, packed_up, w_scale_up, out_d
         _opt_ptr(a_scale, torch.float32, "a_scale_out", (M,)), _stream(x)),
         "bitnet_quant_gemv_swiglu")
     return (out, xq, a_scale) if return_quant else out
+
+
+def a16_gemv(x, packed, w_scale, out_dtype="f32", out=None):
+    """bf16 activations (M <= 16) times the packed ternary weights, no activation
+    quantization, fp32 accumulation."""
+    M, K = x.shape
+    N = packed.shape[0]
+    code = _out_code(out_dtype)
+    if code == OUT_I32:
+        raise ValueError("the bf16-activation product is fp32 or bf16")
+    out = _alloc_out(out, M, N, code, x.device)
+    _check(lib().bitnet_a16_gemv(_tensor(x, torch.bfloat16, "x", (M, K)),
+                                 _tensor(packed, torch.uint8, "packed", (N, K // 4)),
+                                 _tensor(w_scale, torch.float32, "w_scale", (N,)), M, N, K,
+                                 _tensor(out, _OUT_TORCH[code], "out", (M, N)), code, _stream(x)),
+           "bitnet_a16_gemv")
+    return out
 
 
 FUSED_MAX_M = 4  # above this, one quantization launch beats requantizing in every block

@@ -236,6 +236,22 @@ int bitnet_repack_codes(const uint8_t* in, int64_t N, int64_t K, int from_table,
                                                   invalid_count, as_stream(stream)));
 }
 
+int bitnet_a16_gemv(const uint16_t* x, const uint8_t* packed, const float* w_scale, int64_t M,
+                    int64_t N, int64_t K, void* out, int out_dtype, void* stream) {
+    if (out_dtype != BITNET_OUT_F32 && out_dtype != BITNET_OUT_BF16) return BITNET_ERR_INVALID_ARG;
+    int st = check_shape(M, N, K);
+    if (st) return st;
+    if (K % 64 != 0) return BITNET_ERR_UNALIGNED;
+    if (M > BITNET_GEMV_MAX_M) return BITNET_ERR_INVALID_ARG;
+    if (M == 0 || N == 0) return BITNET_OK;
+    if (!x || !packed || !w_scale || !out) return BITNET_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(packed) || !aligned16(w_scale) || !aligned16(out))
+        return BITNET_ERR_UNALIGNED;
+    if ((st = check_device())) return st;
+    return record_hip(bitnet::launch_a16(x, packed, w_scale, M, N, K, out, out_dtype,
+                                         as_stream(stream)));
+}
+
 int bitnet_quant_gemv_swiglu(const uint16_t* x, const uint8_t* packed_gate,
                              const float* w_scale_gate, const uint8_t* packed_up,
                              const float* w_scale_up, int64_t M, int64_t N, int64_t K, void* h,

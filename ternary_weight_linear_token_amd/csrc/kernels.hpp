@@ -46,6 +46,11 @@ hipError_t launch_skinny_swiglu(const uint16_t* x_bf16, const uint8_t* packed_ga
                                 void* out, int out_dtype, int8_t* xq_out, float* a_out,
                                 hipStream_t stream);
 
+// bf16 activations times ternary weights (no activation quantization), fp32 accumulation,
+// 1 <= M <= 16, K % 64 == 0; out fp32 (0) or bf16 (1).
+hipError_t launch_a16(const uint16_t* x, const uint8_t* packed, const float* w_scale, int64_t M,
+                      int64_t N, int64_t K, void* out, int out_dtype, hipStream_t stream);
+
 // Tiled int8 matrix-core product for any M.  `workspace` must hold
 // tiled_workspace_size(M, N, K) bytes whose counter area is zero (it is left zero).
 size_t tiled_workspace_size(int64_t M, int64_t N, int64_t K);

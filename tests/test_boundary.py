@@ -185,6 +185,16 @@ def test_per_tensor_and_repack_validation(L):
     assert g(A, 0, 256, 0, 1, B, None, None) == OK
 
 
+def test_a16_validation(L):
+    f = L.bitnet_a16_gemv
+    assert f(A, B, C, 1, 16, 256, D, 2, None) == INVALID     # int32 output
+    assert f(None, B, C, 1, 16, 256, D, 0, None) == INVALID
+    assert f(A, B, C, 17, 16, 256, D, 0, None) == INVALID    # M above 16
+    assert f(A, B, C, 1, 16, 260, D, 0, None) == UNALIGNED   # K % 64
+    assert f(A, B + 4, C, 1, 16, 256, D, 1, None) == UNALIGNED
+    assert f(A, B, C, 0, 16, 256, D, 0, None) == OK
+
+
 def test_valid_call_without_gpu_reports_hip_error(L):
     # Arguments pass validation, so the library asks HIP for the device; with no GPU in
     # this container that fails and comes back as BITNET_ERR_HIP with the HIP message.

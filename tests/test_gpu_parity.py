@@ -252,6 +252,37 @@ def test_quant_gemv_swiglu_matches_oracle(M, N, K):
     assert d.max(initial=0) <= 1, f"swiglu bf16 M={M} N={N} K={K}: off by {d.max()} ulp"
 
 
+@pytest.mark.parametrize("M", [1, 2, 16])
+@pytest.mark.parametrize("N,K", [(16, 64), (300, 1024), (37, 320), (129, 2560), (640, 6912),
+                                 (20, 28672)])
+def test_a16_gemv_matches_oracle(M, N, K):
+    """bf16 activations times ternary weights: each product is exact, the fp32 sum of K
+    terms is within (K + 2) 2^-24 sum|x w| of the exact sum (any order), times w_scale."""
+    pb = Problem(M, N, K, seed=M * 17000 + N + K)
+    o = pb.oracle(full=False)
+    ref, sumabs = oracle.a16(pb.xbits, o["packed"], o["w_scale"], K)
+    lim = (K + 2) * 2.0 ** -24 * sumabs
+    packed, s = dev(o["packed"]), dev(o["w_scale"])
+    out = to_np(bw.a16_gemv(pb.x_dev, packed, s, "f32")).astype(np.float64)
+    bad = np.flatnonzero((np.abs(out - ref) > lim).reshape(-1))
+    assert bad.size == 0, f"a16 M={M} N={N} K={K}: {bad.size} outputs beyond the bound"
+    # the measured error sits far inside the worst-case bound
+    assert np.max(np.abs(out - ref) / np.maximum(sumabs, 1e-30)) < 64 * 2.0 ** -24 * np.sqrt(K)
+    outb = to_np(bw.a16_gemv(pb.x_dev, packed, s, "bf16"))
+    fb = outb.astype(np.uint32) << 16
+    vb = fb.view(np.float32).astype(np.float64)
+    # bf16 adds one rounding of the fp32 value v: half an ulp, <= 2^-9 |v| <= 2^-9 (|ref| + lim)
+    assert np.all(np.abs(vb - ref) <= (1 + 2.0 ** -8) * lim + 2.0 ** -8 * np.abs(ref)), \
+        f"a16 bf16 M={M} N={N} K={K}"
+    # integer-valued activations make every partial sum exact: then it is the int8 result
+    xi = torch.randint(-127, 128, (M, K), generator=torch.Generator().manual_seed(K))
+    xq = xi.to(torch.int8)
+    acc = oracle.accumulate(xq.numpy(), o["packed"], K)
+    exact, _, _ = oracle.rescale(acc, np.ones(M, np.float32), o["w_scale"])
+    outi = to_np(bw.a16_gemv(xi.to(torch.bfloat16).cuda(), packed, s, "f32")).astype(np.float64)
+    assert np.all(np.abs(outi - exact) <= 2.0 ** -24 * np.abs(exact)), f"a16 integer M={M} N={N} K={K}"
+
+
 def test_extreme_accumulators():
     # every activation at +-127 and every weight +1 / -1: |acc| = 127 K, the largest sums
     M, N, K = 3, 40, 28672

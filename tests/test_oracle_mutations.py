@@ -48,6 +48,10 @@ MUTATIONS = {
                                     "return w == 1 ? 3u : (w == -1 ? 2u : 0u);"),
     "repack_field_order": ("byte |= table_code(to, w) << (2 * i);",
                            "byte |= table_code(to, w) << (2 * (3 - i));"),
+    "a16_drops_weight_scale": ("ref[m * N + n] = s * (double)w_scale[n];",
+                               "ref[m * N + n] = s;"),
+    "a16_weight_index": ("const double t = (double)bf16_to_f32(x[m * K + k]) * weight_at(packed, KB, n, k);",
+                         "const double t = (double)bf16_to_f32(x[m * K + k]) * weight_at(packed, KB, n, K - 1 - k);"),
     "swiglu_sign_of_exp": ("h[t] = g[t] / (1.0 + exp(-g[t])) * u[t];",
                            "h[t] = g[t] / (1.0 + exp(g[t])) * u[t];"),
     "swiglu_sigmoid_only": ("h[t] = g[t] / (1.0 + exp(-g[t])) * u[t];",

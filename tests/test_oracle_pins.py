@@ -407,3 +407,39 @@ def test_repack_unused_codes_and_roundtrip():
     r, bad2 = oracle.repack(q, 64, oracle.CODES_SIGN, oracle.CODES_OFFSET)
     assert bad1 == 0 and bad2 == 0 and np.array_equal(r, p)
     assert not np.array_equal(q, p)
+
+
+# ------------------------------------------------- O6 bf16 activations (W1.58A16)
+
+
+def test_a16_hand_example():
+    """x = (1, 2, 3, 4), w = (+1, 0, -1, +1), w_scale = 0.5: 0.5 * (1 - 3 + 4) = 1."""
+    q = np.array([[1, 0, -1, 1]], np.int8)
+    ref, sa = oracle.a16(_bits([[1.0, 2.0, 3.0, 4.0]]), oracle.pack(q), np.array([0.5], np.float32), 4)
+    assert ref.tolist() == [[1.0]] and sa.tolist() == [[4.0]]
+
+
+def test_a16_reduces_to_int8_path_for_integer_activations():
+    """Integer activations |x| <= 127 are their own int8 codes: the product is then
+    w_scale * acc from the pinned int8 accumulation (O3) with a unit activation scale."""
+    rng = np.random.default_rng(12)
+    M, N, K = 3, 17, 260
+    xi = rng.integers(-127, 128, size=(M, K))
+    p, s = oracle.pack_weights(workloads.latent_weights(N, K, seed=4).numpy())
+    ref, sa = oracle.a16(_bits(xi.astype(np.float32).tolist()), p, s, K)
+    acc = oracle.accumulate(xi.astype(np.int8), p, K)
+    r2, _, _ = oracle.rescale(acc, np.ones(M, np.float32), s)
+    assert np.array_equal(ref, r2)
+    assert np.all(sa >= np.abs(ref))
+
+
+def test_a16_linearity_and_zero_weights():
+    X = workloads.activations(2, 64, seed=8).to(torch.bfloat16)
+    p, s = oracle.pack_weights(workloads.latent_weights(5, 64, seed=1).numpy())
+    r1, _ = oracle.a16(workloads.bf16_bits(X), p, s, 64)
+    r2, _ = oracle.a16(workloads.bf16_bits(-X), p, s, 64)          # exact negation
+    r4, _ = oracle.a16(workloads.bf16_bits(4 * X), p, s, 64)       # exact power-of-two scale
+    assert np.array_equal(r2, -r1) and np.array_equal(r4, 4 * r1)
+    zero = oracle.pack(np.zeros((5, 64), np.int8))
+    rz, sz = oracle.a16(workloads.bf16_bits(X), zero, s, 64)
+    assert not rz.any() and not sz.any()
