@@ -34,6 +34,12 @@ FLAGS = [
 ]
 
 
+def _flags_key() -> bytes:
+    """The compile flags as they affect the code: include directories are dropped, so the
+    key (and every hash below) is the same wherever the repository is checked out."""
+    return " ".join(f for f in FLAGS if not os.path.isabs(f)).encode()
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
                   if f.endswith((".hip", ".hpp")))
@@ -45,7 +51,7 @@ def source_hash() -> str:
         h.update(os.path.basename(path).encode())
         with open(path, "rb") as f:
             h.update(f.read())
-    h.update(" ".join(FLAGS).encode())
+    h.update(_flags_key())
     return h.hexdigest()
 
 
@@ -57,7 +63,7 @@ def kernel_hash(*names: str) -> str:
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())
-    h.update(" ".join(FLAGS).encode())
+    h.update(_flags_key())
     return h.hexdigest()
 
 
