@@ -92,8 +92,8 @@ def load_traffic(kernel_hash: str):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path has no "
-              "multi-GPU mode in this build.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the library has no "
+              "multi-GPU mode.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -95,8 +95,8 @@ int oracle_weight_quant(const float* W, int64_t N, int64_t K, int8_t* q, float* 
  * [Deep] §4.3 (位打包): the first of the four weights occupies bits 0-1, the second bits
  * 2-3, the third bits 4-5, the fourth bits 6-7.
  * Code values: code = w + 1 (w = -1 -> 0b00, 0 -> 0b01, +1 -> 0b10; 0b11 unused).  The
- * page uses a different code table (11 -> +1, 00 -> 0, 01 -> -1); this build stores
- * w + 1 so that the code is an unsigned digit and w = code - 1.
+ * page uses a different code table (11 -> +1, 00 -> 0, 01 -> -1); the library stores
+ * w + 1 so that the code is an unsigned digit and w = code - 1 (oracle_repack converts).
  * K must be a multiple of 4.
  */
 int oracle_pack(const int8_t* q, int64_t N, int64_t K, uint8_t* packed) {
