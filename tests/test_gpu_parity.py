@@ -420,6 +420,52 @@ def test_graph_replay_matches_eager():
     check_out(to_np(out2), o2["acc"], o2["ref"], "bf16", "graph replay gemm")
 
 
+def test_graph_replay_of_grouped_swiglu_and_a16_launches():
+    # The same for the decode-step launches the benchmark captures: grouped q|k|v, the
+    # SwiGLU pair, the bf16-activation product and the per-tensor quantization.
+    X = workloads.activations(1, 1024, seed=21)
+    pbs = [Problem(1, n, 1024, seed=30 + i, X=X) for i, n in enumerate((300, 64, 64))]
+    os_ = [pb.oracle() for pb in pbs]
+    pk = [dev(o["packed"]) for o in os_]
+    sc = [dev(o["w_scale"]) for o in os_]
+    x = pbs[0].x_dev
+    outs = [torch.empty((1, pb.N), dtype=torch.float32, device="cuda") for pb in pbs]
+    h = torch.empty((1, 64), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((1, 300), dtype=torch.float32, device="cuda")
+    xq = torch.empty((1, 1024), dtype=torch.int8, device="cuda")
+    a = torch.empty((1,), dtype=torch.float32, device="cuda")
+    bufs = outs + [h, y, xq, a]
+
+    def work():
+        bw.quant_gemv_grouped(x, pk, sc, "f32", out=outs)
+        bw.quant_gemv_swiglu(x, pk[1], sc[1], pk[2], sc[2], "bf16", out=h)
+        bw.a16_gemv(x, pk[0], sc[0], "f32", out=y)
+        bw.quant_act_per_tensor(x, xq=xq, a_scale=a)
+
+    work()
+    torch.cuda.synchronize()
+    eager = [b.clone() for b in bufs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        work()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        work()
+    for rep in range(4):
+        for b in bufs:
+            b.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for b, e in zip(bufs, eager):
+            assert torch.equal(b.view(torch.uint8), e.view(torch.uint8)), rep
+        bw.quant_gemv(x, pk[0], sc[0], "f32")  # unrelated eager work
+    for o, out, pb in zip(os_, outs, pbs):
+        check_out(to_np(out), o["acc"], o["ref"], "f32", f"graph replay grouped N={pb.N}")
+
+
 def test_gemm_small_and_large_tile_grids_with_caller_workspace():
     # Shapes that select each tile configuration (64x128 with four k-groups, 128x128 with
     # two, 256x128, 256x256), including grids far smaller than the CU count and ragged
