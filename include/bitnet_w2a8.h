@@ -70,7 +70,7 @@ typedef enum {
 } bitnet_out_dtype;
 
 typedef enum {
-    BITNET_ALGO_AUTO = 0,   /* SKINNY while M*N is small (M <= 32), else TILED        */
+    BITNET_ALGO_AUTO = 0,   /* weight-streaming kernels for small products, else TILED */
     BITNET_ALGO_SKINNY = 1, /* weight-streaming kernel, M <= BITNET_SKINNY_MAX_M      */
     BITNET_ALGO_TILED = 2   /* tiled int8 matrix-core kernel, any M                    */
 } bitnet_algo;

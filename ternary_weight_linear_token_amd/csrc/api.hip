@@ -59,6 +59,21 @@ bool valid_dtype(int dt) {
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+// int8 product for M <= 16: the kernel that stages the activations in LDS for one to
+// three tokens (and for four to seven with large N), the one that reads them straight
+// into the matrix-core operands above (K % 64 == 0).  Measured crossover; both give
+// identical outputs.
+hipError_t launch_small_m(const int8_t* xq, const float* a_scale, const uint8_t* packed,
+                          const float* w_scale, int64_t M, int64_t N, int64_t K, void* out,
+                          int out_dtype, hipStream_t stream) {
+    const bool direct = K % 64 == 0 && (M >= 8 || (M >= 4 && N <= 4096));
+    if (direct)
+        return bitnet::launch_gemv_direct(xq, a_scale, packed, w_scale, M, N, K, out, out_dtype,
+                                          stream);
+    return bitnet::launch_skinny(xq, a_scale, nullptr, packed, w_scale, M, N, K, out, out_dtype,
+                                 nullptr, nullptr, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -125,8 +140,8 @@ int bitnet_w2a8_gemv(const int8_t* xq, const float* a_scale, const uint8_t* pack
         !aligned16(out))
         return BITNET_ERR_UNALIGNED;
     if ((st = check_device())) return st;
-    return record_hip(bitnet::launch_skinny(xq, a_scale, nullptr, packed, w_scale, M, N, K, out,
-                                            out_dtype, nullptr, nullptr, as_stream(stream)));
+    return record_hip(launch_small_m(xq, a_scale, packed, w_scale, M, N, K, out, out_dtype,
+                                     as_stream(stream)));
 }
 
 size_t bitnet_w2a8_gemm_workspace_size(int64_t M, int64_t N, int64_t K) {
@@ -151,15 +166,23 @@ int bitnet_w2a8_gemm(const int8_t* xq, const float* a_scale, const uint8_t* pack
         !aligned16(out) || !aligned16(workspace))
         return BITNET_ERR_UNALIGNED;
     if ((st = check_device())) return st;
-    // Auto: the weight-streaming kernel while M * N is small (each of its 16-row blocks
-    // stages all M x K activations, so its cost grows with M * N); otherwise the tiled
-    // kernel, whose single-round grids cost about the same for any M up to 64.
-    const bool skinny_auto = (M <= 16 && M * N <= 196608) || (M <= 32 && M * N <= 131072);
-    const bool skinny = algo == BITNET_ALGO_SKINNY || (algo == BITNET_ALGO_AUTO && skinny_auto);
-    if (skinny)
+    // Auto: the weight-streaming kernels while the product is small enough that one
+    // round of their blocks beats the tiled kernel (whose single-round grids cost about
+    // the same for any M up to 64): always up to 4 tokens, up to 16 while the weights
+    // are at most 16 MB, and the staged kernel's token tiles up to 32 while M * N is small.
+    if (algo == BITNET_ALGO_SKINNY)
         return record_hip(bitnet::launch_skinny(xq, a_scale, nullptr, packed, w_scale, M, N, K,
                                                 out, out_dtype, nullptr, nullptr,
                                                 as_stream(stream)));
+    if (algo == BITNET_ALGO_AUTO) {
+        if (M <= 4 || (M <= 16 && N * K <= ((int64_t)1 << 26)))
+            return record_hip(launch_small_m(xq, a_scale, packed, w_scale, M, N, K, out,
+                                             out_dtype, as_stream(stream)));
+        if (M <= 32 && M * N <= 131072)
+            return record_hip(bitnet::launch_skinny(xq, a_scale, nullptr, packed, w_scale, M, N,
+                                                    K, out, out_dtype, nullptr, nullptr,
+                                                    as_stream(stream)));
+    }
     return record_hip(bitnet::launch_tiled(xq, a_scale, packed, w_scale, M, N, K, out, out_dtype,
                                            workspace, as_stream(stream)));
 }

@@ -159,6 +159,21 @@ def test_gemv_matches_oracle(M, N, K):
         check_out(to_np(out), o["acc"], o["ref"], dt, f"gemv M={M} N={N} K={K} {dt}")
 
 
+@pytest.mark.parametrize("M", [4, 8, 13, 16])
+@pytest.mark.parametrize("N,K", [(300, 1024), (4097, 512), (50, 14336), (17, 64)])
+def test_direct_and_staged_small_m_kernels_agree(M, N, K):
+    """For a few tokens the int8 product reads the activations straight into the matrix
+    cores (bitnet_w2a8_gemv routes there); the staged kernel (ALGO_SKINNY) must give the
+    same bits, and both the oracle's result."""
+    pb = Problem(M, N, K, seed=M * 19000 + N + K)
+    xq, a, packed, s, o = product_inputs(pb)
+    for dt in DT:
+        direct = bw.gemv(xq, a, packed, s, dt)
+        staged = bw.gemm(xq, a, packed, s, dt, algo="skinny")
+        check_out(to_np(direct), o["acc"], o["ref"], dt, f"direct M={M} N={N} K={K} {dt}")
+        assert np.array_equal(to_np(direct), to_np(staged)), f"direct != staged M={M} N={N} K={K} {dt}"
+
+
 @pytest.mark.parametrize("algo", ["tiled", "auto"])
 @pytest.mark.parametrize("M", [1, 16, 17, 130, 300])
 @pytest.mark.parametrize("N,K", [(64, 64), (200, 256), (130, 1000), (257, 320), (96, 2560)])
