@@ -68,8 +68,8 @@ hipError_t launch_small_m(const int8_t* xq, const float* a_scale, const uint8_t*
                           int out_dtype, hipStream_t stream) {
     const bool direct = K % 64 == 0 && (M >= 8 || (M >= 4 && N <= 4096));
     if (direct)
-        return bitnet::launch_gemv_direct(xq, a_scale, packed, w_scale, M, N, K, out, out_dtype,
-                                          stream);
+        return bitnet::launch_gemv_direct(xq, a_scale, nullptr, packed, w_scale, M, N, K, out,
+                                          out_dtype, nullptr, nullptr, stream);
     return bitnet::launch_skinny(xq, a_scale, nullptr, packed, w_scale, M, N, K, out, out_dtype,
                                  nullptr, nullptr, stream);
 }
@@ -200,6 +200,12 @@ int bitnet_quant_gemv(const uint16_t* x, const uint8_t* packed, const float* w_s
         !aligned16(xq_out) || !aligned16(a_scale_out))
         return BITNET_ERR_UNALIGNED;
     if ((st = check_device())) return st;
+    // 12 to 16 tokens: the kernel that quantizes in registers (its whole-row max scan is
+    // cheaper there than the staged kernel's LDS copy); fewer: the staged kernel
+    if (M >= 12 && K % 64 == 0)
+        return record_hip(bitnet::launch_gemv_direct(nullptr, nullptr, x, packed, w_scale, M, N,
+                                                     K, out, out_dtype, xq_out, a_scale_out,
+                                                     as_stream(stream)));
     return record_hip(bitnet::launch_skinny(nullptr, nullptr, x, packed, w_scale, M, N, K, out,
                                             out_dtype, xq_out, a_scale_out, as_stream(stream)));
 }

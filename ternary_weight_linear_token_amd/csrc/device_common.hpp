@@ -85,4 +85,56 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, int dtype, int
     }
 }
 
+// Quantize 16 bf16 values (h: 8 words, 2 values each, low half first) with scale a into
+// 16 int8 codes, packed transposed for the operand layout: byte b of e[i] is the code of
+// element 4 b + i.  The code is rint(fl(x * a)) with ties to even: adding 1.5 * 2^23 to
+// fl(x * a) (|x * a| < 2^22) rounds it to an integer in one fp32 addition, and the low
+// byte of the sum's bit pattern is that integer in two's complement.  The clamp to
+// +-127 of the definition never binds here: a = fl(127 / amax) and |x| <= amax give
+// |fl(x * a)| <= 127 (1 + 2^-23) < 127.5.
+__device__ __forceinline__ void quant16_t(const uint32_t h[8], float a, uint32_t e[4]) {
+    constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
+    uint32_t v[16];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        v[2 * j] = __float_as_uint(bf16_bits_to_f32(h[j]) * a + kMagic);
+        v[2 * j + 1] = __float_as_uint(__uint_as_float(h[j] & 0xFFFF0000u) * a + kMagic);
+    }
+    // low bytes of elements i, 4+i (bytes 0, 1) and 8+i, 12+i (bytes 2, 3); selector 0x0c
+    // gives a zero byte
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        e[i] = __builtin_amdgcn_perm(v[4 + i], v[i], 0x0c0c0400u) |
+               __builtin_amdgcn_perm(v[12 + i], v[8 + i], 0x04000c0cu);
+}
+
+// max |x| of 16 bf16 values as bf16 bits (a monotone key for non-negative values),
+// two lanes at a time with the packed 16-bit integer max.
+__device__ __forceinline__ uint32_t absmax_bits16(const uint32_t h[8]) {
+    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+    u16x2 m = __builtin_bit_cast(u16x2, h[0] & 0x7FFF7FFFu);
+#pragma unroll
+    for (int j = 1; j < 8; ++j)
+        m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, h[j] & 0x7FFF7FFFu));
+    return max((uint32_t)m.x, (uint32_t)m.y);
+}
+
+// Element-order codes of a transposed group (for the optional copy of the codes).
+__device__ __forceinline__ void untranspose(const uint32_t e[4], uint32_t d[4]) {
+    transpose4x4_bytes(e, d);  // the 4x4 byte transpose is its own inverse
+}
+
+template <bool FAST>
+__device__ __forceinline__ void store_codes16(int8_t* xq_out, int K, int m, int k0,
+                                              const uint32_t d[4]) {
+    int8_t* dst = xq_out + (int64_t)m * K + k0;
+    if (FAST) {
+        if (k0 < K) *reinterpret_cast<uint4*>(dst) = make_uint4(d[0], d[1], d[2], d[3]);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+            if (k0 + j < K) dst[j] = (int8_t)(d[j >> 2] >> (8 * (j & 3)));
+    }
+}
+
 }  // namespace bitnet

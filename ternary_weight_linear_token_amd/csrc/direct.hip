@@ -19,6 +19,11 @@
 //    is requested before the current one is multiplied; chunks past the end read zeros
 //    through out-of-range buffer offsets.
 //  * int32 partials of the four waves are added through LDS, then rescaled.
+//  * Fused variant (bf16 activations): the block first finds every token's max |x| (all
+//    threads scan the M rows, wave reductions, one barrier), then each lane quantizes
+//    its 16 activations per operand in registers (fp32 multiply, round half to even by
+//    the 1.5 * 2^23 addition), already in the transposed order.  The first block also
+//    writes the codes and scales when asked.
 //  * K must be a multiple of 64 (16-byte aligned rows); other K use the staged kernel.
 #include "device_common.hpp"
 #include "kernels.hpp"
@@ -36,6 +41,9 @@ constexpr uint32_t kDrOOB = 0x80000000u;  // buffer offset past every resource: 
 struct DirectArgs {
     const int8_t* xq;
     const float* a_scale;
+    const uint16_t* xb;  // bf16 activations (fused variant)
+    int8_t* xq_out;      // optional copies (fused variant, first block)
+    float* a_out;
     const uint8_t* packed;
     const float* w_scale;
     void* out;
@@ -52,9 +60,10 @@ __device__ __forceinline__ u32x4_d dr_load16(__amdgpu_buffer_rsrc_t r, uint32_t 
     return __builtin_bit_cast(u32x4_d, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
-template <int U>
+template <int U, bool FUSED>
 __global__ __launch_bounds__(64 * kDrWaves) void gemv_direct_kernel(DirectArgs p) {
     __shared__ int red[kDrWaves * 4 * 64];
+    __shared__ uint32_t s_max[kDrWaves][16];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int M = p.M, N = p.N, K = p.K;
@@ -67,32 +76,74 @@ __global__ __launch_bounds__(64 * kDrWaves) void gemv_direct_kernel(DirectArgs p
     const float ws_n = p.w_scale[n0 + min(l16, rows - 1)];  // used by threads tid < 16 M
     const __amdgpu_buffer_rsrc_t w_rsrc =
         dr_rsrc(p.packed + (int64_t)n0 * row_bytes, (uint32_t)(rows * row_bytes));
-    const __amdgpu_buffer_rsrc_t x_rsrc = dr_rsrc(p.xq, (uint32_t)(M * K));
+    const __amdgpu_buffer_rsrc_t x_rsrc =
+        FUSED ? dr_rsrc(p.xb, (uint32_t)(M * K * 2)) : dr_rsrc(p.xq, (uint32_t)(M * K));
     const uint32_t w_lane = (uint32_t)(l16 * row_bytes + 16 * q);
     const bool x_row = l16 < M;
+    constexpr int XW = FUSED ? 2 : 1;  // 16-byte loads per 16-activation group
 
-    // chunk j of this wave: 16 packed bytes and the four 16-byte activation groups
-    auto load = [&](int j, u32x4_d& w, u32x4_d (&X)[4]) {
+    // fused: every token's scale 127 / max|x| from a scan of its row by the whole block
+    float a_row = 0.f;  // scale of this lane's token (fused)
+    if constexpr (FUSED) {
+        const int pieces = K / 8;  // 16-byte pieces (8 bf16) per row
+        for (int m = 0; m < M; ++m) {
+            uint32_t mx = 0;
+            for (int i = tid; i < pieces; i += 64 * kDrWaves) {
+                const u32x4_d v = dr_load16(x_rsrc, (uint32_t)((m * K + 8 * i) * 2));
+                const uint32_t h[8] = {v[0], v[1], v[2], v[3], 0u, 0u, 0u, 0u};
+                mx = max(mx, absmax_bits16(h));
+            }
+            mx = wave_max_u32(mx);
+            if (lane == 0) s_max[wave][m] = mx;
+        }
+        __syncthreads();
+        const int mr = x_row ? l16 : 0;
+        uint32_t mx = s_max[0][mr];
+#pragma unroll
+        for (int w = 1; w < kDrWaves; ++w) mx = max(mx, s_max[w][mr]);
+        float amax = bf16_bits_to_f32(mx);
+        amax = amax < 1e-5f ? 1e-5f : amax;
+        a_row = 127.0f / amax;
+        if (blockIdx.x == 0 && p.a_out && lane < M && tid < 64) p.a_out[lane] = a_row;
+    }
+
+    // chunk j of this wave: 16 packed bytes and the four 16-activation groups
+    auto load = [&](int j, u32x4_d& w, u32x4_d (&X)[4][XW]) {
         const int c = wave + kDrWaves * j;
         const bool live = c < nch;
         w = dr_load16(w_rsrc, live ? w_lane + 64 * c : kDrOOB);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const int k0 = 256 * c + 64 * q + 16 * s;
-            X[s] = dr_load16(x_rsrc, (live && x_row && k0 < K) ? (uint32_t)(l16 * K + k0) : kDrOOB);
+            const bool ok = live && x_row && k0 < K;
+#pragma unroll
+            for (int h = 0; h < XW; ++h)
+                X[s][h] = dr_load16(x_rsrc, ok ? (uint32_t)((l16 * K + k0) * XW + 16 * h) : kDrOOB);
         }
     };
 
     v4i_d acc = {0, 0, 0, 0};
-    auto compute = [&](const u32x4_d& w, const u32x4_d (&X)[4]) {
+    auto compute = [&](int j, const u32x4_d& w, const u32x4_d (&X)[4][XW]) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const uint32_t d = w[s];
             const v4i_d b = {(int)ternary_field_i8<0>(d), (int)ternary_field_i8<1>(d),
                              (int)ternary_field_i8<2>(d), (int)ternary_field_i8<3>(d)};
-            const uint32_t xs[4] = {X[s][0], X[s][1], X[s][2], X[s][3]};
             uint32_t e[4];
-            transpose4x4_bytes(xs, e);
+            if constexpr (FUSED) {
+                const uint32_t h[8] = {X[s][0][0], X[s][0][1], X[s][0][2], X[s][0][3],
+                                       X[s][1][0], X[s][1][1], X[s][1][2], X[s][1][3]};
+                quant16_t(h, a_row, e);
+                const int k0 = 256 * (wave + kDrWaves * j) + 64 * q + 16 * s;
+                if (blockIdx.x == 0 && p.xq_out && x_row && k0 < K) {
+                    uint32_t dd[4];
+                    untranspose(e, dd);
+                    store_codes16<true>(p.xq_out, K, l16, k0, dd);
+                }
+            } else {
+                const uint32_t xs[4] = {X[s][0][0], X[s][0][1], X[s][0][2], X[s][0][3]};
+                transpose4x4_bytes(xs, e);
+            }
             const v4i_d a = {(int)e[0], (int)e[1], (int)e[2], (int)e[3]};
             acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc, 0, 0, 0);
         }
@@ -100,19 +151,21 @@ __global__ __launch_bounds__(64 * kDrWaves) void gemv_direct_kernel(DirectArgs p
     // batches of U chunks, two in flight: batch t + 1 is requested before batch t is
     // multiplied; batches past the wave's chunks read zeros
     const int nj = (nch - wave + kDrWaves - 1) / kDrWaves;  // chunks of this wave
-    u32x4_d wA[U], XA[U][4], wB[U], XB[U][4];
+    u32x4_d wA[U], XA[U][4][XW], wB[U], XB[U][4][XW];
 #pragma unroll
     for (int u = 0; u < U; ++u) load(u, wA[u], XA[u]);
     for (int j0 = 0; j0 < nj; j0 += 2 * U) {
 #pragma unroll
         for (int u = 0; u < U; ++u) load(j0 + U + u, wB[u], XB[u]);
 #pragma unroll
-        for (int u = 0; u < U; ++u) compute(wA[u], XA[u]);
+        for (int u = 0; u < U; ++u)
+            if (j0 + u < nj) compute(j0 + u, wA[u], XA[u]);
         if (j0 + U >= nj) break;
 #pragma unroll
         for (int u = 0; u < U; ++u) load(j0 + 2 * U + u, wA[u], XA[u]);
 #pragma unroll
-        for (int u = 0; u < U; ++u) compute(wB[u], XB[u]);
+        for (int u = 0; u < U; ++u)
+            if (j0 + U + u < nj) compute(j0 + U + u, wB[u], XB[u]);
     }
 
     // 16x16 int32 accumulator layout: lane l, register r -> row 4*(l/16)+r, column l%16
@@ -127,7 +180,18 @@ __global__ __launch_bounds__(64 * kDrWaves) void gemv_direct_kernel(DirectArgs p
 #pragma unroll
             for (int w = 0; w < kDrWaves; ++w) sum += red[(w * 4 + r) * 64 + l];
             // 1/a: v_rcp_f32 is within 1 ulp, and the rescale stays within 3 ulp
-            const float inv_a = __builtin_amdgcn_rcpf(p.a_scale[m]);
+            float a_m;
+            if constexpr (FUSED) {
+                uint32_t mx = s_max[0][m];
+#pragma unroll
+                for (int w = 1; w < kDrWaves; ++w) mx = max(mx, s_max[w][m]);
+                float amax = bf16_bits_to_f32(mx);
+                amax = amax < 1e-5f ? 1e-5f : amax;
+                a_m = 127.0f / amax;
+            } else {
+                a_m = p.a_scale[m];
+            }
+            const float inv_a = __builtin_amdgcn_rcpf(a_m);
             store_out(p.out, (int64_t)m * N + n0 + col, p.out_dtype, sum, ws_n, inv_a);
         }
     }
@@ -135,13 +199,17 @@ __global__ __launch_bounds__(64 * kDrWaves) void gemv_direct_kernel(DirectArgs p
 
 }  // namespace
 
-hipError_t launch_gemv_direct(const int8_t* xq, const float* a_scale, const uint8_t* packed,
-                              const float* w_scale, int64_t M, int64_t N, int64_t K, void* out,
-                              int out_dtype, hipStream_t stream) {
-    if (M < 1 || M > 16 || N < 1 || K % 64 != 0 || M * K > INT32_MAX) return hipErrorInvalidValue;
+hipError_t launch_gemv_direct(const int8_t* xq, const float* a_scale, const uint16_t* x_bf16,
+                              const uint8_t* packed, const float* w_scale, int64_t M, int64_t N,
+                              int64_t K, void* out, int out_dtype, int8_t* xq_out, float* a_out,
+                              hipStream_t stream) {
+    if (M < 1 || M > 16 || N < 1 || K % 64 != 0 || M * K * 2 > INT32_MAX) return hipErrorInvalidValue;
     DirectArgs a;
     a.xq = xq;
     a.a_scale = a_scale;
+    a.xb = x_bf16;
+    a.xq_out = xq_out;
+    a.a_out = a_out;
     a.packed = packed;
     a.w_scale = w_scale;
     a.out = out;
@@ -151,12 +219,17 @@ hipError_t launch_gemv_direct(const int8_t* xq, const float* a_scale, const uint
     a.out_dtype = out_dtype;
     const dim3 grid((unsigned)((N + 15) / 16)), blk(64 * kDrWaves);
     const int nj = ((K + 255) / 256 + kDrWaves - 1) / kDrWaves;  // chunks per wave
-    if (nj <= 2)
-        hipLaunchKernelGGL(gemv_direct_kernel<1>, grid, blk, 0, stream, a);
-    else if (nj <= 8)
-        hipLaunchKernelGGL(gemv_direct_kernel<2>, grid, blk, 0, stream, a);
-    else
-        hipLaunchKernelGGL(gemv_direct_kernel<4>, grid, blk, 0, stream, a);
+    const bool fused = x_bf16 != nullptr;
+    if (nj <= 2) {
+        if (fused) hipLaunchKernelGGL((gemv_direct_kernel<1, true>), grid, blk, 0, stream, a);
+        else hipLaunchKernelGGL((gemv_direct_kernel<1, false>), grid, blk, 0, stream, a);
+    } else if (nj <= 8) {
+        if (fused) hipLaunchKernelGGL((gemv_direct_kernel<2, true>), grid, blk, 0, stream, a);
+        else hipLaunchKernelGGL((gemv_direct_kernel<2, false>), grid, blk, 0, stream, a);
+    } else {
+        if (fused) hipLaunchKernelGGL((gemv_direct_kernel<4, true>), grid, blk, 0, stream, a);
+        else hipLaunchKernelGGL((gemv_direct_kernel<4, false>), grid, blk, 0, stream, a);
+    }
     return hipGetLastError();
 }
 

@@ -162,6 +162,7 @@ def test_gemv_matches_oracle(M, N, K):
 @pytest.mark.parametrize("M", [4, 8, 13, 16])
 @pytest.mark.parametrize("N,K", [(300, 1024), (4097, 512), (50, 14336), (17, 64)])
 def test_direct_and_staged_small_m_kernels_agree(M, N, K):
+    # (also: the fused launch at 12+ tokens equals quant_act followed by the int8 product)
     """For a few tokens the int8 product reads the activations straight into the matrix
     cores (bitnet_w2a8_gemv routes there); the staged kernel (ALGO_SKINNY) must give the
     same bits, and both the oracle's result."""
@@ -172,6 +173,9 @@ def test_direct_and_staged_small_m_kernels_agree(M, N, K):
         staged = bw.gemm(xq, a, packed, s, dt, algo="skinny")
         check_out(to_np(direct), o["acc"], o["ref"], dt, f"direct M={M} N={N} K={K} {dt}")
         assert np.array_equal(to_np(direct), to_np(staged)), f"direct != staged M={M} N={N} K={K} {dt}"
+        fused, xq_f, a_f = bw.quant_gemv(pb.x_dev, packed, s, dt, return_quant=True)
+        assert torch.equal(xq_f, xq) and torch.equal(a_f, a)
+        assert np.array_equal(to_np(fused), to_np(direct)), f"fused != two-step M={M} N={N} K={K} {dt}"
 
 
 @pytest.mark.parametrize("algo", ["tiled", "auto"])
@@ -197,8 +201,8 @@ def test_skinny_token_tiles_match_oracle(M, N, K):
         check_out(to_np(out), o["acc"], o["ref"], dt, f"skinny M={M} N={N} K={K} {dt}")
 
 
-@pytest.mark.parametrize("M", [1, 3, 16])
-@pytest.mark.parametrize("N,K", [(16, 256), (300, 1024), (37, 260), (50, 6912)])
+@pytest.mark.parametrize("M", [1, 3, 12, 16])
+@pytest.mark.parametrize("N,K", [(16, 256), (300, 1024), (37, 260), (50, 6912), (129, 14336)])
 def test_quant_gemv_matches_oracle(M, N, K):
     pb = Problem(M, N, K, seed=M * 5000 + N + K)
     o = pb.oracle()
