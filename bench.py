@@ -24,8 +24,10 @@ one launch per projection is reported beside it (value_ungrouped).
   copies, timed with events), against 8 TB/s; traffic from the committed rocprofv3
   counter summary when it matches the current kernel source.
 * gemm: the BitNet-2B-shaped prefill set at M = 512 (tiled int8-MFMA GEMM, bf16 out),
-  int8 TOPS against 5.0 POPS dense from the per-launch GEMM durations; the step rate
-  with the four quantization launches (one per shared input) is reported beside it.
+  with the projections that share an input in one grouped launch (q|k|v, o, gate|up,
+  down), int8 TOPS against 5.0 POPS dense from the per-launch GEMM durations; the step
+  rate with the four quantization launches and the rate of seven ungrouped launches are
+  reported beside it.
 * cpu_baseline: the CPU oracle on the host cores (test infrastructure, timed only
   here), on the same decode step repeated for ~10 s.
 * extras: the same per-launch rooflines at large shapes, where the bandwidth and
@@ -468,12 +470,16 @@ def bench_gemm(bw, workloads, torch, np, dev, layer, R_bytes, reps):
     index = {name: i for i, (name, _, _) in enumerate(layer)}
     groups = [[index[n] for n in grp] for grp in workloads.DECODE_GROUPS]
 
+    def grouped(r, grp):
+        i0 = grp[0]
+        return bw.gemm_grouped(xqs[i0], avs[i0], [copies[r][i] for i in grp],
+                               [scales[i] for i in grp], "bf16", out=[outs[i] for i in grp])
+
     def step(r):
         for grp in groups:
             i0 = grp[0]
             bw.quant_act(xs[i0], xq=xqs[i0], a_scale=avs[i0])
-            for i in grp:
-                bw.gemm(xqs[i0], avs[i0], copies[r][i], scales[i], "bf16", out=outs[i])
+            grouped(r, grp)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -483,18 +489,23 @@ def bench_gemm(bw, workloads, torch, np, dev, layer, R_bytes, reps):
     torch.cuda.synchronize()
     ms_step = run_steps(torch, step, R, 3, 40)
 
+    per_group_us = [graph_launch_us(torch, lambda r, grp=grp: grouped(r, grp), R, reps)
+                    for grp in groups]
     per_shape_us = [graph_launch_us(torch, lambda r, i=i: bw.gemm(
         xqs[i], avs[i], copies[r][i], scales[i], "bf16", out=outs[i]), R, reps)
         for i in range(len(layer))]
-    tops = ops / (sum(per_shape_us) * 1e-6) / 1e12
+    tops = ops / (sum(per_group_us) * 1e-6) / 1e12
     return {
         "metric": "GEMM int8 TOPS at M=512 (prefill layer set, bf16 out)",
         "workload": "bitnet-2b-prefill-layer-set",
         "value": round(tops, 2),
         "unit": "TOPS",
+        "launches": ["|".join(grp) for grp in workloads.DECODE_GROUPS],
         "step_tops_incl_quant": round(ops / (ms_step * 1e-3) / 1e12, 2),
-        "step": "one quant_act per shared input (q|k|v, o, gate|up, down) + seven GEMMs",
+        "step": "one quant_act + one grouped tiled GEMM per shared input (q|k|v, o, gate|up, "
+                "down)",
         "ms_per_step_incl_quant": round(ms_step, 4),
+        "value_ungrouped": round(ops / (sum(per_shape_us) * 1e-6) / 1e12, 2),
         "roofline": {
             "bound": "mfma",
             "achieved": round(tops, 2),
@@ -502,8 +513,11 @@ def bench_gemm(bw, workloads, torch, np, dev, layer, R_bytes, reps):
             "unit": "TFLOP/s",
             "frac": round(tops / INT8_MFMA_PEAK_TOPS, 4),
             "traffic": None,
-            "kernel": "tiled_kernel (per-shape tile plan)",
-            "per_shape_us": {name: round(us, 3) for (name, _, _), us in zip(layer, per_shape_us)},
+            "kernel": "tiled_kernel (tile plan per launch)",
+            "per_launch_us": {"|".join(grp): round(us, 3)
+                              for grp, us in zip(workloads.DECODE_GROUPS, per_group_us)},
+            "ungrouped_per_shape_us": {name: round(us, 3)
+                                       for (name, _, _), us in zip(layer, per_shape_us)},
         },
     }
 

@@ -175,6 +175,29 @@ int bitnet_w2a8_gemm(const int8_t* xq, const float* a_scale, const uint8_t* pack
                      int out_dtype, int algo, void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * bitnet_w2a8_gemm_grouped -- the tiled product (BITNET_ALGO_TILED) for several weight
+ * matrices that read the same int8 activations, in one launch: a prefill-sized batch
+ * through q, k and v, or through gate and up, of the LLaMA block in "BitNet 深度实战" §3.2
+ * (every nn.Linear a BitLinear layer; q, k, v share their input, and so do gate and up).
+ *   xq, a_scale      : int8 (M, K) codes and float (M) scales, shared; M >= 0.
+ *   groups           : 1 <= groups <= BITNET_MAX_GROUPS.
+ *   packed, w_scale, N, out : HOST arrays of `groups` entries, read during the call only;
+ *                      entry g is one product exactly as bitnet_w2a8_gemm's packed
+ *                      (N[g], K/4), w_scale (N[g]) and out (M, N[g]) arguments (device
+ *                      pointers, caller-owned).  N[g] == 0 is allowed and touches nothing
+ *                      of that entry.
+ *   out_dtype        : one output type for every group.
+ * The tile shape is chosen for the launch's total tile count; each out[g] is
+ * bit-identical to bitnet_w2a8_gemm(..., BITNET_ALGO_TILED, ...) on entry g alone (every
+ * tile shape yields the exact int32 sum and the same rescale).  Output buffers must not
+ * overlap one another or any input.
+ */
+int bitnet_w2a8_gemm_grouped(const int8_t* xq, const float* a_scale, int64_t M, int64_t K,
+                             int64_t groups, const uint8_t* const* packed,
+                             const float* const* w_scale, const int64_t* N, void* const* out,
+                             int out_dtype, void* stream);
+
+/*
  * bitnet_quant_gemv -- activation quantization fused into the decode product, one
  * launch ("BitNet-Triton" 技术架构 §3: the quantization folded into the matmul launch).
  *   x               : bf16 (M, K) as uint16, 1 <= M <= BITNET_GEMV_MAX_M.

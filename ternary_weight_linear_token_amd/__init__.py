@@ -21,6 +21,7 @@ from ._binding import (  # noqa: F401
     abi_version,
     bitlinear,
     gemm,
+    gemm_grouped,
     gemv,
     lib,
     library_path,

@@ -63,6 +63,7 @@ def lib():
             "bitnet_w2a8_gemm": ([p, p, p, p, i64, i64, i64, p, i32, i32, p, ctypes.c_size_t, p], i32),
             "bitnet_quant_gemv": ([p, p, p, i64, i64, i64, p, i32, p, p, p], i32),
             "bitnet_quant_gemv_grouped": ([p, i64, i64, i64, p, p, p, p, i32, p, p, p], i32),
+            "bitnet_w2a8_gemm_grouped": ([p, p, i64, i64, i64, p, p, p, p, i32, p], i32),
             "bitnet_quant_gemv_swiglu": ([p, p, p, p, p, i64, i64, i64, p, i32, p, p, p], i32),
             "bitnet_quant_act_per_tensor": ([p, i64, i64, p, p, p], i32),
             "bitnet_a16_gemv": ([p, p, p, i64, i64, i64, p, i32, p], i32),
@@ -260,6 +261,37 @@ def gemm(xq, a_scale, packed, w_scale, out_dtype="f32", algo="auto", out=None, w
                                   ws_ptr, ws_bytes, stream),
            "bitnet_w2a8_gemm")
     return out
+
+
+def gemm_grouped(xq, a_scale, packed, w_scale, out_dtype="f32", out=None):
+    """Tiled product for up to MAX_GROUPS weight matrices that read the same xq, one launch.
+
+    packed / w_scale: sequences of equal length; returns the list of (M, N_g) outputs."""
+    M, K = xq.shape
+    G = len(packed)
+    if len(w_scale) != G:
+        raise ValueError("packed and w_scale must have the same length")
+    code = _out_code(out_dtype)
+    Ns = [int(pk.shape[0]) for pk in packed]
+    outs = list(out) if out is not None else [None] * G
+    if len(outs) != G:
+        raise ValueError("out must have one tensor per group")
+    outs = [_alloc_out(o, M, n, code, xq.device) for o, n in zip(outs, Ns)]
+    P = (ctypes.c_void_p * max(G, 1))(*[_tensor(pk, torch.uint8, f"packed[{g}]", (Ns[g], K // 4))
+                                        for g, pk in enumerate(packed)])
+    S = (ctypes.c_void_p * max(G, 1))(*[_tensor(sc, torch.float32, f"w_scale[{g}]", (Ns[g],))
+                                        for g, sc in enumerate(w_scale)])
+    O = (ctypes.c_void_p * max(G, 1))(*[_tensor(o, _OUT_TORCH[code], f"out[{g}]", (M, Ns[g]))
+                                        for g, o in enumerate(outs)])
+    NN = (ctypes.c_int64 * max(G, 1))(*Ns)
+    _check(lib().bitnet_w2a8_gemm_grouped(_tensor(xq, torch.int8, "xq", (M, K)),
+                                          _tensor(a_scale, torch.float32, "a_scale", (M,)), M, K,
+                                          G, ctypes.cast(P, ctypes.c_void_p),
+                                          ctypes.cast(S, ctypes.c_void_p),
+                                          ctypes.cast(NN, ctypes.c_void_p),
+                                          ctypes.cast(O, ctypes.c_void_p), code, _stream(xq)),
+           "bitnet_w2a8_gemm_grouped")
+    return outs
 
 
 def quant_gemv(x, packed, w_scale, out_dtype="f32", out=None, return_quant=False):

@@ -187,6 +187,35 @@ int bitnet_w2a8_gemm(const int8_t* xq, const float* a_scale, const uint8_t* pack
                                            workspace, as_stream(stream)));
 }
 
+int bitnet_w2a8_gemm_grouped(const int8_t* xq, const float* a_scale, int64_t M, int64_t K,
+                             int64_t groups, const uint8_t* const* packed,
+                             const float* const* w_scale, const int64_t* N, void* const* out,
+                             int out_dtype, void* stream) {
+    if (!valid_dtype(out_dtype)) return BITNET_ERR_INVALID_ARG;
+    if (groups < 1 || groups > BITNET_MAX_GROUPS) return BITNET_ERR_INVALID_ARG;
+    if (!packed || !w_scale || !N || !out) return BITNET_ERR_INVALID_ARG;
+    int64_t total_n = 0;
+    for (int64_t g = 0; g < groups; ++g) {
+        int st = check_shape(M, N[g], K);
+        if (st) return st;
+        total_n += N[g];
+    }
+    if (total_n > INT32_MAX) return BITNET_ERR_INVALID_ARG;
+    if (M == 0 || total_n == 0) return BITNET_OK;
+    if (!xq || !a_scale) return BITNET_ERR_INVALID_ARG;
+    for (int64_t g = 0; g < groups; ++g) {
+        if (N[g] == 0) continue;
+        if (!packed[g] || !w_scale[g] || !out[g]) return BITNET_ERR_INVALID_ARG;
+        if (!aligned16(packed[g]) || !aligned16(w_scale[g]) || !aligned16(out[g]))
+            return BITNET_ERR_UNALIGNED;
+    }
+    if (!aligned16(xq) || !aligned16(a_scale)) return BITNET_ERR_UNALIGNED;
+    int st = check_device();
+    if (st) return st;
+    return record_hip(bitnet::launch_tiled_grouped(xq, a_scale, (int)groups, packed, w_scale, N,
+                                                   out, M, K, out_dtype, as_stream(stream)));
+}
+
 int bitnet_quant_gemv(const uint16_t* x, const uint8_t* packed, const float* w_scale,
                       int64_t M, int64_t N, int64_t K, void* out, int out_dtype,
                       int8_t* xq_out, float* a_scale_out, void* stream) {

@@ -62,6 +62,13 @@ hipError_t launch_gemv_direct(const int8_t* xq, const float* a_scale, const uint
 // Tiled int8 matrix-core product for any M.  `workspace` must hold
 // tiled_workspace_size(M, N, K) bytes whose counter area is zero (it is left zero).
 size_t tiled_workspace_size(int64_t M, int64_t N, int64_t K);
+// The tiled product for 1 <= groups <= BITNET_MAX_GROUPS weight matrices (N[g] rows
+// each, all K columns) against the same activations, in one launch; the tile plan is
+// chosen for the launch's total tile count.
+hipError_t launch_tiled_grouped(const int8_t* xq, const float* a_scale, int groups,
+                                const uint8_t* const* packed, const float* const* w_scale,
+                                const int64_t* N, void* const* out, int64_t M, int64_t K,
+                                int out_dtype, hipStream_t stream);
 hipError_t launch_tiled(const int8_t* xq, const float* a_scale, const uint8_t* packed,
                         const float* w_scale, int64_t M, int64_t N, int64_t K, void* out,
                         int out_dtype, void* workspace, hipStream_t stream);

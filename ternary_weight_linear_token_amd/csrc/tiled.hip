@@ -52,15 +52,22 @@ constexpr int kBK = 64;             // k per LDS stage
 constexpr int kAStride = kBK + 16;  // padded A row in LDS (bytes)
 constexpr int kXcds = 8;
 
+constexpr int kTdGroups = BITNET_MAX_GROUPS;
+
 struct TiledArgs {
     const int8_t* xq;
     const float* a_scale;
-    const uint8_t* packed;
-    const float* w_scale;
-    void* out;
-    int M, N, K;
-    int tiles_m, tiles_n;
-    int units;       // tiles
+    // weight matrices that share the activations: group g owns the work units
+    // first[g] .. first[g + 1] - 1 (row panel major, tiles_n[g] tiles per panel)
+    int groups;
+    int first[kTdGroups];
+    int g_N[kTdGroups];
+    int g_tiles_n[kTdGroups];
+    const uint8_t* g_packed[kTdGroups];
+    const float* g_wscale[kTdGroups];
+    void* g_out[kTdGroups];
+    int M, K;
+    int units;       // tiles of all groups
     int units_per_xcd;
     int out_dtype;
 };
@@ -92,9 +99,26 @@ __global__ __launch_bounds__(kTdThreads * G) void tiled_kernel(TiledArgs p) {
     const int xcd = blockIdx.x % kXcds;
     const int unit = xcd * p.units_per_xcd + blockIdx.x / kXcds;
     if (unit >= p.units) return;
-    const int tile = unit;
-    const int tile_m = tile / p.tiles_n;
-    const int tile_n = tile - tile_m * p.tiles_n;
+    // the unit's weight matrix: the last group whose first unit is at most `unit`
+    // (scalar compares and selects on the kernel arguments)
+    int first = p.first[0], N = p.g_N[0], tiles_n = p.g_tiles_n[0];
+    const uint8_t* packed = p.g_packed[0];
+    const float* w_scale = p.g_wscale[0];
+    void* out = p.g_out[0];
+#pragma unroll
+    for (int i = 1; i < kTdGroups; ++i) {
+        if (i < p.groups && unit >= p.first[i]) {
+            first = p.first[i];
+            N = p.g_N[i];
+            tiles_n = p.g_tiles_n[i];
+            packed = p.g_packed[i];
+            w_scale = p.g_wscale[i];
+            out = p.g_out[i];
+        }
+    }
+    const int tile = unit - first;
+    const int tile_m = tile / tiles_n;
+    const int tile_n = tile - tile_m * tiles_n;
     const int m0 = tile_m * BM, n0 = tile_n * BN;
 
     // G groups of four waves; group g takes the k-stages g, g + G, g + 2G, ... of the
@@ -109,7 +133,7 @@ __global__ __launch_bounds__(kTdThreads * G) void tiled_kernel(TiledArgs p) {
     const int wm = wave / WGN, wn = wave % WGN;
     unsigned char (*a_lds)[BM * kAStride] =
         reinterpret_cast<unsigned char (*)[BM * kAStride]>(smem + g * 2 * BM * kAStride);
-    const int M = p.M, N = p.N, K = p.K;
+    const int M = p.M, K = p.K;
     const int64_t row_bytes = K / 4;
     const int nk = (K + kBK - 1) / kBK;
 
@@ -124,7 +148,7 @@ __global__ __launch_bounds__(kTdThreads * G) void tiled_kernel(TiledArgs p) {
     const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<int8_t*>(p.xq) + (int64_t)m0 * K, (short)0, rows_a * K, 0x00020000);
     const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(p.packed) + (int64_t)n0 * row_bytes, (short)0,
+        const_cast<uint8_t*>(packed) + (int64_t)n0 * row_bytes, (short)0,
         (int)(rows_b * row_bytes), 0x00020000);
 
     // A: thread tid loads AV 16-byte pieces per stage (rows idx/4, k-groups idx%4).
@@ -186,7 +210,7 @@ __global__ __launch_bounds__(kTdThreads * G) void tiled_kernel(TiledArgs p) {
                 const int64_t off = k0 / 4 + 8 * q;
                 uint32_t d[2] = {0u, 0u};
                 if (row < rows_b) {
-                    const uint8_t* src = p.packed + (int64_t)(n0 + row) * row_bytes + off;
+                    const uint8_t* src = packed + (int64_t)(n0 + row) * row_bytes + off;
 #pragma unroll
                     for (int t = 0; t < 8; ++t)
                         if (off + t < row_bytes) d[t >> 2] |= (uint32_t)src[t] << (8 * (t & 3));
@@ -337,13 +361,13 @@ __global__ __launch_bounds__(kTdThreads * G) void tiled_kernel(TiledArgs p) {
             const int64_t o = (int64_t)m * N + nb;
             if (vec_ok && nb + 16 <= N) {
                 if (DT == 2) {
-                    int4* dst = reinterpret_cast<int4*>(static_cast<int*>(p.out) + o);
+                    int4* dst = reinterpret_cast<int4*>(static_cast<int*>(out) + o);
 #pragma unroll
                     for (int t = 0; t < 4; ++t)
                         dst[t] = make_int4(row[4 * t], row[4 * t + 1], row[4 * t + 2], row[4 * t + 3]);
                 } else {
                     float f[16];
-                    const float4* ws = reinterpret_cast<const float4*>(p.w_scale + nb);
+                    const float4* ws = reinterpret_cast<const float4*>(w_scale + nb);
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
                         const float4 sc = ws[t];
@@ -353,7 +377,7 @@ __global__ __launch_bounds__(kTdThreads * G) void tiled_kernel(TiledArgs p) {
                         f[4 * t + 3] = ((float)row[4 * t + 3] * sc.w) * inv_a;
                     }
                     if (DT == 0) {
-                        float4* dst = reinterpret_cast<float4*>(static_cast<float*>(p.out) + o);
+                        float4* dst = reinterpret_cast<float4*>(static_cast<float*>(out) + o);
 #pragma unroll
                         for (int t = 0; t < 4; ++t)
                             dst[t] = make_float4(f[4 * t], f[4 * t + 1], f[4 * t + 2], f[4 * t + 3]);
@@ -361,7 +385,7 @@ __global__ __launch_bounds__(kTdThreads * G) void tiled_kernel(TiledArgs p) {
                         uint32_t h[8];
 #pragma unroll
                         for (int t = 0; t < 8; ++t) h[t] = f32x2_to_bf16x2_rne(f[2 * t], f[2 * t + 1]);
-                        uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) + o);
+                        uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + o);
                         dst[0] = make_uint4(h[0], h[1], h[2], h[3]);
                         dst[1] = make_uint4(h[4], h[5], h[6], h[7]);
                     }
@@ -369,7 +393,7 @@ __global__ __launch_bounds__(kTdThreads * G) void tiled_kernel(TiledArgs p) {
             } else {
 #pragma unroll
                 for (int t = 0; t < 16; ++t)
-                    if (nb + t < N) store_out(p.out, o + t, DT, row[t], p.w_scale[nb + t], inv_a);
+                    if (nb + t < N) store_out(out, o + t, DT, row[t], w_scale[nb + t], inv_a);
             }
         }
         // keep consecutive blocks from being interleaved (bounds the live registers)
@@ -471,7 +495,6 @@ __global__ __launch_bounds__(kTdThreads * G) void tiled_kernel(TiledArgs p) {
 
 struct TilePlan {
     int bm, bn, g;  // block tile and k-groups per block
-    int tiles_m, tiles_n;
 };
 
 int device_cus() {
@@ -517,14 +540,19 @@ bool config_override(int* bm, int* bn, int* g) {
 // still covers every CU (per-CU matrix-core efficiency grows with the wave tile, because
 // the weight unpack and the activation transpose are amortized over more products), or
 // else 128x128 blocks with two k-groups, so each SIMD interleaves two waves.
-TilePlan plan_tiles(int64_t M, int64_t N, int64_t K) {
-    (void)K;
+TilePlan plan_tiles(int64_t M, const int64_t* N, int groups) {
     const int cus = device_cus();
     int bm = 128, bn = 128, g = 2;
     if (!config_override(&bm, &bn, &g)) {
-        const int64_t t64 = ((M + 63) / 64) * ((N + 127) / 128);
-        const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
-        const int64_t t256x128 = ((M + 255) / 256) * ((N + 127) / 128);
+        // tiles of the whole launch (all groups) for each candidate shape
+        int64_t n128 = 0, n256 = 0;
+        for (int i = 0; i < groups; ++i) {
+            n128 += (N[i] + 127) / 128;
+            n256 += (N[i] + 255) / 256;
+        }
+        const int64_t t64 = ((M + 63) / 64) * n128;
+        const int64_t t256 = ((M + 255) / 256) * n256;
+        const int64_t t256x128 = ((M + 255) / 256) * n128;
         if (t64 <= cus) {
             bm = 64;
             bn = 128;
@@ -543,16 +571,21 @@ TilePlan plan_tiles(int64_t M, int64_t N, int64_t K) {
     t.bm = bm;
     t.bn = bn;
     t.g = g;
-    t.tiles_m = (int)((M + bm - 1) / bm);
-    t.tiles_n = (int)((N + bn - 1) / bn);
     return t;
 }
 
 template <int BM, int BN, int D, int G, int WGN>
-hipError_t launch_plan(TiledArgs a, const TilePlan& t, bool aligned, hipStream_t stream) {
-    a.tiles_m = t.tiles_m;
-    a.tiles_n = t.tiles_n;
-    a.units = t.tiles_m * t.tiles_n;
+hipError_t launch_plan(TiledArgs a, const int64_t* N, bool aligned, hipStream_t stream) {
+    const int tiles_m = (a.M + BM - 1) / BM;
+    int units = 0;
+    for (int i = 0; i < kTdGroups; ++i) {
+        const int tn = i < a.groups ? (int)((N[i] + BN - 1) / BN) : 0;
+        a.first[i] = units;
+        a.g_tiles_n[i] = tn;
+        units += tiles_m * tn;
+    }
+    a.units = units;
+    if (units == 0) return hipSuccess;
     a.units_per_xcd = (a.units + kXcds - 1) / kXcds;
     const dim3 grid((unsigned)(a.units_per_xcd * kXcds));
     const dim3 blk(kTdThreads * G);
@@ -576,26 +609,42 @@ size_t tiled_workspace_size(int64_t M, int64_t N, int64_t K) {
     return 0;
 }
 
-hipError_t launch_tiled(const int8_t* xq, const float* a_scale, const uint8_t* packed,
-                        const float* w_scale, int64_t M, int64_t N, int64_t K, void* out,
-                        int out_dtype, void* workspace, hipStream_t stream) {
+hipError_t launch_tiled_grouped(const int8_t* xq, const float* a_scale, int groups,
+                                const uint8_t* const* packed, const float* const* w_scale,
+                                const int64_t* N, void* const* out, int64_t M, int64_t K,
+                                int out_dtype, hipStream_t stream) {
+    if (groups < 1 || groups > kTdGroups) return hipErrorInvalidValue;
     TiledArgs a;
     a.xq = xq;
     a.a_scale = a_scale;
-    a.packed = packed;
-    a.w_scale = w_scale;
-    a.out = out;
+    a.groups = groups;
+    for (int i = 0; i < kTdGroups; ++i) {
+        const bool on = i < groups;
+        a.g_N[i] = on ? (int)N[i] : 0;
+        a.g_packed[i] = on ? packed[i] : nullptr;
+        a.g_wscale[i] = on ? w_scale[i] : nullptr;
+        a.g_out[i] = on ? out[i] : nullptr;
+    }
     a.M = (int)M;
-    a.N = (int)N;
     a.K = (int)K;
     a.out_dtype = out_dtype;
     const bool aligned = (K % kBK) == 0;
+    int64_t n_all[kTdGroups];
+    for (int i = 0; i < kTdGroups; ++i) n_all[i] = i < groups ? N[i] : 0;
+    const TilePlan t = plan_tiles(M, n_all, groups);
+    if (t.bm == 256 && t.bn == 256) return launch_plan<256, 256, 2, 1, 4>(a, n_all, aligned, stream);
+    if (t.bm == 256) return launch_plan<256, 128, 4, 1, 2>(a, n_all, aligned, stream);
+    if (t.bm == 64) return launch_plan<64, 128, 4, 4, 4>(a, n_all, aligned, stream);
+    return launch_plan<128, 128, 4, 2, 2>(a, n_all, aligned, stream);
+}
+
+hipError_t launch_tiled(const int8_t* xq, const float* a_scale, const uint8_t* packed,
+                        const float* w_scale, int64_t M, int64_t N, int64_t K, void* out,
+                        int out_dtype, void* workspace, hipStream_t stream) {
     (void)workspace;
-    const TilePlan t = plan_tiles(M, N, K);
-    if (t.bm == 256 && t.bn == 256) return launch_plan<256, 256, 2, 1, 4>(a, t, aligned, stream);
-    if (t.bm == 256) return launch_plan<256, 128, 4, 1, 2>(a, t, aligned, stream);
-    if (t.bm == 64) return launch_plan<64, 128, 4, 4, 4>(a, t, aligned, stream);
-    return launch_plan<128, 128, 4, 2, 2>(a, t, aligned, stream);
+    void* outs[1] = {out};
+    return launch_tiled_grouped(xq, a_scale, 1, &packed, &w_scale, &N, outs, M, K, out_dtype,
+                                stream);
 }
 
 }  // namespace bitnet

@@ -157,6 +157,40 @@ def test_quant_gemv_grouped_validation(L):
     assert call(A, 1, 256, 2, arrs([None, None], [None, None], [0, 0], [None, None])) == OK
 
 
+def test_gemm_grouped_validation(L):
+    f = L.bitnet_w2a8_gemm_grouped
+    P = ctypes.c_void_p
+
+    def arrs(packed, scales, ns, outs):
+        g = len(ns)
+        return ((P * g)(*packed), (P * g)(*scales), (ctypes.c_int64 * g)(*ns), (P * g)(*outs))
+
+    ok3 = arrs([B, B + 0x100, B + 0x200], [C, C + 0x100, C + 0x200], [64, 16, 16],
+               [D, D + 0x1000, D + 0x2000])
+
+    def call(xq, sc, M, K, G, a, dt=1):
+        pk, ws, ns, outs = a
+        return f(xq, sc, M, K, G, ctypes.cast(pk, P), ctypes.cast(ws, P), ctypes.cast(ns, P),
+                 ctypes.cast(outs, P), dt, None)
+
+    assert call(A, E, 512, 256, 0, ok3) == INVALID             # no groups
+    assert call(A, E, 512, 256, 5, arrs([B] * 5, [C] * 5, [16] * 5, [D] * 5)) == INVALID
+    assert f(A, E, 512, 256, 3, None, None, None, None, 1, None) == INVALID
+    assert call(None, E, 512, 256, 3, ok3) == INVALID           # no activations
+    assert call(A, None, 512, 256, 3, ok3) == INVALID           # no scales
+    assert call(A, E, 512, 256, 3, ok3, dt=3) == INVALID        # bad dtype
+    assert call(A, E, -1, 256, 3, ok3) == INVALID
+    assert call(A, E, 512, 250, 3, ok3) == UNALIGNED            # K % 4
+    assert call(A + 4, E, 512, 256, 3, ok3) == UNALIGNED
+    assert call(A, E, 512, 256, 2, arrs([B, B + 4], [C, C], [16, 40], [D, F])) == UNALIGNED
+    assert call(A, E, 512, 256, 2, arrs([B, B], [C, C], [16, 40], [D, F + 2])) == UNALIGNED
+    assert call(A, E, 512, 256, 2, arrs([B, None], [C, C], [16, 40], [D, F])) == INVALID
+    assert call(A, E, 512, 256, 2, arrs([B, B], [C, C], [16, -1], [D, F])) == INVALID
+    # nothing to do: M == 0, or every group empty (its pointers are never looked at)
+    assert call(A, E, 0, 256, 3, ok3) == OK
+    assert call(A, E, 512, 256, 2, arrs([None, None], [None, None], [0, 0], [None, None])) == OK
+
+
 def test_quant_gemv_swiglu_validation(L):
     f = L.bitnet_quant_gemv_swiglu
     assert f(A, B, C, D, E, 1, 16, 256, F, 2, None, None, None) == INVALID   # int32 output

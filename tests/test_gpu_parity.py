@@ -239,6 +239,33 @@ def test_quant_gemv_grouped_matches_oracle(M, K, Ns):
                                    alone.view(torch.int32) if dt != "bf16" else alone.view(torch.int16))
 
 
+@pytest.mark.parametrize("M,K,Ns,dts", [
+    (130, 320, [257, 64, 0, 96], DT),             # 64x128 tiles, an empty group
+    (512, 384, [2560, 640, 640], DT),             # q|k|v shapes: 64x128 tiles
+    (600, 256, [6912, 6912], ("bf16", "i32")),    # gate|up shapes: 256x128 tiles
+    (1024, 128, [4096, 1024, 1024, 300], ("f32", "i32")),  # 128x128 tiles
+    (1300, 192, [6000, 5000], ("bf16", "i32")),   # 256x256 tiles
+])
+def test_gemm_grouped_matches_oracle(M, K, Ns, dts):
+    """Several weight matrices against one int8 activation matrix in one tiled launch
+    (the tile shape follows the launch's total tile count): each output matches the
+    oracle and is bit-identical to the tiled launch on that matrix alone."""
+    X = workloads.activations(M, K, seed=M * 13000 + K)
+    pbs = [Problem(M, n, K, seed=M * 13000 + K + 23 * g, X=X) for g, n in enumerate(Ns)]
+    os_ = [pb.oracle() for pb in pbs]
+    xq, a = dev(os_[0]["xq"]), dev(os_[0]["a_scale"])
+    packed = [dev(o["packed"]) for o in os_]
+    scales = [dev(o["w_scale"]) for o in os_]
+    for dt in dts:
+        outs = bw.gemm_grouped(xq, a, packed, scales, dt)
+        for g, (o, out) in enumerate(zip(os_, outs)):
+            assert tuple(out.shape) == (M, Ns[g])
+            check_out(to_np(out), o["acc"], o["ref"], dt, f"gemm grouped g={g} {M}x{Ns[g]}x{K} {dt}")
+            if Ns[g]:
+                alone = bw.gemm(xq, a, packed[g], scales[g], dt, algo="tiled")
+                assert torch.equal(out.view(torch.int16), alone.view(torch.int16)), (g, dt)
+
+
 def swiglu_tolerance(g_ref, u_ref, h_ref):
     """fp32 bound for h = silu(g) * u: g and u are each within 3 ulp of exact (see
     gpu_helpers); silu scales g's relative error by at most 1 + |g|; exp, the division
@@ -453,13 +480,17 @@ def test_graph_replay_of_grouped_swiglu_and_a16_launches():
     y = torch.empty((1, 300), dtype=torch.float32, device="cuda")
     xq = torch.empty((1, 1024), dtype=torch.int8, device="cuda")
     a = torch.empty((1,), dtype=torch.float32, device="cuda")
-    bufs = outs + [h, y, xq, a]
+    # a prefill-sized batch through the grouped tiled product
+    xq64, a64 = bw.quant_act(workloads.activations(64, 1024, seed=22).cuda())
+    gouts = [torch.empty((64, pb.N), dtype=torch.bfloat16, device="cuda") for pb in pbs]
+    bufs = outs + [h, y, xq, a] + gouts
 
     def work():
         bw.quant_gemv_grouped(x, pk, sc, "f32", out=outs)
         bw.quant_gemv_swiglu(x, pk[1], sc[1], pk[2], sc[2], "bf16", out=h)
         bw.a16_gemv(x, pk[0], sc[0], "f32", out=y)
         bw.quant_act_per_tensor(x, xq=xq, a_scale=a)
+        bw.gemm_grouped(xq64, a64, pk, sc, "bf16", out=gouts)
 
     work()
     torch.cuda.synchronize()
