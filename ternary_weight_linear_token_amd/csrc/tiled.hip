@@ -31,11 +31,14 @@
 //  * No split across blocks: handing int32 partial tiles between blocks needs
 //    device-scope release/acquire, which on this chip (one L2 per XCD) costs more than
 //    the split saves.  Small grids instead split K inside the block: 128x128 blocks of
-//    two four-wave k-groups, or, when 64x128 blocks fit the CUs in one round, 64x128
-//    blocks of four k-groups (alternate k-stages, accumulators combined through LDS),
-//    so each SIMD interleaves two or four waves.
+//    two four-wave k-groups and 64x128 blocks of four (alternate k-stages, accumulators
+//    combined through LDS), so each SIMD interleaves two or four waves.  The tile shape
+//    of a launch is the one with the least estimated time (plan_tiles).
 //  * Blocks are mapped to work units XCD by XCD (dispatch assigns consecutive blocks to
 //    the 8 XCDs in turn), so an XCD's L2 sees consecutive tiles of the same row panel.
+//  * Grouped launches: up to BITNET_MAX_GROUPS weight matrices that read the same
+//    activations (q, k, v; gate, up) share one grid; a block finds its matrix by scalar
+//    compares of its work unit against the groups' first units.
 #include <cstdio>
 #include <cstdlib>
 #include <type_traits>
@@ -534,43 +537,42 @@ bool config_override(int* bm, int* bn, int* g) {
     return true;
 }
 
-// Tile shape.  A grid that 64x128 blocks fit in one round (at most one block per CU)
-// is latency-bound per block: there 64x128 blocks with four k-groups (sixteen waves,
-// four per SIMD) finish each tile soonest.  Otherwise the largest block tile whose grid
-// still covers every CU (per-CU matrix-core efficiency grows with the wave tile, because
-// the weight unpack and the activation transpose are amortized over more products), or
-// else 128x128 blocks with two k-groups, so each SIMD interleaves two waves.
-TilePlan plan_tiles(int64_t M, const int64_t* N, int groups) {
-    const int cus = device_cus();
-    int bm = 128, bn = 128, g = 2;
-    if (!config_override(&bm, &bn, &g)) {
-        // tiles of the whole launch (all groups) for each candidate shape
-        int64_t n128 = 0, n256 = 0;
-        for (int i = 0; i < groups; ++i) {
-            n128 += (N[i] + 127) / 128;
-            n256 += (N[i] + 255) / 256;
-        }
-        const int64_t t64 = ((M + 63) / 64) * n128;
-        const int64_t t256 = ((M + 255) / 256) * n256;
-        const int64_t t256x128 = ((M + 255) / 256) * n128;
-        if (t64 <= cus) {
-            bm = 64;
-            bn = 128;
-            g = 4;
-        } else if (t256 >= cus) {
-            bm = 256;
-            bn = 256;
-            g = 1;
-        } else if (t256x128 >= cus) {
-            bm = 256;
-            bn = 128;
-            g = 1;
+// Tile shape: the compiled configuration with the least estimated time.  Every
+// configuration runs one block per CU, so a launch takes ceil(tiles / CUs) rounds, and
+// a round costs about the same whether it is full or not (a lone tile is bound by its
+// own latency, not by the matrix cores).  A round's cost is a fixed part plus a part per
+// unit of K, fitted to launches of each configuration on the 2B-shaped prefill products
+// (M = 512, N = 2560 and 13824, K = 64 .. 6912): small tiles start and finish soonest
+// (64x128 blocks with four k-groups: four waves per SIMD), large tiles amortize the
+// weight unpack and the activation transpose over more products per k.
+struct TileCost {
+    int bm, bn, g;
+    double fixed_us, per_k_us;
+};
+constexpr TileCost kTileCosts[] = {
+    {64, 128, 4, 4.7, 2.96e-3},
+    {128, 128, 2, 6.4, 4.5e-3},
+    {256, 128, 1, 7.0, 7.3e-3},
+    {256, 256, 1, 13.8, 11.8e-3},
+};
+
+TilePlan plan_tiles(int64_t M, int64_t K, const int64_t* N, int groups) {
+    TilePlan t;
+    if (config_override(&t.bm, &t.bn, &t.g)) return t;
+    const int64_t cus = device_cus();
+    double best = 0.0;
+    for (const TileCost& c : kTileCosts) {
+        int64_t tiles_n = 0;
+        for (int i = 0; i < groups; ++i) tiles_n += (N[i] + c.bn - 1) / c.bn;
+        const int64_t tiles = ((M + c.bm - 1) / c.bm) * tiles_n;
+        const double est = (double)((tiles + cus - 1) / cus) * (c.fixed_us + c.per_k_us * (double)K);
+        if (&c == kTileCosts || est < best) {
+            best = est;
+            t.bm = c.bm;
+            t.bn = c.bn;
+            t.g = c.g;
         }
     }
-    TilePlan t;
-    t.bm = bm;
-    t.bn = bn;
-    t.g = g;
     return t;
 }
 
@@ -631,7 +633,7 @@ hipError_t launch_tiled_grouped(const int8_t* xq, const float* a_scale, int grou
     const bool aligned = (K % kBK) == 0;
     int64_t n_all[kTdGroups];
     for (int i = 0; i < kTdGroups; ++i) n_all[i] = i < groups ? N[i] : 0;
-    const TilePlan t = plan_tiles(M, n_all, groups);
+    const TilePlan t = plan_tiles(M, K, n_all, groups);
     if (t.bm == 256 && t.bn == 256) return launch_plan<256, 256, 2, 1, 4>(a, n_all, aligned, stream);
     if (t.bm == 256) return launch_plan<256, 128, 4, 1, 2>(a, n_all, aligned, stream);
     if (t.bm == 64) return launch_plan<64, 128, 4, 4, 4>(a, n_all, aligned, stream);
