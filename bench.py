@@ -168,6 +168,15 @@ def main():
         for i in range(len(layer))]
     kern_us_total = sum(per_group_us)
     achieved = set_bytes / (kern_us_total * 1e-6) / 1e9
+    # the floor of each launch's grid: a plain streaming read of the launch's packed
+    # bytes with the same number of 256-thread blocks (one per 16 weight rows)
+    from ternary_weight_linear_token_amd import ceilings
+    shapes = {name: (N, K) for name, N, K in layer}
+    floor_us = [ceilings.same_grid_read_us(
+        torch, dev, sum(shapes[n][0] * shapes[n][1] // 4 for n in grp),
+        sum((shapes[n][0] + 15) // 16 for n in grp),
+        lambda launch, R: graph_launch_us(torch, launch, R, args.kernel_reps))
+        for grp in workloads.DECODE_GROUPS]
     kernel_hash = bw_build.kernel_hash("skinny.hip")
     traffic_bytes = load_traffic(kernel_hash)
     roofline = {
@@ -183,6 +192,9 @@ def main():
         "algorithmic_bytes_per_launch": set_bytes / len(groups),
         "per_launch_us": {"|".join(grp): round(us, 3)
                           for grp, us in zip(workloads.DECODE_GROUPS, per_group_us)},
+        "same_grid_plain_read_us": {"|".join(grp): round(us, 3)
+                                    for grp, us in zip(workloads.DECODE_GROUPS, floor_us)},
+        "frac_of_same_grid_plain_read": round(sum(floor_us) / kern_us_total, 4),
         "ungrouped_per_shape_us": {name: round(us, 3)
                                    for (name, _, _), us in zip(layer, per_shape_us)},
         "ungrouped_achieved": round(set_bytes / (sum(per_shape_us) * 1e-6) / 1e9, 1),

@@ -78,6 +78,31 @@ def hbm_read_gbs(torch, dev, nbytes=2 << 30, blocks=2048, reps=5):
     return nbytes / us / 1e3
 
 
+def same_grid_read_us(torch, dev, nbytes, blocks, graph_us, rotate_bytes=1 << 30):
+    """Per-launch time (us) of the plain streaming read of nbytes with `blocks` blocks of
+    256 threads (each block over its own contiguous share): the floor of any launch that
+    reads those bytes with that grid.  Buffers rotate over rotate_bytes so the bytes come
+    from HBM; graph_us(launch(r), R) times R back-to-back launches the way the product
+    kernels are timed."""
+    L = _probes()
+    n16 = max(1, nbytes // 16)
+    stride = n16 * 16
+    R = max(4, min(256, rotate_bytes // stride))
+    buf = torch.ones((R * stride // 4,), dtype=torch.int32, device=dev)
+    out = torch.empty((blocks * 256,), dtype=torch.int32, device=dev)
+
+    def launch(r):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        rc = L.bitnet_probe_read(buf.data_ptr() + (r % R) * stride, n16, out.data_ptr(),
+                                 blocks, stream)
+        if rc:
+            raise RuntimeError(f"bitnet_probe_read: hip error {rc}")
+
+    us = graph_us(launch, R)
+    del buf
+    return us
+
+
 def vendor_int8_gemm_tops(torch, dev, M, N, K, reps=10):
     """hipBLASLt int8 GEMM (torch._int_mm) on dense int8 operands: xq (M, K) times
     codes^T with codes (N, K) in {-1, 0, 1}; TOPS, or None if unavailable."""
