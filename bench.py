@@ -507,6 +507,16 @@ def bench_gemm(bw, workloads, torch, np, dev, layer, R_bytes, reps):
         xqs[i], avs[i], copies[r][i], scales[i], "bf16", out=outs[i]), R, reps)
         for i in range(len(layer))]
     tops = ops / (sum(per_group_us) * 1e-6) / 1e12
+    # context: the vendor int8 GEMM (hipBLASLt, dense int8 weights) on the same four
+    # products (each group's matrices concatenated along N)
+    from ternary_weight_linear_token_amd import ceilings
+    shapes = {name: (N, K) for name, N, K in layer}
+    vendor_us = 0.0
+    for grp in workloads.DECODE_GROUPS:
+        N = sum(shapes[n][0] for n in grp)
+        K = shapes[grp[0]][1]
+        t = ceilings.vendor_int8_gemm_tops(torch, dev, M, N, K)
+        vendor_us = None if (t is None or vendor_us is None) else vendor_us + 2.0 * M * N * K / t / 1e6
     return {
         "metric": "GEMM int8 TOPS at M=512 (prefill layer set, bf16 out)",
         "workload": "bitnet-2b-prefill-layer-set",
@@ -518,6 +528,8 @@ def bench_gemm(bw, workloads, torch, np, dev, layer, R_bytes, reps):
                 "down)",
         "ms_per_step_incl_quant": round(ms_step, 4),
         "value_ungrouped": round(ops / (sum(per_shape_us) * 1e-6) / 1e12, 2),
+        "vendor_int8_gemm_same_products_tops": (None if vendor_us is None else
+                                                round(ops / (vendor_us * 1e-6) / 1e12, 2)),
         "roofline": {
             "bound": "mfma",
             "achieved": round(tops, 2),
