@@ -6,7 +6,7 @@
 // dense contraction, so it runs on v_mfma_i32_32x32x32_i8.
 //
 // Design:
-//  * Block tile BM x BN, k-stage BK = 64, four wave64s in a (4/WGN) x WGN grid, each a
+//  * Block tile BM x BN, k-stage BK = 64 or 128, four wave64s in a (4/WGN) x WGN grid, each a
 //    tile of 32x32 int32 accumulator blocks.  Tall wave tiles amortize the weight
 //    unpack over more rows: the 256x256 blocks use a 1 x 4 grid (256 x 64 per wave,
 //    half the unpack of a 2 x 2 grid for twice the activation fragment reads).
@@ -51,8 +51,6 @@ namespace bitnet {
 namespace {
 
 constexpr int kTdThreads = 256;
-constexpr int kBK = 64;             // k per LDS stage
-constexpr int kAStride = kBK + 16;  // padded A row in LDS (bytes)
 constexpr int kXcds = 8;
 
 constexpr int kTdGroups = BITNET_MAX_GROUPS;
@@ -75,12 +73,16 @@ struct TiledArgs {
     int out_dtype;
 };
 
-template <int BM, int BN, int D, int G, int WGN, bool ALIGNED, int DT>
+template <int BM, int BN, int D, int G, int WGN, int BK, bool ALIGNED, int DT>
 __global__ __launch_bounds__(kTdThreads * G) void tiled_kernel(TiledArgs p) {
+    static_assert(BK == 64 || BK == 128, "k per LDS stage");
+    constexpr int KS = BK / 32;          // 32-k matrix products per stage and column block
+    constexpr int kAStride = BK + 16;    // padded A row in LDS (bytes)
+    constexpr int APR = BK / 16;         // 16-byte A pieces per row and stage
     constexpr int WGM = 4 / WGN;                 // waves along M and N
     constexpr int WM = BM / WGM, WN = BN / WGN;  // wave tile
     constexpr int MB = WM / 32, NB = WN / 32;  // 32x32 blocks per wave
-    constexpr int AV = BM * (kBK / 16) / kTdThreads;  // 16-byte A loads per thread per stage
+    constexpr int AV = BM * APR / kTdThreads;  // 16-byte A loads per thread per stage
     constexpr int BROWS_PER_THREAD = (BN + kTdThreads - 1) / kTdThreads;
     static_assert(AV >= 1, "tile/thread mismatch");
     (void)BROWS_PER_THREAD;
@@ -138,7 +140,7 @@ __global__ __launch_bounds__(kTdThreads * G) void tiled_kernel(TiledArgs p) {
         reinterpret_cast<unsigned char (*)[BM * kAStride]>(smem + g * 2 * BM * kAStride);
     const int M = p.M, K = p.K;
     const int64_t row_bytes = K / 4;
-    const int nk = (K + kBK - 1) / kBK;
+    const int nk = (K + BK - 1) / BK;
 
     for (int i = (int)threadIdx.x; i < BM; i += kTdThreads * G) {
         const int m = m0 + i;
@@ -162,22 +164,24 @@ __global__ __launch_bounds__(kTdThreads * G) void tiled_kernel(TiledArgs p) {
 #pragma unroll
     for (int j = 0; j < AV; ++j) {
         const int idx = tid + j * kTdThreads;
-        a_voff[j] = (idx >> 2) * K + 16 * (idx & 3);
+        a_voff[j] = (idx / APR) * K + 16 * (idx % APR);
     }
     int b_voff[NB];
 #pragma unroll
-    for (int j = 0; j < NB; ++j) b_voff[j] = (wn * WN + 32 * j + l32) * (int)row_bytes + 8 * q;
+    for (int j = 0; j < NB; ++j) b_voff[j] = (wn * WN + 32 * j + l32) * (int)row_bytes + (BK / 8) * q;
 
     static_assert(D == 2 || D == 4, "pipeline depth");
+    // B registers of one stage: per column block, KS packed dwords (16 weights each)
+    using BVec = std::conditional_t<KS == 2, uint2, uint4>;
     uint4 a_reg[D][AV];
-    uint2 b_reg[D][NB];
+    BVec b_reg[D][NB];
 
     // Stage kt of K; a stage past the end (kt >= nk) reads as zeros: its scalar offset
     // lies beyond both descriptors' ranges (the 32-bit sum with any in-range voffset
     // cannot wrap), so the products it feeds add nothing.
-    auto load_stage = [&](uint4 (&ar)[AV], uint2 (&br)[NB], int kt) {
+    auto load_stage = [&](uint4 (&ar)[AV], BVec (&br)[NB], int kt) {
         const bool live = kt < nk;
-        const int k0 = live ? kt * kBK : 0;
+        const int k0 = live ? kt * BK : 0;
         if (ALIGNED) {
             const uint32_t sa = live ? (uint32_t)k0 : 0x80000000u;
             const uint32_t sb = live ? (uint32_t)(k0 / 4) : 0x80000000u;
@@ -185,19 +189,23 @@ __global__ __launch_bounds__(kTdThreads * G) void tiled_kernel(TiledArgs p) {
             for (int j = 0; j < AV; ++j)
                 ar[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, a_voff[j], sa, 0));
 #pragma unroll
-            for (int j = 0; j < NB; ++j)
-                br[j] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(b_rsrc, b_voff[j], sb, 0));
+            for (int j = 0; j < NB; ++j) {
+                if constexpr (KS == 2)
+                    br[j] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(b_rsrc, b_voff[j], sb, 0));
+                else
+                    br[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, b_voff[j], sb, 0));
+            }
         } else if (!live) {
 #pragma unroll
             for (int j = 0; j < AV; ++j) ar[j] = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
-            for (int j = 0; j < NB; ++j) br[j] = make_uint2(0u, 0u);
+            for (int j = 0; j < NB; ++j) br[j] = BVec{};
         } else {
-            // K not a multiple of 64: byte loads, zero past the end of each row
+            // K not a multiple of the stage: byte loads, zero past the end of each row
 #pragma unroll
             for (int j = 0; j < AV; ++j) {
                 const int idx = tid + j * kTdThreads;
-                const int row = idx >> 2, kk = k0 + 16 * (idx & 3);
+                const int row = idx / APR, kk = k0 + 16 * (idx % APR);
                 uint32_t d[4] = {0u, 0u, 0u, 0u};
                 if (row < rows_a) {
                     const int8_t* src = p.xq + (int64_t)(m0 + row) * K + kk;
@@ -210,15 +218,20 @@ __global__ __launch_bounds__(kTdThreads * G) void tiled_kernel(TiledArgs p) {
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
                 const int row = wn * WN + 32 * j + l32;
-                const int64_t off = k0 / 4 + 8 * q;
-                uint32_t d[2] = {0u, 0u};
+                const int64_t off = k0 / 4 + (BK / 8) * q;
+                uint32_t d[KS];
+#pragma unroll
+                for (int t = 0; t < KS; ++t) d[t] = 0u;
                 if (row < rows_b) {
                     const uint8_t* src = packed + (int64_t)(n0 + row) * row_bytes + off;
 #pragma unroll
-                    for (int t = 0; t < 8; ++t)
+                    for (int t = 0; t < BK / 8; ++t)
                         if (off + t < row_bytes) d[t >> 2] |= (uint32_t)src[t] << (8 * (t & 3));
                 }
-                br[j] = make_uint2(d[0], d[1]);
+                if constexpr (KS == 2)
+                    br[j] = make_uint2(d[0], d[1]);
+                else
+                    br[j] = make_uint4(d[0], d[1], d[2], d[3]);
             }
         }
     };
@@ -227,7 +240,7 @@ __global__ __launch_bounds__(kTdThreads * G) void tiled_kernel(TiledArgs p) {
 #pragma unroll
         for (int j = 0; j < AV; ++j) {
             const int idx = tid + j * kTdThreads;
-            const int row = idx >> 2, col = idx & 3;
+            const int row = idx / APR, col = idx % APR;
             const uint32_t d[4] = {ar[j].x, ar[j].y, ar[j].z, ar[j].w};
             uint32_t e[4];
             transpose4x4_bytes(d, e);
@@ -246,29 +259,33 @@ __global__ __launch_bounds__(kTdThreads * G) void tiled_kernel(TiledArgs p) {
 
     // Weight operands of one stage, unpacked: B[s][j] feeds k-substep s, column block j.
     // Lane group q owns the 16-weight groups 2q + s of the 64-k stage.
-    auto unpack_b = [&](const uint2 (&br)[NB], v4i (&Bu)[2][NB]) {
+    auto unpack_b = [&](const BVec (&br)[NB], v4i (&Bu)[KS][NB]) {
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
+        for (int s = 0; s < KS; ++s)
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
-                const uint32_t d = s == 0 ? br[j].x : br[j].y;
+                uint32_t d;
+                if constexpr (KS == 2)
+                    d = s == 0 ? br[j].x : br[j].y;
+                else
+                    d = s == 0 ? br[j].x : (s == 1 ? br[j].y : (s == 2 ? br[j].z : br[j].w));
                 Bu[s][j][0] = (int)ternary_field_i8<0>(d);
                 Bu[s][j][1] = (int)ternary_field_i8<1>(d);
                 Bu[s][j][2] = (int)ternary_field_i8<2>(d);
                 Bu[s][j][3] = (int)ternary_field_i8<3>(d);
             }
     };
-    auto read_a = [&](int buf, v4i (&A)[2][MB]) {
+    auto read_a = [&](int buf, v4i (&A)[KS][MB]) {
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
+        for (int s = 0; s < KS; ++s)
 #pragma unroll
             for (int i = 0; i < MB; ++i)
                 A[s][i] = *reinterpret_cast<const v4i*>(
-                    &a_lds[buf][(wm * WM + 32 * i + l32) * kAStride + 16 * (2 * q + s)]);
+                    &a_lds[buf][(wm * WM + 32 * i + l32) * kAStride + 16 * (KS * q + s)]);
     };
-    auto mfma_stage = [&](const v4i (&A)[2][MB], const v4i (&Bu)[2][NB]) {
+    auto mfma_stage = [&](const v4i (&A)[KS][MB], const v4i (&Bu)[KS][NB]) {
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
+        for (int s = 0; s < KS; ++s)
 #pragma unroll
             for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -293,10 +310,10 @@ __global__ __launch_bounds__(kTdThreads * G) void tiled_kernel(TiledArgs p) {
     // products are interleaved with the next step's weight unpack, the loads D steps
     // ahead and the transposed store of the next step's activations, so the vector ALU
     // and LDS work hides under the matrix cores.
-    constexpr int kMf = 2 * MB * NB;                               // products per step
-    constexpr int kVa = (2 * NB * 11 + AV * 8 + kMf - 1) / kMf;    // VALU per product
+    constexpr int kMf = KS * MB * NB;                              // products per step
+    constexpr int kVa = (KS * NB * 11 + AV * 8 + kMf - 1) / kMf;   // VALU per product
     auto schedule_step = [&]() {
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * MB, 0);   // A fragment reads
+        __builtin_amdgcn_sched_group_barrier(0x100, KS * MB, 0);  // A fragment reads
         __builtin_amdgcn_sched_group_barrier(0x020, AV + NB, 0);  // loads D steps ahead
 #pragma unroll
         for (int i = 0; i < kMf; ++i) {
@@ -308,14 +325,14 @@ __global__ __launch_bounds__(kTdThreads * G) void tiled_kernel(TiledArgs p) {
 #pragma unroll
     for (int d = 0; d < D; ++d) load_stage(a_reg[d], b_reg[d], stage_of(d));
     store_stage(a_reg[0], 0);
-    v4i Bu[2][2][NB];
+    v4i Bu[2][KS][NB];
     unpack_b(b_reg[0], Bu[0]);
     __syncthreads();
     int it = 0;
     for (; it + D <= nsteps; it += D) {
 #pragma unroll
         for (int u = 0; u < D; ++u) {
-            v4i A[2][MB];
+            v4i A[KS][MB];
             read_a(u & 1, A);
             load_stage(a_reg[u], b_reg[u], stage_of(it + u + D));
             unpack_b(b_reg[(u + 1) % D], Bu[(u + 1) & 1]);
@@ -328,7 +345,7 @@ __global__ __launch_bounds__(kTdThreads * G) void tiled_kernel(TiledArgs p) {
 #pragma unroll
     for (int u = 0; u < D - 1; ++u) {
         if (it + u >= nsteps) break;
-        v4i A[2][MB];
+        v4i A[KS][MB];
         read_a(u & 1, A);
         if (it + u + 1 < nsteps) {
             unpack_b(b_reg[u + 1], Bu[(u + 1) & 1]);
@@ -498,6 +515,7 @@ __global__ __launch_bounds__(kTdThreads * G) void tiled_kernel(TiledArgs p) {
 
 struct TilePlan {
     int bm, bn, g;  // block tile and k-groups per block
+    int bk;         // k per LDS stage
 };
 
 int device_cus() {
@@ -542,42 +560,53 @@ bool config_override(int* bm, int* bn, int* g) {
 // a round costs about the same whether it is full or not (a lone tile is bound by its
 // own latency, not by the matrix cores).  A round's cost is a fixed part plus a part per
 // unit of K, fitted to launches of each configuration on the 2B-shaped prefill products
-// (M = 512, N = 2560 and 13824, K = 64 .. 6912): small tiles start and finish soonest
+// (M = 512, N = 2560, K = 256 .. 5120, one round): small tiles start and finish soonest
 // (64x128 blocks with four k-groups: four waves per SIMD), large tiles amortize the
-// weight unpack and the activation transpose over more products per k.
+// weight unpack and the activation transpose over more products per k.  128-k stages
+// (half the barriers and twice the bytes per load of 64-k stages) need K % 128 == 0;
+// the 256x256 tile keeps 64-k stages (128-k ones spill its registers).
 struct TileCost {
-    int bm, bn, g;
+    int bm, bn, g, bk;
     double fixed_us, per_k_us;
 };
 constexpr TileCost kTileCosts[] = {
-    {64, 128, 4, 4.7, 2.96e-3},
-    {128, 128, 2, 6.4, 4.5e-3},
-    {256, 128, 1, 7.0, 7.3e-3},
-    {256, 256, 1, 13.8, 11.8e-3},
+    {64, 128, 4, 128, 5.4, 2.13e-3},
+    {128, 128, 2, 128, 6.3, 3.42e-3},
+    {256, 128, 1, 128, 8.2, 6.61e-3},
+    {64, 128, 4, 64, 4.7, 2.96e-3},
+    {128, 128, 2, 64, 6.4, 4.5e-3},
+    {256, 128, 1, 64, 7.0, 7.3e-3},
+    {256, 256, 1, 64, 10.5, 11.7e-3},
 };
 
 TilePlan plan_tiles(int64_t M, int64_t K, const int64_t* N, int groups) {
     TilePlan t;
-    if (config_override(&t.bm, &t.bn, &t.g)) return t;
+    if (config_override(&t.bm, &t.bn, &t.g)) {
+        t.bk = (K % 128 == 0 && !(t.bm == 256 && t.bn == 256)) ? 128 : 64;
+        return t;
+    }
     const int64_t cus = device_cus();
-    double best = 0.0;
+    double best = -1.0;
     for (const TileCost& c : kTileCosts) {
+        if (K % c.bk != 0 && c.bk != 64) continue;
         int64_t tiles_n = 0;
         for (int i = 0; i < groups; ++i) tiles_n += (N[i] + c.bn - 1) / c.bn;
         const int64_t tiles = ((M + c.bm - 1) / c.bm) * tiles_n;
         const double est = (double)((tiles + cus - 1) / cus) * (c.fixed_us + c.per_k_us * (double)K);
-        if (&c == kTileCosts || est < best) {
+        if (best < 0.0 || est < best) {
             best = est;
             t.bm = c.bm;
             t.bn = c.bn;
             t.g = c.g;
+            t.bk = c.bk;
         }
     }
     return t;
 }
 
-template <int BM, int BN, int D, int G, int WGN>
-hipError_t launch_plan(TiledArgs a, const int64_t* N, bool aligned, hipStream_t stream) {
+template <int BM, int BN, int D, int G, int WGN, int BK>
+hipError_t launch_plan(TiledArgs a, const int64_t* N, hipStream_t stream) {
+    const bool aligned = (a.K % BK) == 0;
     const int tiles_m = (a.M + BM - 1) / BM;
     int units = 0;
     for (int i = 0; i < kTdGroups; ++i) {
@@ -591,13 +620,23 @@ hipError_t launch_plan(TiledArgs a, const int64_t* N, bool aligned, hipStream_t 
     a.units_per_xcd = (a.units + kXcds - 1) / kXcds;
     const dim3 grid((unsigned)(a.units_per_xcd * kXcds));
     const dim3 blk(kTdThreads * G);
+    if constexpr (BK == 128) {
+        // planned only for K % 128 == 0: the aligned kernels alone are built
+        if (!aligned) return hipErrorInvalidValue;
+        switch (a.out_dtype) {
+            case 0: hipLaunchKernelGGL((tiled_kernel<BM, BN, D, G, WGN, BK, true, 0>), grid, blk, 0, stream, a); break;
+            case 1: hipLaunchKernelGGL((tiled_kernel<BM, BN, D, G, WGN, BK, true, 1>), grid, blk, 0, stream, a); break;
+            default: hipLaunchKernelGGL((tiled_kernel<BM, BN, D, G, WGN, BK, true, 2>), grid, blk, 0, stream, a); break;
+        }
+        return hipGetLastError();
+    }
     switch (a.out_dtype * 2 + (aligned ? 1 : 0)) {
-        case 0: hipLaunchKernelGGL((tiled_kernel<BM, BN, D, G, WGN, false, 0>), grid, blk, 0, stream, a); break;
-        case 1: hipLaunchKernelGGL((tiled_kernel<BM, BN, D, G, WGN, true, 0>), grid, blk, 0, stream, a); break;
-        case 2: hipLaunchKernelGGL((tiled_kernel<BM, BN, D, G, WGN, false, 1>), grid, blk, 0, stream, a); break;
-        case 3: hipLaunchKernelGGL((tiled_kernel<BM, BN, D, G, WGN, true, 1>), grid, blk, 0, stream, a); break;
-        case 4: hipLaunchKernelGGL((tiled_kernel<BM, BN, D, G, WGN, false, 2>), grid, blk, 0, stream, a); break;
-        default: hipLaunchKernelGGL((tiled_kernel<BM, BN, D, G, WGN, true, 2>), grid, blk, 0, stream, a); break;
+        case 0: hipLaunchKernelGGL((tiled_kernel<BM, BN, D, G, WGN, BK, false, 0>), grid, blk, 0, stream, a); break;
+        case 1: hipLaunchKernelGGL((tiled_kernel<BM, BN, D, G, WGN, BK, true, 0>), grid, blk, 0, stream, a); break;
+        case 2: hipLaunchKernelGGL((tiled_kernel<BM, BN, D, G, WGN, BK, false, 1>), grid, blk, 0, stream, a); break;
+        case 3: hipLaunchKernelGGL((tiled_kernel<BM, BN, D, G, WGN, BK, true, 1>), grid, blk, 0, stream, a); break;
+        case 4: hipLaunchKernelGGL((tiled_kernel<BM, BN, D, G, WGN, BK, false, 2>), grid, blk, 0, stream, a); break;
+        default: hipLaunchKernelGGL((tiled_kernel<BM, BN, D, G, WGN, BK, true, 2>), grid, blk, 0, stream, a); break;
     }
     return hipGetLastError();
 }
@@ -630,14 +669,20 @@ hipError_t launch_tiled_grouped(const int8_t* xq, const float* a_scale, int grou
     a.M = (int)M;
     a.K = (int)K;
     a.out_dtype = out_dtype;
-    const bool aligned = (K % kBK) == 0;
     int64_t n_all[kTdGroups];
     for (int i = 0; i < kTdGroups; ++i) n_all[i] = i < groups ? N[i] : 0;
     const TilePlan t = plan_tiles(M, K, n_all, groups);
-    if (t.bm == 256 && t.bn == 256) return launch_plan<256, 256, 2, 1, 4>(a, n_all, aligned, stream);
-    if (t.bm == 256) return launch_plan<256, 128, 4, 1, 2>(a, n_all, aligned, stream);
-    if (t.bm == 64) return launch_plan<64, 128, 4, 4, 4>(a, n_all, aligned, stream);
-    return launch_plan<128, 128, 4, 2, 2>(a, n_all, aligned, stream);
+    // register sets in flight: 64-k stages 4 (2 for 256x256); 128-k stages 2, or 4 for
+    // the 256x128 tile (its accumulators live in the matrix-core registers)
+    if (t.bm == 256 && t.bn == 256) return launch_plan<256, 256, 2, 1, 4, 64>(a, n_all, stream);
+    if (t.bk == 128) {
+        if (t.bm == 256) return launch_plan<256, 128, 4, 1, 2, 128>(a, n_all, stream);
+        if (t.bm == 64) return launch_plan<64, 128, 2, 4, 4, 128>(a, n_all, stream);
+        return launch_plan<128, 128, 2, 2, 2, 128>(a, n_all, stream);
+    }
+    if (t.bm == 256) return launch_plan<256, 128, 4, 1, 2, 64>(a, n_all, stream);
+    if (t.bm == 64) return launch_plan<64, 128, 4, 4, 4, 64>(a, n_all, stream);
+    return launch_plan<128, 128, 4, 2, 2, 64>(a, n_all, stream);
 }
 
 hipError_t launch_tiled(const int8_t* xq, const float* a_scale, const uint8_t* packed,

@@ -240,11 +240,15 @@ def test_quant_gemv_grouped_matches_oracle(M, K, Ns):
 
 
 @pytest.mark.parametrize("M,K,Ns,dts", [
-    (130, 320, [257, 64, 0, 96], DT),             # 64x128 tiles, an empty group
-    (512, 384, [2560, 640, 640], DT),             # q|k|v shapes: 64x128 tiles
-    (600, 256, [6912, 6912], ("bf16", "i32")),    # gate|up shapes: 256x256 tiles
-    (1024, 128, [4096, 1024, 1024, 300], ("f32", "i32")),  # 256x128 tiles
-    (257, 320, [5000, 4000], ("bf16", "i32")),    # 128x128 tiles
+    # tile shape and k-stage chosen by the plan for each launch:
+    (130, 320, [257, 64, 0, 96], DT),             # 64x128, 64-k, an empty group
+    (512, 384, [2560, 640, 640], DT),             # q|k|v shapes: 64x128, 64-k
+    (512, 2560, [2560, 640, 640], ("bf16", "i32")),  # q|k|v at full size: 64x128, 128-k
+    (600, 256, [6912, 6912], ("bf16", "i32")),    # gate|up shapes: 256x256, 64-k
+    (500, 2048, [6000, 7000], ("f32", "i32")),    # 256x128, 128-k
+    (1024, 128, [4096, 1024, 1024, 300], ("f32", "i32")),  # 256x128, 64-k
+    (257, 320, [5000, 4000], ("bf16", "i32")),    # 128x128, 64-k
+    (300, 384, [4100, 4100], ("bf16", "i32")),    # 128x128, 128-k
 ])
 def test_gemm_grouped_matches_oracle(M, K, Ns, dts):
     """Several weight matrices against one int8 activation matrix in one tiled launch
@@ -518,8 +522,8 @@ def test_graph_replay_of_grouped_swiglu_and_a16_launches():
 
 def test_gemm_small_and_large_tile_grids_with_caller_workspace():
     # Shapes that select each tile configuration (64x128 with four k-groups, 128x128 with
-    # two, 256x128, 256x256), including grids far smaller than the CU count and ragged
-    # edges; a caller workspace is accepted and left untouched.
+    # two, 256x128, 256x256; 64-k and 128-k stages), including grids far smaller than
+    # the CU count and ragged edges; a caller workspace is accepted and left untouched.
     ws = torch.full((1 << 20,), 0x5A, dtype=torch.uint8, device="cuda")
     for (M, N, K) in [(300, 257, 2560), (512, 2560, 2560), (130, 640, 6912), (17, 1024, 4096),
                       (1024, 8192, 512), (600, 16384, 256), (257, 9000, 320), (520, 33000, 320),
