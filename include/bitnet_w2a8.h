@@ -198,6 +198,22 @@ int bitnet_w2a8_gemm_grouped(const int8_t* xq, const float* a_scale, int64_t M, 
                              int out_dtype, void* stream);
 
 /*
+ * bitnet_w2a8_gemm_plan -- the tile plan a tiled launch (BITNET_ALGO_TILED, or
+ * bitnet_w2a8_gemm_grouped) takes for M tokens, K columns and `groups` weight matrices of
+ * N[g] rows (HOST array), on a device with `cus` compute units (cus <= 0: the current
+ * device's; with no device the count defaults to 256).  Host-only: launches nothing.
+ *   plan : HOST int32[4] output = block rows, block columns, k-groups per block (waves
+ *          per block / 4), k per LDS stage.
+ * The plan is the compiled tile configuration with the least estimated time (rounds of
+ * one block per CU times a per-configuration cost fitted on this chip); the environment
+ * variable BITNET_TILED_CONFIG="bm,bn,g" (read once per process) overrides the shape.
+ * Returns BITNET_ERR_INVALID_ARG for M < 1, groups outside 1..BITNET_MAX_GROUPS, N[g] < 0,
+ * no rows at all, or NULL arrays; BITNET_ERR_UNALIGNED for K % 4 != 0.
+ */
+int bitnet_w2a8_gemm_plan(int64_t M, int64_t K, int64_t groups, const int64_t* N, int64_t cus,
+                          int32_t* plan);
+
+/*
  * bitnet_quant_gemv -- activation quantization fused into the decode product, one
  * launch ("BitNet-Triton" 技术架构 §3: the quantization folded into the matmul launch).
  *   x               : bf16 (M, K) as uint16, 1 <= M <= BITNET_GEMV_MAX_M.

@@ -64,6 +64,7 @@ def lib():
             "bitnet_quant_gemv": ([p, p, p, i64, i64, i64, p, i32, p, p, p], i32),
             "bitnet_quant_gemv_grouped": ([p, i64, i64, i64, p, p, p, p, i32, p, p, p], i32),
             "bitnet_w2a8_gemm_grouped": ([p, p, i64, i64, i64, p, p, p, p, i32, p], i32),
+            "bitnet_w2a8_gemm_plan": ([i64, i64, i64, p, i64, p], i32),
             "bitnet_quant_gemv_swiglu": ([p, p, p, p, p, i64, i64, i64, p, i32, p, p, p], i32),
             "bitnet_quant_act_per_tensor": ([p, i64, i64, p, p, p], i32),
             "bitnet_a16_gemv": ([p, p, p, i64, i64, i64, p, i32, p], i32),
@@ -292,6 +293,18 @@ def gemm_grouped(xq, a_scale, packed, w_scale, out_dtype="f32", out=None):
                                           ctypes.cast(O, ctypes.c_void_p), code, _stream(xq)),
            "bitnet_w2a8_gemm_grouped")
     return outs
+
+
+def gemm_plan(M, K, Ns, cus=0):
+    """Tile plan (block rows, block columns, k-groups, k per stage) of a tiled launch over
+    weight matrices of Ns rows; host-only."""
+    G = len(Ns)
+    NN = (ctypes.c_int64 * max(G, 1))(*[int(n) for n in Ns])
+    out = (ctypes.c_int32 * 4)()
+    _check(lib().bitnet_w2a8_gemm_plan(int(M), int(K), G, ctypes.cast(NN, ctypes.c_void_p),
+                                       int(cus), ctypes.cast(out, ctypes.c_void_p)),
+           "bitnet_w2a8_gemm_plan")
+    return tuple(int(v) for v in out)
 
 
 def quant_gemv(x, packed, w_scale, out_dtype="f32", out=None, return_quant=False):

@@ -216,6 +216,23 @@ int bitnet_w2a8_gemm_grouped(const int8_t* xq, const float* a_scale, int64_t M, 
                                                    out, M, K, out_dtype, as_stream(stream)));
 }
 
+int bitnet_w2a8_gemm_plan(int64_t M, int64_t K, int64_t groups, const int64_t* N, int64_t cus,
+                          int32_t* plan) {
+    if (groups < 1 || groups > BITNET_MAX_GROUPS || !N || !plan || M < 1)
+        return BITNET_ERR_INVALID_ARG;
+    int64_t total_n = 0;
+    for (int64_t g = 0; g < groups; ++g) {
+        int st = check_shape(M, N[g], K);
+        if (st) return st;
+        total_n += N[g];
+    }
+    if (total_n == 0 || total_n > INT32_MAX) return BITNET_ERR_INVALID_ARG;
+    int p[4];
+    bitnet::tiled_plan(M, K, (int)groups, N, cus, p);
+    for (int i = 0; i < 4; ++i) plan[i] = p[i];
+    return BITNET_OK;
+}
+
 int bitnet_quant_gemv(const uint16_t* x, const uint8_t* packed, const float* w_scale,
                       int64_t M, int64_t N, int64_t K, void* out, int out_dtype,
                       int8_t* xq_out, float* a_scale_out, void* stream) {

@@ -65,6 +65,9 @@ size_t tiled_workspace_size(int64_t M, int64_t N, int64_t K);
 // The tiled product for 1 <= groups <= BITNET_MAX_GROUPS weight matrices (N[g] rows
 // each, all K columns) against the same activations, in one launch; the tile plan is
 // chosen for the launch's total tile count.
+// The tile plan of a tiled launch over `groups` matrices of N[g] rows: plan[0..3] = block
+// rows, block columns, k-groups per block, k per LDS stage; cus <= 0: the current device's.
+void tiled_plan(int64_t M, int64_t K, int groups, const int64_t* N, int64_t cus, int* plan);
 hipError_t launch_tiled_grouped(const int8_t* xq, const float* a_scale, int groups,
                                 const uint8_t* const* packed, const float* const* w_scale,
                                 const int64_t* N, void* const* out, int64_t M, int64_t K,

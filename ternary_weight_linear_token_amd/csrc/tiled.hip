@@ -579,13 +579,12 @@ constexpr TileCost kTileCosts[] = {
     {256, 256, 1, 64, 10.5, 11.7e-3},
 };
 
-TilePlan plan_tiles(int64_t M, int64_t K, const int64_t* N, int groups) {
+TilePlan plan_tiles(int64_t M, int64_t K, const int64_t* N, int groups, int64_t cus) {
     TilePlan t;
     if (config_override(&t.bm, &t.bn, &t.g)) {
         t.bk = (K % 128 == 0 && !(t.bm == 256 && t.bn == 256)) ? 128 : 64;
         return t;
     }
-    const int64_t cus = device_cus();
     double best = -1.0;
     for (const TileCost& c : kTileCosts) {
         if (K % c.bk != 0 && c.bk != 64) continue;
@@ -650,6 +649,14 @@ size_t tiled_workspace_size(int64_t M, int64_t N, int64_t K) {
     return 0;
 }
 
+void tiled_plan(int64_t M, int64_t K, int groups, const int64_t* N, int64_t cus, int* plan) {
+    const TilePlan t = plan_tiles(M, K, N, groups, cus > 0 ? cus : device_cus());
+    plan[0] = t.bm;
+    plan[1] = t.bn;
+    plan[2] = t.g;
+    plan[3] = t.bk;
+}
+
 hipError_t launch_tiled_grouped(const int8_t* xq, const float* a_scale, int groups,
                                 const uint8_t* const* packed, const float* const* w_scale,
                                 const int64_t* N, void* const* out, int64_t M, int64_t K,
@@ -671,7 +678,7 @@ hipError_t launch_tiled_grouped(const int8_t* xq, const float* a_scale, int grou
     a.out_dtype = out_dtype;
     int64_t n_all[kTdGroups];
     for (int i = 0; i < kTdGroups; ++i) n_all[i] = i < groups ? N[i] : 0;
-    const TilePlan t = plan_tiles(M, K, n_all, groups);
+    const TilePlan t = plan_tiles(M, K, n_all, groups, device_cus());
     // register sets in flight: 64-k stages 4 (2 for 256x256); 128-k stages 2, or 4 for
     // the 256x128 tile (its accumulators live in the matrix-core registers)
     if (t.bm == 256 && t.bn == 256) return launch_plan<256, 256, 2, 1, 4, 64>(a, n_all, stream);

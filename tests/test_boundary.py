@@ -191,6 +191,76 @@ def test_gemm_grouped_validation(L):
     assert call(A, E, 512, 256, 2, arrs([None, None], [None, None], [0, 0], [None, None])) == OK
 
 
+def test_gemm_plan_validation(L):
+    f = L.bitnet_w2a8_gemm_plan
+    P = ctypes.c_void_p
+    ns = (ctypes.c_int64 * 2)(640, 2560)
+    out = (ctypes.c_int32 * 4)()
+    assert f(512, 2560, 2, ctypes.cast(ns, P), 256, ctypes.cast(out, P)) == OK
+    assert f(0, 2560, 2, ctypes.cast(ns, P), 256, ctypes.cast(out, P)) == INVALID     # M < 1
+    assert f(512, 2560, 0, ctypes.cast(ns, P), 256, ctypes.cast(out, P)) == INVALID   # groups
+    assert f(512, 2560, 5, ctypes.cast(ns, P), 256, ctypes.cast(out, P)) == INVALID
+    assert f(512, 2562, 2, ctypes.cast(ns, P), 256, ctypes.cast(out, P)) == UNALIGNED  # K % 4
+    assert f(512, 2560, 2, None, 256, ctypes.cast(out, P)) == INVALID
+    assert f(512, 2560, 2, ctypes.cast(ns, P), 256, None) == INVALID
+    zero = (ctypes.c_int64 * 2)(0, 0)
+    assert f(512, 2560, 2, ctypes.cast(zero, P), 256, ctypes.cast(out, P)) == INVALID  # no rows
+    neg = (ctypes.c_int64 * 2)(16, -1)
+    assert f(512, 2560, 2, ctypes.cast(neg, P), 256, ctypes.cast(out, P)) == INVALID
+
+
+# (M, K, N per group) -> (block rows, block cols, k-groups, k per stage) on 256 CUs: the
+# launches of the 2B prefill step and the 8B/70B prefill shapes, and the shapes the GPU
+# parity tests use to reach every compiled (tile, k-stage) pair.
+PLAN_CASES = [
+    ((512, 2560, [2560, 640, 640]), (64, 128, 4, 128)),    # 2B q|k|v: 240 tiles, one round
+    ((512, 2560, [2560]), (64, 128, 4, 128)),              # 2B o
+    ((512, 2560, [6912, 6912]), (256, 128, 1, 128)),       # 2B gate|up: 216 tiles, one round
+    ((512, 6912, [2560]), (64, 128, 4, 128)),              # 2B down
+    ((2048, 4096, [14336]), (256, 256, 1, 64)),            # 8B gate: two rounds of 256x256
+    ((2048, 14336, [4096]), (256, 128, 1, 128)),           # 8B down
+    ((1024, 8192, [28672, 28672]), (256, 256, 1, 64)),     # 70B gate|up
+    ((130, 320, [257, 64, 0, 96]), (64, 128, 4, 64)),      # K % 128 != 0: 64-k stages
+    ((512, 2560, [2560, 640, 640]), (64, 128, 4, 128)),
+    ((600, 256, [6912, 6912]), (256, 256, 1, 64)),
+    ((500, 2048, [6000, 7000]), (256, 128, 1, 128)),
+    ((1024, 128, [4096, 1024, 1024, 300]), (256, 128, 1, 64)),
+    ((257, 320, [5000, 4000]), (128, 128, 2, 64)),
+    ((300, 384, [4100, 4100]), (128, 128, 2, 128)),
+]
+
+
+@pytest.mark.parametrize("shape,plan", PLAN_CASES)
+def test_gemm_plan_choices(shape, plan):
+    M, K, Ns = shape
+    assert bw.gemm_plan(M, K, Ns, cus=256) == plan
+
+
+def test_gemm_plan_covers_every_compiled_configuration():
+    # every (tile, k-stage) pair the launcher instantiates is chosen for some shape, and
+    # 128-k stages only when K % 128 == 0
+    seen = set()
+    for M in (17, 130, 300, 512, 1024, 2048):
+        for K in (128, 192, 320, 384, 1024, 2048, 2560, 4096, 6912, 14336):
+            for Ns in ([640], [2560], [6912, 6912], [4096, 1024, 1024], [14336], [28672]):
+                p = bw.gemm_plan(M, K, Ns, cus=256)
+                seen.add(p)
+                if K % 128:
+                    assert p[3] == 64, (M, K, Ns, p)
+    assert seen == {(64, 128, 4, 128), (128, 128, 2, 128), (256, 128, 1, 128),
+                    (64, 128, 4, 64), (128, 128, 2, 64), (256, 128, 1, 64),
+                    (256, 256, 1, 64)}, seen
+
+
+def test_gemm_plan_grids_of_one_round_take_small_tiles():
+    # a grid of 64x128 tiles that fits the CUs in one round is never given larger tiles
+    for M, N in ((64, 4096), (512, 2560), (256, 8192)):
+        assert bw.gemm_plan(M, 2560, [N], cus=256)[:2] == (64, 128)
+    # with fewer CUs the same launch moves to larger tiles
+    assert bw.gemm_plan(512, 2560, [2560], cus=256)[:2] == (64, 128)
+    assert bw.gemm_plan(512, 2560, [13824], cus=64)[:2] != (64, 128)
+
+
 def test_quant_gemv_swiglu_validation(L):
     f = L.bitnet_quant_gemv_swiglu
     assert f(A, B, C, D, E, 1, 16, 256, F, 2, None, None, None) == INVALID   # int32 output
