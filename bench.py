@@ -342,7 +342,8 @@ def bench_extras(bw, workloads, torch, dev, reps):
     out = {}
     print("[bench] 70B-shaped decode set, M=1", file=sys.stderr, flush=True)
     shapes = {name: (N, K) for name, N, K in workloads.LAYER_70B}
-    per, tot_b, tot_us = {}, 0, 0.0
+    from ternary_weight_linear_token_amd import ceilings
+    per, tot_b, tot_us, tot_floor = {}, 0, 0.0, 0.0
     for grp in workloads.DECODE_GROUPS:
         K = shapes[grp[0]][1]
         ps, ss = [], []
@@ -362,15 +363,22 @@ def bench_extras(bw, workloads, torch, dev, reps):
         else:
             launch = lambda r: bw.quant_gemv_grouped(x, copies[r], ss, "f32", out=os_)
         us = graph_launch_us(torch, launch, R, reps)
-        per["|".join(grp)] = {"us": round(us, 3), "GB/s": round(nbytes / us / 1e3, 1)}
+        del copies, ps
+        torch.cuda.empty_cache()
+        floor = ceilings.same_grid_read_us(
+            torch, dev, nbytes, sum((shapes[name][0] + 15) // 16 for name in grp),
+            lambda fn, RR: graph_launch_us(torch, fn, RR, reps))
+        per["|".join(grp)] = {"us": round(us, 3), "GB/s": round(nbytes / us / 1e3, 1),
+                              "same_grid_plain_read_us": round(floor, 3)}
         tot_b += nbytes
         tot_us += us
-        del copies, ps
+        tot_floor += floor
         torch.cuda.empty_cache()
     out["decode_70b_m1"] = {"bound": "hbm", "achieved": round(tot_b / tot_us / 1e3, 1),
                             "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": round(tot_b / tot_us / 1e3 / HBM_PEAK_GBS, 4),
-                            "packed_bytes": tot_b, "per_launch": per}
+                            "packed_bytes": tot_b, "per_launch": per,
+                            "frac_of_same_grid_plain_read": round(tot_floor / tot_us, 4)}
     print("[bench] 8B-shaped prefill MLP, M=2048", file=sys.stderr, flush=True)
     M, per, tot_ops, tot_us = 2048, {}, 0.0, 0.0
     for name, N, K in workloads.LAYER_8B:
@@ -440,7 +448,6 @@ def bench_extras(bw, workloads, torch, dev, reps):
                                "per_shape_us": per}
 
     # what this chip sustains (context for the fractions above)
-    from ternary_weight_linear_token_amd import ceilings
     print("[bench] ceilings", file=sys.stderr, flush=True)
     mfma = ceilings.mfma_i8_tops(torch, dev)
     read = ceilings.hbm_read_gbs(torch, dev)
