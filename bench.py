@@ -56,6 +56,7 @@ INT8_MFMA_PEAK_TOPS = 5000.0  # MI355X dense int8 matrix cores, TOPS
 ROTATE_BYTES = 1 << 30        # weight copies per rotation (> 4x the 256 MB MALL)
 METRIC = "W2A8 ternary GEMV GB/s (%HBM peak) at M=1; GEMM int8 TOPS (%MFMA) at M=512"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "quant_gemv_2b_decode_m1_traffic.txt")
+GEMM_COUNTERS_FILE = os.path.join(ROOT, "profiles", "tiled_gemm_2b_prefill_m512_counters.txt")
 
 
 def parse():
@@ -70,7 +71,22 @@ def parse():
                     help="skip the 70B-shaped decode and 8B-shaped prefill rooflines")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run the counter-collection launch pattern and exit (no timing)")
+    ap.add_argument("--gemm-probe", action="store_true",
+                    help="run the prefill GEMM launches for counter collection and exit")
     return ap.parse_args()
+
+
+def load_summary(path: str, kernel_hash: str):
+    """key = value lines of a committed counter summary, if its kernel hash still applies."""
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                vals[k.strip()] = v.strip()
+    return vals if vals.get("kernel_source_sha256") == kernel_hash else None
 
 
 def load_traffic(kernel_hash: str):
@@ -145,6 +161,10 @@ def main():
 
     if args.traffic_probe:
         traffic_probe(torch, launch_set, R, dev)
+        return
+    if args.gemm_probe:
+        bench_gemm(bw, workloads, torch, np, dev, layer, R_bytes=ROTATE_BYTES,
+                   reps=args.kernel_reps, probe=True)
         return
 
     # Steps are captured STEPS_PER_GRAPH at a time, each on the next weight copy, so the
@@ -464,7 +484,7 @@ def bench_extras(bw, workloads, torch, dev, reps):
     return out
 
 
-def bench_gemm(bw, workloads, torch, np, dev, layer, R_bytes, reps):
+def bench_gemm(bw, workloads, torch, np, dev, layer, R_bytes, reps, probe=False):
     M = 512
     print(f"[bench] prefill M={M}", file=sys.stderr, flush=True)
     packed0, scales, xs, xqs, avs, outs = [], [], [], [], [], []
@@ -500,6 +520,24 @@ def bench_gemm(bw, workloads, torch, np, dev, layer, R_bytes, reps):
             bw.quant_act(xs[i0], xq=xqs[i0], a_scale=avs[i0])
             grouped(r, grp)
 
+    if probe:
+        # counter collection: the calibration copies of the traffic probe, then the four
+        # grouped GEMM launches once per weight copy (weights from HBM), eagerly
+        from ternary_weight_linear_token_amd import profiling
+        n = profiling.COPY_BYTES // 4
+        src = torch.arange(n, dtype=torch.int32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+        for r in range(R):
+            for grp in groups:
+                grouped(r, grp)
+        torch.cuda.synchronize()
+        print(f"[bench] gemm probe: {R} prefill steps", file=sys.stderr)
+        return None
+
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -524,6 +562,8 @@ def bench_gemm(bw, workloads, torch, np, dev, layer, R_bytes, reps):
         K = shapes[grp[0]][1]
         t = ceilings.vendor_int8_gemm_tops(torch, dev, M, N, K)
         vendor_us = None if (t is None or vendor_us is None) else vendor_us + 2.0 * M * N * K / t / 1e6
+    from ternary_weight_linear_token_amd import build as bw_build
+    counters = load_summary(GEMM_COUNTERS_FILE, bw_build.kernel_hash("tiled.hip"))
     return {
         "metric": "GEMM int8 TOPS at M=512 (prefill layer set, bf16 out)",
         "workload": "bitnet-2b-prefill-layer-set",
@@ -543,7 +583,9 @@ def bench_gemm(bw, workloads, torch, np, dev, layer, R_bytes, reps):
             "peak": INT8_MFMA_PEAK_TOPS,
             "unit": "TFLOP/s",
             "frac": round(tops / INT8_MFMA_PEAK_TOPS, 4),
-            "traffic": None,
+            "traffic": float(counters["hbm_bytes_per_launch"]) if counters else None,
+            "mfma_busy_frac_counters": (float(counters["mfma_busy_frac_weighted"])
+                                        if counters else None),
             "kernel": "tiled_kernel (tile plan per launch)",
             "per_launch_us": {"|".join(grp): round(us, 3)
                               for grp, us in zip(workloads.DECODE_GROUPS, per_group_us)},

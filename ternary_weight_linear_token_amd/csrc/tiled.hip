@@ -39,6 +39,7 @@
 //  * Grouped launches: up to BITNET_MAX_GROUPS weight matrices that read the same
 //    activations (q, k, v; gate, up) share one grid; a block finds its matrix by scalar
 //    compares of its work unit against the groups' first units.
+#include <cmath>
 #include <cstdio>
 #include <cstdlib>
 #include <type_traits>
@@ -70,6 +71,7 @@ struct TiledArgs {
     int M, K;
     int units;       // tiles of all groups
     int units_per_xcd;
+    int gm;          // tile rows per panel of the unit order (see the kernel)
     int out_dtype;
 };
 
@@ -121,9 +123,17 @@ __global__ __launch_bounds__(kTdThreads * G) void tiled_kernel(TiledArgs p) {
             out = p.g_out[i];
         }
     }
+    // A group's tiles are ordered in panels of gm tile rows, column by column inside a
+    // panel, so the run of consecutive units one XCD takes is a block of about gm x
+    // (run / gm) tiles: its L2 holds gm activation row panels and run / gm weight column
+    // panels instead of one row panel and every column panel.
     const int tile = unit - first;
-    const int tile_m = tile / tiles_n;
-    const int tile_n = tile - tile_m * tiles_n;
+    const int tiles_m = (p.M + BM - 1) / BM;
+    const int panel = tile / (p.gm * tiles_n);
+    const int rem = tile - panel * p.gm * tiles_n;
+    const int pm = min(p.gm, tiles_m - panel * p.gm);  // rows of this (possibly last) panel
+    const int tile_m = panel * p.gm + rem % pm;
+    const int tile_n = rem / pm;
     const int m0 = tile_m * BM, n0 = tile_n * BN;
 
     // G groups of four waves; group g takes the k-stages g, g + G, g + 2G, ... of the
@@ -617,6 +627,11 @@ hipError_t launch_plan(TiledArgs a, const int64_t* N, hipStream_t stream) {
     a.units = units;
     if (units == 0) return hipSuccess;
     a.units_per_xcd = (a.units + kXcds - 1) / kXcds;
+    // panel height: an XCD's run of units_per_xcd tiles as gm rows by units_per_xcd / gm
+    // columns reads gm * BM * K activation bytes and (units_per_xcd / gm) * BN * K / 4
+    // weight bytes, least at gm = sqrt(units_per_xcd * BN / (4 BM))
+    a.gm = (int)(std::sqrt((double)a.units_per_xcd * BN / (4.0 * BM)) + 0.5);
+    a.gm = a.gm < 1 ? 1 : (a.gm > tiles_m ? tiles_m : a.gm);
     const dim3 grid((unsigned)(a.units_per_xcd * kXcds));
     const dim3 blk(kTdThreads * G);
     if constexpr (BK == 128) {

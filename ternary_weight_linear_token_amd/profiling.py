@@ -10,6 +10,13 @@ one with FETCH_SIZE and one with WRITE_SIZE):
     python -m ternary_weight_linear_token_amd.profiling traffic --fetch DIR1 --write DIR2 \
         --out FILE --cmd "..."
 
+Matrix-core use and HBM traffic of the prefill GEMM (three `rocprofv3 --pmc` runs of
+`bench.py --gemm-probe`: SQ_INSTS_VALU_MFMA_MOPS_I8 SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU
+SQ_INSTS_MFMA GRBM_GUI_ACTIVE, then FETCH_SIZE, then WRITE_SIZE):
+
+    python -m ternary_weight_linear_token_amd.profiling gemm --util DIR0 --fetch DIR1 \
+        --write DIR2 --out FILE --cmd "..."
+
 FETCH_SIZE and WRITE_SIZE read in KiB per dispatch.  They are scaled by what the same
 counters read for a plain elementwise kernel of known size that the probe runs first (it
 reads and writes COPY_BYTES each), so the reported bytes are in the units of that copy.
@@ -147,6 +154,85 @@ def traffic(fetch_dir: str, write_dir: str, out: str, cmd: str, source_hash: str
     return text
 
 
+SIMDS = 256 * 4  # MI355X: 256 CUs of 4 SIMDs
+XCDS = 8         # GRBM_GUI_ACTIVE is counted per XCD; the summary sums the eight
+
+
+def gemm(util_dir: str, fetch_dir: str, write_dir: str, out: str, cmd: str, source_hash: str,
+         launches) -> str:
+    """Matrix-core use and HBM traffic of the tiled GEMM launches of `bench.py --gemm-probe`.
+
+    launches: [(name, M, N, K)] of one prefill step, in launch order.  Per launch shape
+    (grid): int8 operations counted by the matrix cores (SQ_INSTS_VALU_MFMA_MOPS_I8 x 512)
+    against 2 M N K, matrix-core busy fraction (SQ_VALU_MFMA_BUSY_CYCLES over all SIMDs
+    / (GRBM_GUI_ACTIVE per XCD x SIMDs); the dispatch's active cycles include what the
+    counter collection adds around it, so this reads low against the unprofiled rate),
+    VALU instructions per matrix product, and calibrated HBM bytes."""
+    mops = _per_dispatch(_counter_rows(util_dir, "SQ_INSTS_VALU_MFMA_MOPS_I8"))
+    busy = _per_dispatch(_counter_rows(util_dir, "SQ_VALU_MFMA_BUSY_CYCLES"))
+    valu = _per_dispatch(_counter_rows(util_dir, "SQ_INSTS_VALU"))
+    mfma = _per_dispatch(_counter_rows(util_dir, "SQ_INSTS_MFMA"))
+    gui = _per_dispatch(_counter_rows(util_dir, "GRBM_GUI_ACTIVE"))
+    fetch = _per_dispatch(_counter_rows(fetch_dir, "FETCH_SIZE"))
+    write = _per_dispatch(_counter_rows(write_dir, "WRITE_SIZE"))
+
+    def calib(table):
+        vals = [v for n, g, v in table.values()
+                if COPY_KERNEL in n and COPY_TAG in n and "bitnet" not in n]
+        if not vals:
+            raise RuntimeError("the calibration copy was not found in the counter output")
+        vals = vals[1:] if len(vals) > 1 else vals
+        return COPY_BYTES / (statistics.median(vals) * 1024.0)
+
+    f_fetch, f_write = calib(fetch), calib(write)
+
+    def tiled(table, scale=1.0):
+        """dispatches of the tiled kernel in launch order: [(name, grid, value)]"""
+        rows = [(int(k), n, g, v * scale) for k, (n, g, v) in table.items() if "tiled_kernel" in n]
+        return [r[1:] for r in sorted(rows)]
+
+    t_mops, t_busy, t_valu, t_mfma, t_gui = (tiled(mops), tiled(busy), tiled(valu), tiled(mfma),
+                                             tiled(gui, 1.0 / XCDS))
+    t_fetch, t_write = tiled(fetch, 1024.0 * f_fetch), tiled(write, 1024.0 * f_write)
+    nl = len(launches)
+    if len(t_mops) % nl or len(t_fetch) % nl or len(t_write) % nl:
+        raise RuntimeError("the tiled dispatches are not whole prefill steps")
+    lines = ["# Matrix-core use and HBM traffic of the tiled GEMM, BitNet-2B prefill set at "
+             "M = 512 (four grouped launches)",
+             f"# command: {cmd}",
+             f"# calibration: FETCH_SIZE reads {1 / f_fetch:.4f}x, WRITE_SIZE "
+             f"{1 / f_write:.4f}x of a {COPY_BYTES}-byte copy",
+             "# per launch: kernel, steps, int8 ops counted / 2MNK, matrix-core busy, VALU per "
+             "product, HBM read MB, HBM write MB, algorithmic MB (packed weights + int8 "
+             "activations + bf16 out)"]
+    tot_busy_w, tot_gui, tot_bytes, tot_alg = 0.0, 0.0, 0.0, 0.0
+    for i, (name, M, N, K) in enumerate(launches):
+        sel = lambda t: [v for j, (_, _, v) in enumerate(t) if j % nl == i]
+        kern = _short(t_mops[i][0])
+        ops = statistics.mean(sel(t_mops)) * 512
+        b = statistics.mean(sel(t_busy))
+        gcy = statistics.mean(sel(t_gui))
+        vpm = statistics.mean(sel(t_valu)) / max(1.0, statistics.mean(sel(t_mfma)))
+        rd, wr = statistics.mean(sel(t_fetch)), statistics.mean(sel(t_write))
+        alg = N * K / 4 + M * K + 2 * M * N
+        lines.append(f"#   {name:8s} {kern[:44]:44s} {len(sel(t_mops)):3d} "
+                     f"{ops / (2.0 * M * N * K):6.3f} {b / (gcy * SIMDS):6.3f} {vpm:6.2f} "
+                     f"{rd / 1e6:8.2f} {wr / 1e6:7.2f} {alg / 1e6:7.2f}")
+        tot_busy_w += b
+        tot_gui += gcy
+        tot_bytes += rd + wr
+        tot_alg += alg
+    lines += [f"kernel_source_sha256 = {source_hash}",
+              f"mfma_busy_frac_weighted = {tot_busy_w / (tot_gui * SIMDS):.4f}",
+              f"hbm_bytes_per_launch = {tot_bytes / nl:.0f}",
+              f"algorithmic_bytes_per_launch = {tot_alg / nl:.0f}",
+              f"traffic_over_algorithmic = {tot_bytes / tot_alg:.4f}"]
+    text = "\n".join(lines) + "\n"
+    with open(out, "w") as f:
+        f.write(text)
+    return text
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(prog="python -m ternary_weight_linear_token_amd.profiling")
     sub = ap.add_subparsers(dest="what", required=True)
@@ -159,9 +245,24 @@ def main(argv=None):
     t.add_argument("--write", required=True)
     t.add_argument("--out", required=True)
     t.add_argument("--cmd", required=True)
+    gm = sub.add_parser("gemm")
+    gm.add_argument("--util", required=True)
+    gm.add_argument("--fetch", required=True)
+    gm.add_argument("--write", required=True)
+    gm.add_argument("--out", required=True)
+    gm.add_argument("--cmd", required=True)
     a = ap.parse_args(argv)
     if a.what == "kernels":
         sys.stdout.write(kernels(a.dir, a.out, a.cmd))
+    elif a.what == "gemm":
+        from . import build
+        sys.path.insert(0, build.ROOT)
+        import workloads
+        shapes = {name: (N, K) for name, N, K in workloads.LAYER_2B}
+        launches = [("|".join(g), 512, sum(shapes[n][0] for n in g), shapes[g[0]][1])
+                    for g in workloads.DECODE_GROUPS]
+        sys.stdout.write(gemm(a.util, a.fetch, a.write, a.out, a.cmd,
+                              build.kernel_hash("tiled.hip"), launches))
     else:
         from . import build
         sys.path.insert(0, build.ROOT)
