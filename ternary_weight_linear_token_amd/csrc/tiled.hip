@@ -95,7 +95,7 @@ __global__ __launch_bounds__(kTdThreads * G) void tiled_kernel(TiledArgs p) {
     // combine of the groups' accumulators and the per-wave epilogue scratch
     constexpr int kStageBytes = G * 2 * BM * kAStride;
     constexpr int kGroupAccBytes = 4 * MB * NB * 16 * 64 * 4;  // one group's accumulators
-    constexpr int kRedBytes = G == 4 ? 2 * kGroupAccBytes : (G == 2 ? kGroupAccBytes / 2 : 0);
+    constexpr int kRedBytes = G == 4 ? 4 * kGroupAccBytes : (G == 2 ? kGroupAccBytes / 2 : 0);
     constexpr int kEpiBytes = (G == 1 ? 1 : 2) * 4 * 32 * 36 * 4;
     constexpr int kLdsBytes = kStageBytes > kRedBytes ? (kStageBytes > kEpiBytes ? kStageBytes : kEpiBytes)
                                                       : (kRedBytes > kEpiBytes ? kRedBytes : kEpiBytes);
@@ -432,34 +432,45 @@ __global__ __launch_bounds__(kTdThreads * G) void tiled_kernel(TiledArgs p) {
 
     // every k-stage ended with a barrier: the A buffers are free for the epilogue scratch
     if constexpr (G == 4) {
-        // ---- groups 2 and 3 hand their accumulators to groups 0 and 1 ----
-        int* red4 = reinterpret_cast<int*>(smem);
-        auto slot4 = [&](int gg, int i, int j, int r) {
-            return ((((gg * 4 + wave) * MB + i) * NB + j) * 16 + r) * 64 + lane;
+        // ---- one pass: every group's partial sums go to LDS, then group g adds up, over
+        // the four groups, the quarter of the tile it owns -- accumulator block g / 2,
+        // registers 8 (g % 2) .. +7, i.e. rows 16 (g % 2) .. +15 of that block -- and
+        // writes it straight from the accumulator layout (lane l: column l % 32) ----
+        static_assert(MB == 2 && NB == 1, "one accumulator quarter per k-group");
+        int* part = reinterpret_cast<int*>(smem);
+        auto slot = [&](int gg, int i, int r) {
+            return (((gg * 4 + wave) * MB + i) * 16 + r) * 64 + lane;
         };
-        if (g >= 2) {
 #pragma unroll
-            for (int i = 0; i < MB; ++i)
+        for (int i = 0; i < MB; ++i)
 #pragma unroll
-                for (int j = 0; j < NB; ++j)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) red4[slot4(g - 2, i, j, r)] = acc[i][j][r];
-        }
+            for (int r = 0; r < 16; ++r) part[slot(g, i, r)] = acc[i][0][r];
         __syncthreads();
-        if (g < 2) {
+        const int io = g >> 1, ho = g & 1;
+        int v[8];
 #pragma unroll
-            for (int i = 0; i < MB; ++i)
+        for (int t = 0; t < 8; ++t) {
+            int sum = 0;
 #pragma unroll
-                for (int j = 0; j < NB; ++j)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[i][j][r] += red4[slot4(g, i, j, r)];
+            for (int gg = 0; gg < 4; ++gg) sum += part[slot(gg, io, 8 * ho + t)];
+            v[t] = sum;
         }
-        __syncthreads();
+        const int nb = n0 + wn * WN + l32;
+        if (nb < N) {
+            const float ws = DT == 2 ? 0.0f : w_scale[nb];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const int r = 8 * ho + t;
+                const int ml = wm * WM + 32 * io + 8 * (r >> 2) + 4 * q + (r & 3);
+                if (m0 + ml < M)
+                    store_out(out, (int64_t)(m0 + ml) * N + nb, DT, v[t], ws, s_inva[ml]);
+            }
+        }
+        return;
     }
-    if constexpr (G >= 2) {
+    if constexpr (G == 2) {
         // ---- combine groups 0 and 1: group 0 ends up owning accumulator rows blocks
-        // i < MB/2, group 1 the others; each half goes through LDS in its own phase
-        // (groups 2 and 3, already folded in, only take part in the barriers) ----
+        // i < MB/2, group 1 the others; each half goes through LDS in its own phase ----
         constexpr int H = MB / 2;
         int* red = reinterpret_cast<int*>(smem);
         auto slot = [&](int ih, int j, int r) { return (((wave * H + ih) * NB + j) * 16 + r) * 64 + lane; };
@@ -499,7 +510,6 @@ __global__ __launch_bounds__(kTdThreads * G) void tiled_kernel(TiledArgs p) {
                     for (int r = 0; r < 16; ++r) acc[H + ih][j][r] += red[slot(ih, j, r)];
         }
         __syncthreads();  // red is reused as epilogue scratch below
-        if (g >= 2) return;
 #pragma unroll
         for (int ih = 0; ih < H; ++ih)
 #pragma unroll
