@@ -169,7 +169,8 @@ int bitnet_w2a8_gemm(const int8_t* xq, const float* a_scale, const uint8_t* pack
     // Auto: the weight-streaming kernels while the product is small enough that one
     // round of their blocks beats the tiled kernel (whose single-round grids cost about
     // the same for any M up to 64): always up to 4 tokens, up to 16 while the weights
-    // are at most 16 MB, and the staged kernel's token tiles up to 32 while M * N is small.
+    // are at most 16 MB, the direct kernel up to 32 tokens while N * K <= 2^25, and the
+    // staged kernel's token tiles up to 32 while M * N is small.
     if (algo == BITNET_ALGO_SKINNY)
         return record_hip(bitnet::launch_skinny(xq, a_scale, nullptr, packed, w_scale, M, N, K,
                                                 out, out_dtype, nullptr, nullptr,
@@ -178,6 +179,12 @@ int bitnet_w2a8_gemm(const int8_t* xq, const float* a_scale, const uint8_t* pack
         if (M <= 4 || (M <= 16 && N * K <= ((int64_t)1 << 26)))
             return record_hip(launch_small_m(xq, a_scale, packed, w_scale, M, N, K, out,
                                              out_dtype, as_stream(stream)));
+        // 17 to 32 tokens: the direct kernel's two token tiles while the activations it
+        // re-reads per 16-row block (M * K bytes each) stay cheap next to the weights
+        if (M <= 32 && K % 64 == 0 && N * K <= ((int64_t)1 << 25))
+            return record_hip(bitnet::launch_gemv_direct(xq, a_scale, nullptr, packed, w_scale,
+                                                         M, N, K, out, out_dtype, nullptr,
+                                                         nullptr, as_stream(stream)));
         if (M <= 32 && M * N <= 131072)
             return record_hip(bitnet::launch_skinny(xq, a_scale, nullptr, packed, w_scale, M, N,
                                                     K, out, out_dtype, nullptr, nullptr,

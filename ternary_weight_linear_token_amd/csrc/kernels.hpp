@@ -51,9 +51,10 @@ hipError_t launch_skinny_swiglu(const uint16_t* x_bf16, const uint8_t* packed_ga
 hipError_t launch_a16(const uint16_t* x, const uint8_t* packed, const float* w_scale, int64_t M,
                       int64_t N, int64_t K, void* out, int out_dtype, hipStream_t stream);
 
-// Product for 1 <= M <= 16 with the activations read straight into matrix-core operands;
-// K % 64 == 0.  With x_bf16 non-null the activations are quantized in the kernel (xq /
-// a_scale ignored; xq_out / a_out optional copies), else int8 codes xq + a_scale.
+// Product for 1 <= M <= 32 (16 with x_bf16) with the activations read straight into
+// matrix-core operands; K % 64 == 0.  With x_bf16 non-null the activations are quantized
+// in the kernel (xq / a_scale ignored; xq_out / a_out optional copies), else int8 codes
+// xq + a_scale.
 hipError_t launch_gemv_direct(const int8_t* xq, const float* a_scale, const uint16_t* x_bf16,
                               const uint8_t* packed, const float* w_scale, int64_t M, int64_t N,
                               int64_t K, void* out, int out_dtype, int8_t* xq_out, float* a_out,

@@ -189,6 +189,18 @@ def test_gemm_matches_oracle(algo, M, N, K):
         check_out(to_np(out), o["acc"], o["ref"], dt, f"gemm {algo} M={M} N={N} K={K} {dt}")
 
 
+@pytest.mark.parametrize("M", [17, 24, 31, 32])
+@pytest.mark.parametrize("N,K", [(37, 320), (300, 1024), (129, 6912), (2560, 2560), (64, 64)])
+def test_auto_product_for_17_to_32_tokens(M, N, K):
+    """17 to 32 tokens through ALGO_AUTO (the direct kernel's two token tiles when K % 64
+    == 0): every output dtype against the oracle."""
+    pb = Problem(M, N, K, seed=M * 7000 + N + K)
+    xq, a, packed, s, o = product_inputs(pb)
+    for dt in DT:
+        out = bw.gemm(xq, a, packed, s, dt, algo="auto")
+        check_out(to_np(out), o["acc"], o["ref"], dt, f"auto M={M} N={N} K={K} {dt}")
+
+
 @pytest.mark.parametrize("M", [17, 31, 32, 33, 48, 64])
 @pytest.mark.parametrize("N,K", [(37, 260), (300, 1024), (129, 6912), (16, 8448)])
 def test_skinny_token_tiles_match_oracle(M, N, K):
