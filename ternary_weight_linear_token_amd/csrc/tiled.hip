@@ -21,11 +21,11 @@
 //    matrix cores.
 //  * Operand A (activations) goes through LDS (double-buffered, one barrier per stage)
 //    with every aligned 16-byte k-group transposed as a 4x4 byte matrix (position
-//    4 r + b holds k = 4 b + r); rows padded to 80 bytes so the 128-bit fragment reads
-//    are conflict-free.
+//    4 r + b holds k = 4 b + r); rows padded by 16 bytes (80 or 144) so the 128-bit
+//    fragment reads are conflict-free.
 //  * Operand B (packed weights, 4x fewer bytes than int8) is loaded straight into the
-//    registers of the waves that use it, 8 bytes (two 16-weight groups) per lane per
-//    32 columns, and unpacked there: field i of each byte is masked out and mapped by a
+//    registers of the waves that use it, 8 or 16 bytes (two or four 16-weight groups)
+//    per lane per 32 columns and stage, and unpacked there: field i of each byte is masked out and mapped by a
 //    v_perm byte lookup to the signed weight (c - 1), so register i, byte b holds weight
 //    k = 4 b + i -- the same k-order as operand A.
 //  * No split across blocks: handing int32 partial tiles between blocks needs
@@ -33,9 +33,10 @@
 //    the split saves.  Small grids instead split K inside the block: 128x128 blocks of
 //    two four-wave k-groups and 64x128 blocks of four (alternate k-stages, accumulators
 //    combined through LDS), so each SIMD interleaves two or four waves.  The tile shape
-//    of a launch is the one with the least estimated time (plan_tiles).
+//    and k-stage of a launch are the ones with the least estimated time (plan_tiles).
 //  * Blocks are mapped to work units XCD by XCD (dispatch assigns consecutive blocks to
-//    the 8 XCDs in turn), so an XCD's L2 sees consecutive tiles of the same row panel.
+//    the 8 XCDs in turn), and units are ordered in panels of tile rows, so an XCD's L2
+//    holds a few activation row panels and a few weight column panels.
 //  * Grouped launches: up to BITNET_MAX_GROUPS weight matrices that read the same
 //    activations (q, k, v; gate, up) share one grid; a block finds its matrix by scalar
 //    compares of its work unit against the groups' first units.
