@@ -107,51 +107,72 @@ __global__ __launch_bounds__(256) void unpack_kernel(const uint8_t* __restrict__
 
 // ------------------------------------------------------- activation quantization ---
 // One 256-thread block per token row.  Pass 1: max |x| as the integer max of the bf16
-// magnitude bits (monotone in |x| for finite values), 4 elements (8 bytes) per load.
-// Pass 2: a = 127 / max(amax, 1e-5) (IEEE division), q = clamp(rne(x * a), +-127).
-// Rows up to G*1024 elements keep their loads in registers between the passes; longer
-// rows (G == 0) read the row twice.
+// magnitude bits (monotone in |x| for finite values), V = 8 elements (16 bytes) per load
+// when K % 8 == 0, else 4 (8 bytes).  Pass 2: a = 127 / max(amax, 1e-5) (IEEE division),
+// q = clamp(rne(x * a), +-127).  Rows up to G * 256 * V elements keep their loads in
+// registers between the passes; longer rows (G == 0) read the row twice.
 // MODE 0: per-token scale (both passes).  Per-tensor scale, three launches: MODE 1 runs
 // pass 1 only and leaves the row's max magnitude bits in a_scale[m]; tensor_scale_kernel
 // reduces them and writes the common scale to every a_scale[m]; MODE 2 runs pass 2 with
 // the scale read from a_scale[m].
-template <int G, int MODE = 0>
+template <int V>
+struct QVec {
+    uint32_t w[V / 2];  // V bf16 values, two per word, low half first
+};
+
+template <int V>
+__device__ __forceinline__ QVec<V> load_qvec(const uint16_t* row, int64_t g) {
+    QVec<V> v;
+    if constexpr (V == 8) {
+        const uint4 t = reinterpret_cast<const uint4*>(row)[g];
+        v.w[0] = t.x; v.w[1] = t.y; v.w[2] = t.z; v.w[3] = t.w;
+    } else {
+        const uint2 t = reinterpret_cast<const uint2*>(row)[g];
+        v.w[0] = t.x; v.w[1] = t.y;
+    }
+    return v;
+}
+
+template <int V>
+__device__ __forceinline__ uint32_t qvec_max_bits(const QVec<V>& v, uint32_t mx) {
+#pragma unroll
+    for (int i = 0; i < V / 2; ++i) {
+        const uint32_t a = v.w[i] & 0x7FFF7FFFu;
+        mx = max(mx, max(a & 0xFFFFu, a >> 16));
+    }
+    return mx;
+}
+
+template <int G, int MODE, int V>
 __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restrict__ x,
                                                         int64_t K, int8_t* __restrict__ xq,
                                                         float* __restrict__ a_scale) {
+    static_assert(V == 4 || V == 8, "elements per load");
     __shared__ uint32_t s_max[4];
     const int64_t m = blockIdx.x;
     const int tid = threadIdx.x;
-    const int64_t groups = K / 4;
-    const uint2* row = reinterpret_cast<const uint2*>(x + m * K);
+    const int64_t groups = K / V;
+    const uint16_t* row = x + m * K;
 
-    uint2 held[G > 0 ? G : 1];
+    QVec<V> held[G > 0 ? G : 1];
     uint32_t mx = 0;
-    if (MODE == 2) {
-        if (G > 0) {
+    if (G > 0) {
 #pragma unroll
-            for (int i = 0; i < G; ++i) {
-                int64_t g = tid + (int64_t)i * 256;
-                held[i] = g < groups ? row[g] : make_uint2(0u, 0u);
+        for (int i = 0; i < G; ++i) {
+            const int64_t g = tid + (int64_t)i * 256;
+            if (g < groups) {
+                held[i] = load_qvec<V>(row, g);
+            } else {
+#pragma unroll
+                for (int t = 0; t < V / 2; ++t) held[i].w[t] = 0u;
             }
         }
-    } else if (G > 0) {
+        if (MODE != 2) {
 #pragma unroll
-        for (int i = 0; i < G; ++i) {
-            int64_t g = tid + (int64_t)i * 256;
-            held[i] = g < groups ? row[g] : make_uint2(0u, 0u);
+            for (int i = 0; i < G; ++i) mx = qvec_max_bits<V>(held[i], mx);
         }
-#pragma unroll
-        for (int i = 0; i < G; ++i) {
-            uint32_t a = held[i].x & 0x7FFF7FFFu, b = held[i].y & 0x7FFF7FFFu;
-            mx = max(mx, max(max(a & 0xFFFFu, a >> 16), max(b & 0xFFFFu, b >> 16)));
-        }
-    } else {
-        for (int64_t g = tid; g < groups; g += 256) {
-            uint2 v = row[g];
-            uint32_t a = v.x & 0x7FFF7FFFu, b = v.y & 0x7FFF7FFFu;
-            mx = max(mx, max(max(a & 0xFFFFu, a >> 16), max(b & 0xFFFFu, b >> 16)));
-        }
+    } else if (MODE != 2) {
+        for (int64_t g = tid; g < groups; g += 256) mx = qvec_max_bits<V>(load_qvec<V>(row, g), mx);
     }
     float a;
     if constexpr (MODE == 2) {
@@ -171,26 +192,44 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restri
         if (tid == 0) a_scale[m] = a;
     }
 
-    uint32_t* orow = reinterpret_cast<uint32_t*>(xq + m * K);
-    auto quant4 = [&](uint2 v) -> uint32_t {
-        const uint32_t h[4] = {v.x & 0xFFFFu, v.x >> 16, v.y & 0xFFFFu, v.y >> 16};
-        uint32_t packed = 0;
+    // V codes per group: one word (V = 4) or two (V = 8)
+    auto quantv = [&](const QVec<V>& v, uint32_t (&packed)[V / 4]) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            float r = rintf(bf16_bits_to_f32(h[j]) * a);
-            r = fminf(fmaxf(r, -127.0f), 127.0f);
-            packed |= ((uint32_t)(int)r & 0xFFu) << (8 * j);
+        for (int w = 0; w < V / 4; ++w) {
+            const uint32_t h[4] = {v.w[2 * w] & 0xFFFFu, v.w[2 * w] >> 16, v.w[2 * w + 1] & 0xFFFFu,
+                                   v.w[2 * w + 1] >> 16};
+            uint32_t p = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float r = rintf(bf16_bits_to_f32(h[j]) * a);
+                r = fminf(fmaxf(r, -127.0f), 127.0f);
+                p |= ((uint32_t)(int)r & 0xFFu) << (8 * j);
+            }
+            packed[w] = p;
         }
-        return packed;
+    };
+    auto store = [&](int64_t g, const uint32_t (&packed)[V / 4]) {
+        if constexpr (V == 8)
+            reinterpret_cast<uint2*>(xq + m * K)[g] = make_uint2(packed[0], packed[1]);
+        else
+            reinterpret_cast<uint32_t*>(xq + m * K)[g] = packed[0];
     };
     if (G > 0) {
 #pragma unroll
         for (int i = 0; i < G; ++i) {
-            int64_t g = tid + (int64_t)i * 256;
-            if (g < groups) orow[g] = quant4(held[i]);
+            const int64_t g = tid + (int64_t)i * 256;
+            if (g < groups) {
+                uint32_t packed[V / 4];
+                quantv(held[i], packed);
+                store(g, packed);
+            }
         }
     } else {
-        for (int64_t g = tid; g < groups; g += 256) orow[g] = quant4(row[g]);
+        for (int64_t g = tid; g < groups; g += 256) {
+            uint32_t packed[V / 4];
+            quantv(load_qvec<V>(row, g), packed);
+            store(g, packed);
+        }
     }
 }
 
@@ -275,27 +314,33 @@ hipError_t launch_unpack_weights(const uint8_t* packed, int64_t N, int64_t K, in
     return hipGetLastError();
 }
 
-template <int MODE>
-hipError_t launch_quant_rows(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float* a_scale,
-                             hipStream_t stream) {
-    const int64_t groups = K / 4;
+template <int MODE, int V>
+hipError_t launch_quant_rows_v(const uint16_t* x, int64_t M, int64_t K, int8_t* xq,
+                               float* a_scale, hipStream_t stream) {
+    const int64_t groups = K / V;
     const int64_t per_thread = (groups + 255) / 256;
     dim3 grid((unsigned)M), blk(256);
     if (per_thread <= 1)
-        hipLaunchKernelGGL((quant_act_kernel<1, MODE>), grid, blk, 0, stream, x, K, xq, a_scale);
+        hipLaunchKernelGGL((quant_act_kernel<1, MODE, V>), grid, blk, 0, stream, x, K, xq, a_scale);
     else if (per_thread <= 2)
-        hipLaunchKernelGGL((quant_act_kernel<2, MODE>), grid, blk, 0, stream, x, K, xq, a_scale);
+        hipLaunchKernelGGL((quant_act_kernel<2, MODE, V>), grid, blk, 0, stream, x, K, xq, a_scale);
     else if (per_thread <= 4)
-        hipLaunchKernelGGL((quant_act_kernel<4, MODE>), grid, blk, 0, stream, x, K, xq, a_scale);
+        hipLaunchKernelGGL((quant_act_kernel<4, MODE, V>), grid, blk, 0, stream, x, K, xq, a_scale);
     else if (per_thread <= 8)
-        hipLaunchKernelGGL((quant_act_kernel<8, MODE>), grid, blk, 0, stream, x, K, xq, a_scale);
+        hipLaunchKernelGGL((quant_act_kernel<8, MODE, V>), grid, blk, 0, stream, x, K, xq, a_scale);
     else if (per_thread <= 16)
-        hipLaunchKernelGGL((quant_act_kernel<16, MODE>), grid, blk, 0, stream, x, K, xq, a_scale);
-    else if (per_thread <= 32)
-        hipLaunchKernelGGL((quant_act_kernel<32, MODE>), grid, blk, 0, stream, x, K, xq, a_scale);
+        hipLaunchKernelGGL((quant_act_kernel<16, MODE, V>), grid, blk, 0, stream, x, K, xq, a_scale);
     else
-        hipLaunchKernelGGL((quant_act_kernel<0, MODE>), grid, blk, 0, stream, x, K, xq, a_scale);
+        hipLaunchKernelGGL((quant_act_kernel<0, MODE, V>), grid, blk, 0, stream, x, K, xq, a_scale);
     return hipGetLastError();
+}
+
+// 16-byte loads when rows are whole 8-element groups (K % 8 == 0), else 8-byte ones
+template <int MODE>
+hipError_t launch_quant_rows(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float* a_scale,
+                             hipStream_t stream) {
+    if (K % 8 == 0) return launch_quant_rows_v<MODE, 8>(x, M, K, xq, a_scale, stream);
+    return launch_quant_rows_v<MODE, 4>(x, M, K, xq, a_scale, stream);
 }
 
 hipError_t launch_quant_act(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float* a_scale,
