@@ -373,7 +373,9 @@ __global__ __launch_bounds__(kTdThreads * G) void tiled_kernel(TiledArgs p) {
     constexpr int kEpiStride = 36;
     int* scratch = reinterpret_cast<int*>(smem) + (g * 4 + wave) * (32 * kEpiStride);
     const int erow = lane >> 1, ecol = (lane & 1) * 16;
-    const bool vec_ok = (N % 16) == 0;
+    // 16-byte stores need 16-byte aligned row starts: N % 8 == 0 for bf16, N % 4 == 0
+    // for 4-byte outputs (column offsets are multiples of 16)
+    const bool vec_ok = (N % (DT == 1 ? 8 : 4)) == 0;
 
     auto emit_block = [&](int i, int j, const int (&v)[16]) {
 #pragma unroll
