@@ -80,9 +80,7 @@ def _load():
             "oracle_unpack": [p, i64, i64, p],
             "oracle_act_quant": [p, i64, i64, p, p],
             "oracle_accumulate": [p, p, i64, i64, i64, p],
-            "oracle_accumulate_sampled": [p, p, i64, i64, i64, p, p, i64, p],
             "oracle_rescale": [p, p, p, i64, i64, p, p, p],
-            "oracle_rescale_sampled": [p, p, p, p, p, i64, p, p, p],
             "oracle_f64_to_bf16": [p, i64, p],
             "oracle_swiglu": [p, p, i64, p],
             "oracle_act_quant_per_tensor": [p, i64, i64, p, p],
@@ -223,18 +221,6 @@ def accumulate(xq: np.ndarray, packed: np.ndarray, K: int) -> np.ndarray:
     return acc
 
 
-def accumulate_sampled(xq, packed, K, ms, ns) -> np.ndarray:
-    xq = np.ascontiguousarray(xq, dtype=np.int8)
-    packed = np.ascontiguousarray(packed, dtype=np.uint8)
-    ms = np.ascontiguousarray(ms, dtype=np.int64)
-    ns = np.ascontiguousarray(ns, dtype=np.int64)
-    M, N = xq.shape[0], packed.shape[0]
-    acc = np.empty(ms.shape, np.int32)
-    _check(_load().oracle_accumulate_sampled(_ptr(xq), _ptr(packed), M, N, K, _ptr(ms),
-                                             _ptr(ns), ms.size, _ptr(acc)), "accumulate_sampled")
-    return acc
-
-
 # --------------------------------------------------------------------------- O4
 
 
@@ -249,21 +235,6 @@ def rescale(acc: np.ndarray, a_scale: np.ndarray, w_scale: np.ndarray):
     bf = np.empty((M, N), np.uint16)
     _check(_load().oracle_rescale(_ptr(acc), _ptr(a_scale), _ptr(w_scale), M, N, _ptr(ref),
                                   _ptr(f32), _ptr(bf)), "rescale")
-    return ref, f32, bf
-
-
-def rescale_sampled(acc, a_scale, w_scale, ms, ns):
-    acc = np.ascontiguousarray(acc, dtype=np.int32)
-    a_scale = np.ascontiguousarray(a_scale, dtype=np.float32)
-    w_scale = np.ascontiguousarray(w_scale, dtype=np.float32)
-    ms = np.ascontiguousarray(ms, dtype=np.int64)
-    ns = np.ascontiguousarray(ns, dtype=np.int64)
-    ref = np.empty(ms.shape, np.float64)
-    f32 = np.empty(ms.shape, np.float32)
-    bf = np.empty(ms.shape, np.uint16)
-    _check(_load().oracle_rescale_sampled(_ptr(acc), _ptr(a_scale), _ptr(w_scale), _ptr(ms),
-                                          _ptr(ns), ms.size, _ptr(ref), _ptr(f32), _ptr(bf)),
-           "rescale_sampled")
     return ref, f32, bf
 
 

@@ -231,26 +231,6 @@ int oracle_accumulate(const int8_t* xq, const uint8_t* packed, int64_t M, int64_
     return overflow ? -1 : 0;
 }
 
-/* Same sum for a list of (m, n) pairs only, for shapes too large to compute whole. */
-int oracle_accumulate_sampled(const int8_t* xq, const uint8_t* packed, int64_t M, int64_t N,
-                              int64_t K, const int64_t* ms, const int64_t* ns, int64_t count,
-                              int32_t* acc) {
-    if (!xq || !packed || !ms || !ns || !acc || K < 4 || K % 4 != 0 || count < 0) return -1;
-    int64_t KB = K / 4;
-    int bad = 0;
-#pragma omp parallel for schedule(static) reduction(| : bad)
-    for (int64_t t = 0; t < count; ++t) {
-        int64_t m = ms[t], n = ns[t];
-        if (m < 0 || m >= M || n < 0 || n >= N) { bad = 1; continue; }
-        int64_t sum = 0;
-        for (int64_t k = 0; k < K; ++k)
-            sum += (int64_t)xq[m * K + k] * weight_at(packed, KB, n, k);
-        if (sum > INT32_MAX || sum < INT32_MIN) bad = 1;
-        acc[t] = (int32_t)sum;
-    }
-    return bad ? -1 : 0;
-}
-
 /* ------------------------------------------------------------- O4: rescale --- */
 
 /*
@@ -276,17 +256,6 @@ int oracle_rescale(const int32_t* acc, const float* a_scale, const float* w_scal
             rescale_one(acc[i], w_scale[n], a_scale[m], ref ? ref + i : NULL,
                         out_f32 ? out_f32 + i : NULL, out_bf16 ? out_bf16 + i : NULL);
         }
-    return 0;
-}
-
-/* Rescale for sampled (m, n) pairs: acc[t] belongs to (ms[t], ns[t]). */
-int oracle_rescale_sampled(const int32_t* acc, const float* a_scale, const float* w_scale,
-                           const int64_t* ms, const int64_t* ns, int64_t count, double* ref,
-                           float* out_f32, uint16_t* out_bf16) {
-    if (!acc || !a_scale || !w_scale || !ms || !ns || count < 0) return -1;
-    for (int64_t t = 0; t < count; ++t)
-        rescale_one(acc[t], w_scale[ns[t]], a_scale[ms[t]], ref ? ref + t : NULL,
-                    out_f32 ? out_f32 + t : NULL, out_bf16 ? out_bf16 + t : NULL);
     return 0;
 }
 

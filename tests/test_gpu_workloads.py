@@ -1,10 +1,15 @@
 """GPU parity at the full workload sizes, in the launch configuration the benchmark
-times: packed weights and scales checked whole; quantized activations checked whole;
-product outputs checked whole where the oracle finishes in seconds, otherwise on a
-fixed sample of (m, n) positions (corners included) that the oracle computes one by
-one.  Decode (M <= 16) runs the fused quant + GEMV entry point; larger M runs the
-separate quantization kernel and then the GEMM entry point.
+times: packed weights and scales checked whole, quantized activations checked whole,
+and every product output checked whole -- the int32 accumulators bit-exact against the
+oracle's, the fp32 and bf16 outputs against the oracle's rescale of those accumulators.
+Decode (M <= 16) runs the fused quant + GEMV entry point; larger M runs the separate
+quantization kernel and then the GEMM entry point.
+
+The oracle's scalar accumulation is the slow part: the largest shapes (70B gate / up /
+down at M = 1024, 2.4e11 multiply-adds each) take tens of seconds on the host cores.
 """
+import time
+
 import numpy as np
 import pytest
 import torch
@@ -15,9 +20,6 @@ import workloads
 from gpu_helpers import check_out, to_np
 
 pytestmark = pytest.mark.gpu
-
-FULL_LIMIT = 1.2e10  # M*N*K up to which the whole output is compared
-SAMPLES = 3000
 
 
 def cases():
@@ -53,17 +55,13 @@ def test_workload_shape(wl, name, N, K, Ms, outliers):
         else:
             xq_dev, a_dev = bw.quant_act(x_dev)
             outs = {dt: bw.gemm(xq_dev, a_dev, packed, w_scale, dt) for dt in ("f32", "bf16", "i32")}
+        outs = {dt: to_np(v) for dt, v in outs.items()}
         assert np.array_equal(to_np(a_dev), a_ref), f"a_scale M={M}"
         assert np.array_equal(to_np(xq_dev), xq_ref), f"xq M={M}"
-        if M * N * K <= FULL_LIMIT:
-            acc = oracle.accumulate(xq_ref, p_ref, K)
-            ref, _, _ = oracle.rescale(acc, a_ref, s_ref)
-            for dt, out in outs.items():
-                check_out(to_np(out), acc, ref, dt, f"{wl} {name} M={M} {dt} full")
-        else:
-            ms, ns = workloads.sample_pairs(M, N, SAMPLES, seed=M + N)
-            acc = oracle.accumulate_sampled(xq_ref, p_ref, K, ms, ns)
-            ref, _, _ = oracle.rescale_sampled(acc, a_ref, s_ref, ms, ns)
-            for dt, out in outs.items():
-                check_out(to_np(out)[ms, ns], acc, ref, dt, f"{wl} {name} M={M} {dt} sampled")
-        print(f"  M={M} ok", flush=True)
+        t0 = time.perf_counter()
+        acc = oracle.accumulate(xq_ref, p_ref, K)
+        ref, _, _ = oracle.rescale(acc, a_ref, s_ref)
+        t_oracle = time.perf_counter() - t0
+        for dt, out in outs.items():
+            check_out(out, acc, ref, dt, f"{wl} {name} M={M} {dt} full")
+        print(f"  M={M} ok (oracle {t_oracle:.1f} s)", flush=True)

@@ -228,16 +228,6 @@ def test_accumulate_special_cases():
     assert acc[0, 0] == 127 * 4096
 
 
-def test_accumulate_sampled_matches_full():
-    rng = np.random.default_rng(9)
-    M, N, K = 7, 33, 64
-    xq = rng.integers(-127, 128, size=(M, K), dtype=np.int8)
-    packed = oracle.pack(rng.integers(-1, 2, size=(N, K), dtype=np.int8))
-    full = oracle.accumulate(xq, packed, K)
-    ms, ns = workloads.sample_pairs(M, N, 40, seed=1)
-    assert np.array_equal(oracle.accumulate_sampled(xq, packed, K, ms, ns), full[ms, ns])
-
-
 # ----------------------------------------------------------------- O4 rescale
 
 

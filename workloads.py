@@ -74,13 +74,3 @@ def bf16_bits(x: torch.Tensor) -> np.ndarray:
     """bf16 tensor -> numpy uint16 array of its bit patterns (a view, no arithmetic)."""
     assert x.dtype == torch.bfloat16
     return x.contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
-
-
-def sample_pairs(M: int, N: int, count: int, seed: int = 0):
-    """Deterministic (m, n) output positions for sampled checks; always includes corners."""
-    rng = np.random.default_rng(seed)
-    ms = rng.integers(0, M, size=count, dtype=np.int64)
-    ns = rng.integers(0, N, size=count, dtype=np.int64)
-    corners_m = np.array([0, 0, M - 1, M - 1], np.int64)
-    corners_n = np.array([0, N - 1, 0, N - 1], np.int64)
-    return np.concatenate([corners_m, ms]), np.concatenate([corners_n, ns])
