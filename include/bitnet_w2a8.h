@@ -38,7 +38,10 @@
  * Packed weight layout (the interface format, produced by bitnet_pack_weights):
  *   packed[n * (K/4) + j] holds weights k = 4j .. 4j+3 of output row n; weight
  *   k = 4j + i sits in bits 2i .. 2i+1 as the code (w + 1): -1 -> 0b00, 0 -> 0b01,
- *   +1 -> 0b10 (0b11 is never produced).
+ *   +1 -> 0b10.  0b11 is never produced.  A buffer that holds it anyway (e.g. weights
+ *   packed with the other code table of "BitNet 深度实战" §4.3 and not converted by
+ *   bitnet_repack_codes) is decoded as w = code - 1 = +2 by every int8 product entry
+ *   point, whatever kernel a call takes, and as 0 by bitnet_a16_gemv.
  */
 #ifndef BITNET_W2A8_H
 #define BITNET_W2A8_H
@@ -102,7 +105,7 @@ int bitnet_pack_weights(const float* w, int64_t N, int64_t K, uint8_t* packed, f
 
 /*
  * bitnet_unpack_weights -- inverse of the packing, for inspection and tests.
- *   codes : int8 (N, K) output in {-1, 0, +1}.
+ *   codes : int8 (N, K) output, w = code - 1: {-1, 0, +1} (+2 for a field holding 0b11).
  */
 int bitnet_unpack_weights(const uint8_t* packed, int64_t N, int64_t K, int8_t* codes,
                           void* stream);
@@ -141,8 +144,8 @@ typedef enum {
  * other (same bit positions: weight 4j+i in bits 2i..2i+1 of byte j).  Converts weights
  * packed with the page's table for use here, and back.  in and out may be the same
  * buffer.  A field holding its table's unused code becomes weight 0; when
- * invalid_count (a device int32, caller-zeroed) is given, the number of such fields is
- * added to it.
+ * invalid_count (a device int32, caller-zeroed, 4-byte aligned, else
+ * BITNET_ERR_UNALIGNED) is given, the number of such fields is added to it.
  */
 int bitnet_repack_codes(const uint8_t* in, int64_t N, int64_t K, int from_table, int to_table,
                         uint8_t* out, int32_t* invalid_count, void* stream);
@@ -162,9 +165,13 @@ int bitnet_w2a8_gemv(const int8_t* xq, const float* a_scale, const uint8_t* pack
                      int out_dtype, void* stream);
 
 /*
- * bitnet_w2a8_gemm -- the same product for any M >= 0 (prefill).  `algo` selects the
- * kernel (bitnet_algo); BITNET_ALGO_SKINNY with M > BITNET_SKINNY_MAX_M returns
- * BITNET_ERR_INVALID_ARG.
+ * bitnet_w2a8_gemm -- the same product for any M >= 0: prefill, where the int8 products
+ * run on the matrix cores ("BitNet-Triton" 技术架构 §2: int8 tensor-core GEMM for the
+ * prefill phase; "BitNet 深度实战" §4.4: int8 x ternary accumulated in int32).
+ *   xq, a_scale, packed, w_scale, out, out_dtype : as in bitnet_w2a8_gemv.
+ *   algo : which kernel (bitnet_algo); an addition to the plain product signature that
+ *          only selects among kernels with identical results.  BITNET_ALGO_SKINNY with
+ *          M > BITNET_SKINNY_MAX_M returns BITNET_ERR_INVALID_ARG.
  * Workspace: reserved for kernels that need device scratch.  This version needs none:
  * bitnet_w2a8_gemm_workspace_size returns 0 and workspace may be NULL with ws_bytes 0
  * (a larger caller buffer is accepted and left untouched).

@@ -219,28 +219,12 @@ def gemv(xq, a_scale, packed, w_scale, out_dtype="f32", out=None):
     return out
 
 
-_workspaces = {}
-
-
-def workspace_for(device: torch.device, nbytes: int, stream: int) -> torch.Tensor:
-    """A zero-filled device workspace of at least nbytes, cached per (device, stream).
-
-    The GEMM leaves the workspace's counters at zero after every call, so a cached
-    buffer can be reused by later calls on the same stream.  Allocate it (first call)
-    outside of any graph capture."""
-    key = (device.index, stream)
-    ws = _workspaces.get(key)
-    if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros((max(nbytes, 1 << 16),), dtype=torch.uint8, device=device)
-        _workspaces[key] = ws
-    return ws
-
-
 def gemm(xq, a_scale, packed, w_scale, out_dtype="f32", algo="auto", out=None, workspace=None):
     """Product for any M: int8 xq x packed ternary -> (M, N).
 
-    The workspace (split-K partials and counters) defaults to a cached zero-filled buffer
-    for the current stream; pass one explicitly to control it."""
+    The library's size query (bitnet_w2a8_gemm_workspace_size) decides whether a device
+    workspace is needed; a uint8 tensor of at least that many bytes may be passed in,
+    and when the query returns 0 (every kernel of this version) none is allocated."""
     M, K = xq.shape
     N = packed.shape[0]
     code = _out_code(out_dtype)
@@ -248,9 +232,9 @@ def gemm(xq, a_scale, packed, w_scale, out_dtype="f32", algo="auto", out=None, w
     out = _alloc_out(out, M, N, code, xq.device)
     stream = _stream(xq)
     ws_need = int(lib().bitnet_w2a8_gemm_workspace_size(M, N, K))
-    ws_ptr, ws_bytes = None, 0
     if workspace is None and ws_need:
-        workspace = workspace_for(xq.device, ws_need, stream)
+        workspace = torch.empty((ws_need,), dtype=torch.uint8, device=xq.device)
+    ws_ptr, ws_bytes = None, 0
     if workspace is not None:
         ws_ptr = _tensor(workspace, torch.uint8, "workspace")
         ws_bytes = workspace.numel()

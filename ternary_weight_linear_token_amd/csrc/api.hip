@@ -313,6 +313,7 @@ int bitnet_repack_codes(const uint8_t* in, int64_t N, int64_t K, int from_table,
     if (st) return st;
     if (N == 0) return BITNET_OK;
     if (!in || !out) return BITNET_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(invalid_count) & 3u) != 0) return BITNET_ERR_UNALIGNED;
     if ((st = check_device())) return st;
     return record_hip(bitnet::launch_repack_codes(in, N, K, from_table, to_table, out,
                                                   invalid_count, as_stream(stream)));

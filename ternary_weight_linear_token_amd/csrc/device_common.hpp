@@ -49,11 +49,13 @@ __device__ __forceinline__ int sum_i8x4(uint32_t v, int acc) {
 }
 
 // Signed weight bytes from 2-bit codes: field i (bits 2i..2i+1) of each byte of d,
-// code c in {0,1,2} -> w = c - 1 as int8 {0xFF, 0x00, 0x01} through a v_perm lookup.
+// code c -> w = c - 1 as int8 {0xFF, 0x00, 0x01, 0x02} through a v_perm lookup.  The
+// code 3, which packing never writes, decodes as +2 like in the mask-based unpack, so
+// every int8 kernel reads any byte the same way.
 template <int I>
 __device__ __forceinline__ uint32_t ternary_field_i8(uint32_t d) {
     uint32_t sel = (d >> (2 * I)) & 0x03030303u;
-    return __builtin_amdgcn_perm(0u, 0x000100FFu, sel);
+    return __builtin_amdgcn_perm(0u, 0x020100FFu, sel);
 }
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {

@@ -60,8 +60,8 @@ hipError_t launch_gemv_direct(const int8_t* xq, const float* a_scale, const uint
                               int64_t K, void* out, int out_dtype, int8_t* xq_out, float* a_out,
                               hipStream_t stream);
 
-// Tiled int8 matrix-core product for any M.  `workspace` must hold
-// tiled_workspace_size(M, N, K) bytes whose counter area is zero (it is left zero).
+// Tiled int8 matrix-core product for any M.  Device scratch it needs, in bytes (none:
+// every tile keeps its whole K range inside one block).
 size_t tiled_workspace_size(int64_t M, int64_t N, int64_t K);
 // The tiled product for 1 <= groups <= BITNET_MAX_GROUPS weight matrices (N[g] rows
 // each, all K columns) against the same activations, in one launch; the tile plan is

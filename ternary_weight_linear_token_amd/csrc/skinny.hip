@@ -38,6 +38,8 @@
 //    grid is the concatenation of the groups' row blocks; a block picks its group with
 //    scalar compares of its index, so each group costs exactly what it costs alone,
 //    minus one launch.
+#include <atomic>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -599,27 +601,31 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
     }
 }
 
-// Dynamic LDS beyond the default 64 KB limit must be granted per kernel (once per device).
-template <typename Kernel>
-hipError_t allow_lds(Kernel* kernel, size_t lds) {
-    if (lds <= 65536) return hipSuccess;
-    static int granted[64] = {0};
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev >= 0 && dev < 64 && granted[dev]) return hipSuccess;
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e == hipSuccess && dev >= 0 && dev < 64) granted[dev] = 1;
-    return e;
-}
+// Dynamic LDS beyond the default 64 KB limit must be granted per kernel and device.
+// Each instantiation of launch_one grants its kernel the whole 160 KB a block may use
+// (so no later, larger request needs a second grant), once per device; the flags are
+// atomics, so concurrent first calls at worst repeat the idempotent grant.
+constexpr int kSkMaxDevices = 64;
+constexpr int kSkLdsMax = 160 * 1024;
 
 template <bool FUSED, bool FAST, int XH, int U, bool SINGLE, int MC = 0, int MT = 1, bool PAIR = false>
 hipError_t launch_one(const SkinnyArgs& a, dim3 grid, size_t lds, hipStream_t stream) {
-    const hipError_t e = allow_lds(&skinny_kernel<FUSED, FAST, XH, U, SINGLE, MC, MT, PAIR>, lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((skinny_kernel<FUSED, FAST, XH, U, SINGLE, MC, MT, PAIR>), grid,
-                       dim3(kSkThreads), lds, stream, a);
+    static std::atomic<bool> granted[kSkMaxDevices];
+    auto* kernel = &skinny_kernel<FUSED, FAST, XH, U, SINGLE, MC, MT, PAIR>;
+    if (lds > 65536) {
+        if (lds > (size_t)kSkLdsMax) return hipErrorInvalidValue;
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return e;
+        if (dev < 0 || dev >= kSkMaxDevices) return hipErrorInvalidDevice;
+        if (!granted[dev].load(std::memory_order_acquire)) {
+            e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, kSkLdsMax);
+            if (e != hipSuccess) return e;
+            granted[dev].store(true, std::memory_order_release);
+        }
+    }
+    hipLaunchKernelGGL(kernel, grid, dim3(kSkThreads), lds, stream, a);
     return hipGetLastError();
 }
 

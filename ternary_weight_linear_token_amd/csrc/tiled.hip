@@ -40,6 +40,7 @@
 //  * Grouped launches: up to BITNET_MAX_GROUPS weight matrices that read the same
 //    activations (q, k, v; gate, up) share one grid; a block finds its matrix by scalar
 //    compares of its work unit against the groups' first units.
+#include <atomic>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -541,41 +542,43 @@ struct TilePlan {
     int bk;         // k per LDS stage
 };
 
+// Compute units of the current device, queried once per device (atomics: concurrent
+// first calls at worst repeat the query).
 int device_cus() {
-    static int cus[64] = {0};
+    static std::atomic<int> cus[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cus[dev] == 0) {
-        int v = 0;
+    int v = cus[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
         if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
             v = 256;
-        cus[dev] = v;
+        cus[dev].store(v, std::memory_order_relaxed);
     }
-    return cus[dev];
+    return v;
 }
 
 // Optional override for tuning: BITNET_TILED_CONFIG="bm,bn,g", one of the compiled
 // configurations (256,256,1 / 256,128,1 / 128,128,2 / 64,128,4); read once
 // per process.
-bool config_override(int* bm, int* bn, int* g) {
-    static int cached[4] = {-1, 0, 0, 0};
-    if (cached[0] == -1) {
+struct ConfigOverride {
+    bool on = false;
+    int bm = 0, bn = 0, g = 0;
+};
+
+const ConfigOverride& config_override() {
+    static const ConfigOverride c = [] {
+        ConfigOverride r;
         const char* e = std::getenv("BITNET_TILED_CONFIG");
-        int a = 0, b = 0, c = 0;
-        const bool ok = e && std::sscanf(e, "%d,%d,%d", &a, &b, &c) == 3 &&
-                        ((a == 256 && b == 256 && c == 1) || (a == 256 && b == 128 && c == 1) ||
-                         (a == 128 && b == 128 && c == 2) ||
-                         (a == 64 && b == 128 && c == 4));
-        cached[0] = ok ? 1 : 0;
-        cached[1] = a;
-        cached[2] = b;
-        cached[3] = c;
-    }
-    if (cached[0] <= 0) return false;
-    *bm = cached[1];
-    *bn = cached[2];
-    *g = cached[3];
-    return true;
+        int a = 0, b = 0, g = 0;
+        r.on = e && std::sscanf(e, "%d,%d,%d", &a, &b, &g) == 3 &&
+               ((a == 256 && b == 256 && g == 1) || (a == 256 && b == 128 && g == 1) ||
+                (a == 128 && b == 128 && g == 2) || (a == 64 && b == 128 && g == 4));
+        r.bm = a;
+        r.bn = b;
+        r.g = g;
+        return r;
+    }();  // thread-safe initialization of a function-local static
+    return c;
 }
 
 // Tile shape: the compiled configuration with the least estimated time.  Every
@@ -604,7 +607,11 @@ constexpr TileCost kTileCosts[] = {
 
 TilePlan plan_tiles(int64_t M, int64_t K, const int64_t* N, int groups, int64_t cus) {
     TilePlan t;
-    if (config_override(&t.bm, &t.bn, &t.g)) {
+    const ConfigOverride& ov = config_override();
+    if (ov.on) {
+        t.bm = ov.bm;
+        t.bn = ov.bn;
+        t.g = ov.g;
         t.bk = (K % 128 == 0 && !(t.bm == 256 && t.bn == 256)) ? 128 : 64;
         return t;
     }

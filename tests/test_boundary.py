@@ -286,6 +286,7 @@ def test_per_tensor_and_repack_validation(L):
     assert g(A, 4, 256, -1, 1, B, None, None) == INVALID
     assert g(None, 4, 256, 0, 1, B, None, None) == INVALID
     assert g(A, 4, 254, 0, 1, B, None, None) == UNALIGNED
+    assert g(A, 4, 256, 0, 1, B, C + 2, None) == UNALIGNED  # int32 counter off 4 bytes
     assert g(A, 0, 256, 0, 1, B, None, None) == OK
 
 

@@ -364,6 +364,37 @@ def test_extreme_accumulators():
             check_out(to_np(out), acc, ref, dt, f"extreme {algo} {dt}")
 
 
+def test_unused_code_decodes_the_same_on_every_route():
+    # Bytes with every 2-bit field value, 0b11 included (never written by the packing):
+    # every int8 product route reads it as w = code - 1 = +2, like the oracle's decode,
+    # and the bf16-activation product reads it as 0.
+    rng = np.random.default_rng(33)
+    K = 1024
+    for M, N in ((1, 300), (5, 300), (16, 129), (17, 64), (40, 300), (130, 257)):
+        packed_np = rng.integers(0, 256, size=(N, K // 4), dtype=np.uint8)
+        assert np.any(((packed_np[..., None] >> np.array([0, 2, 4, 6], np.uint8)) & 3) == 3)
+        X = workloads.activations(M, K, seed=M + N)
+        xq_np, a_np = oracle.act_quant(workloads.bf16_bits(X))
+        s_np = np.linspace(0.01, 0.03, N).astype(np.float32)
+        acc = oracle.accumulate(xq_np, packed_np, K)
+        ref, _, _ = oracle.rescale(acc, a_np, s_np)
+        packed, s, xq, a = dev(packed_np), dev(s_np), dev(xq_np), dev(a_np)
+        outs = {f"gemm {algo}": bw.gemm(xq, a, packed, s, "i32", algo=algo)
+                for algo in ("tiled", "auto") + (("skinny",) if M <= 64 else ())}
+        outs["grouped"] = bw.gemm_grouped(xq, a, [packed], [s], "i32")[0]
+        if M <= bw.GEMV_MAX_M:
+            outs["gemv"] = bw.gemv(xq, a, packed, s, "i32")
+            outs["quant_gemv"] = bw.quant_gemv(X.cuda(), packed, s, "i32")
+            outs["quant_gemv_grouped"] = bw.quant_gemv_grouped(X.cuda(), [packed], [s], "i32")[0]
+        for route, out in outs.items():
+            check_out(to_np(out), acc, ref, "i32", f"code 3, {route}, M={M} N={N}")
+        if M <= bw.GEMV_MAX_M:
+            as_zero, _ = oracle.repack(packed_np, K, oracle.CODES_OFFSET, oracle.CODES_OFFSET)
+            ref16, sumabs = oracle.a16(workloads.bf16_bits(X), as_zero, s_np, K)
+            out16 = to_np(bw.a16_gemv(X.cuda(), packed, s, "f32")).astype(np.float64)
+            assert np.all(np.abs(out16 - ref16) <= (K + 2) * 2.0 ** -24 * sumabs), "code 3, a16"
+
+
 def test_zero_rows_and_zero_weights():
     M, N, K = 4, 48, 512
     X = workloads.activations(M, K, seed=1)
