@@ -1,8 +1,9 @@
 #!/usr/bin/env python3
 """Benchmark of the W2A8 BitLinear hot path on one MI355X.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-sweep]
 python bench.py --traffic-probe   (launch pattern for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)
+python bench.py --gemm-probe      (prefill GEMM launches for rocprofv3 --pmc)
 
 A step is one BitNet-2B-shaped decode layer set at M = 1: the seven projections
 (q, k, v, o, gate, up, down; (N, K) = (2560,2560) (640,2560) (640,2560) (2560,2560)
@@ -12,31 +13,38 @@ int32 accumulation, rescale.  Projections that read the same activations share o
 fused quant + GEMV launch (q|k|v, o, gate|up, down: four launches); the same set with
 one launch per projection is reported beside it (value_ungrouped).
 
-* Inputs are resident in HBM before timing.  The packed weights are replicated into
-  enough copies to exceed 1 GiB and every step uses the next copy, so the weights come
-  from HBM rather than the 256 MB Infinity Cache.
+* Inputs are resident in HBM before timing.  Every timed graph rotates over copies of
+  the weights it reads that together exceed 1 GiB (four times the 256 MB Infinity
+  Cache), so the weights come from HBM: the step over copies of the whole set, and each
+  per-launch graph over copies of that launch's own matrices.
 * Steps are captured in HIP graphs, ten consecutive steps (each on the next weight
   copy) per graph, so host submission does not pace the GPU; W warmup steps, then
   exactly K steps between two synchronizations timed with events.
 * value = packed-weight bytes of the set / step time (GB/s).
 * roofline: the fused quant+GEMV kernel, algorithmic bytes (N*K/4 packed bytes per
-  launch) / its mean launch duration (a graph of back-to-back launches over the weight
-  copies, timed with events), against 8 TB/s; traffic from the committed rocprofv3
-  counter summary when it matches the current kernel source.
+  launch) / its mean launch duration (a graph of back-to-back launches over the
+  launch's weight copies, timed with events on the launching stream), against 8 TB/s;
+  traffic from the committed rocprofv3 counter summary when it matches the current
+  kernel source.
 * gemm: the BitNet-2B-shaped prefill set at M = 512 (tiled int8-MFMA GEMM, bf16 out),
   with the projections that share an input in one grouped launch (q|k|v, o, gate|up,
   down), int8 TOPS against 5.0 POPS dense from the per-launch GEMM durations; the step
   rate with the four quantization launches and the rate of seven ungrouped launches are
   reported beside it.
+* sweep: every (shape, M) of the 8B-shaped sweep (M = 1, 4, 16, 64, 256, 2048) and the
+  70B-shaped chain (M = 1, 32, 1024): M <= 16 through the fused quant + GEMV entry point,
+  larger M through the GEMM entry point on int8 activations (the quantization launch
+  timed beside it).  Each entry gives the time, packed GB/s, TOPS, the roofline that
+  binds (HBM or int8 MFMA, from the algorithmic bytes and operations), the attainable
+  rate min(peak, arithmetic intensity x bandwidth) and the fractions of both.
 * cpu_baseline: the CPU oracle on the host cores (test infrastructure, timed only
   here), on the same decode step repeated for ~10 s.
-* extras: the same per-launch rooflines at large shapes, where the bandwidth and
-  matrix-core bars are reachable: the 70B-shaped decode layer set (M = 1) and the
-  8B-shaped prefill MLP GEMMs (M = 2048); the 2B decode MLP as two launches (gate|up
-  with the SwiGLU epilogue, then down); the 2B decode set with bf16 activations and no
-  activation quantization (W1.58A16); and ceilings measured on this chip: an int8
-  matrix-core loop on register operands, a 2 GiB streaming read, and the vendor int8
-  GEMM (hipBLASLt, dense int8 weights) at the prefill shapes.
+* extras: the 70B-shaped decode layer set at M = 1 with grouped launches and the
+  same-grid read floors; the 2B decode MLP as two launches (gate|up with the SwiGLU
+  epilogue, then down); the 2B decode set with bf16 activations (W1.58A16); and
+  ceilings measured on this chip: an int8 matrix-core loop on register operands with
+  the core clock it sustained, a 2 GiB streaming read, and the vendor int8 GEMM
+  (hipBLASLt, dense int8 weights) at prefill shapes.
 """
 from __future__ import annotations
 
@@ -67,8 +75,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--kernel-reps", type=int, default=5)
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the 8B- and 70B-shaped (shape, M) sweep")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the 70B-shaped decode and 8B-shaped prefill rooflines")
+                    help="skip the 70B decode set, MLP chain, W1.58A16 set and the ceilings")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run the counter-collection launch pattern and exit (no timing)")
     ap.add_argument("--gemm-probe", action="store_true",
@@ -89,22 +99,11 @@ def load_summary(path: str, kernel_hash: str):
     return vals if vals.get("kernel_source_sha256") == kernel_hash else None
 
 
-def load_traffic(kernel_hash: str):
-    """Per-launch HBM bytes from the committed counter summary, if it still applies."""
-    if not os.path.exists(TRAFFIC_FILE):
-        return None
-    vals = {}
-    with open(TRAFFIC_FILE) as f:
-        for line in f:
-            if "=" in line and not line.startswith("#"):
-                k, v = line.split("=", 1)
-                vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_sha256") != kernel_hash:
-        return None
-    try:
-        return float(vals["hbm_bytes_per_launch"])
-    except (KeyError, ValueError):
-        return None
+def rotation(tensors, nbytes):
+    """Copies of `tensors` (nbytes together) whose total exceeds ROTATE_BYTES: entry r
+    of the returned list is the r-th copy (entry 0 the tensors themselves)."""
+    R = max(2, math.ceil(ROTATE_BYTES / nbytes))
+    return [list(tensors)] + [[t.clone() for t in tensors] for _ in range(R - 1)]
 
 
 def main():
@@ -139,21 +138,22 @@ def main():
         xs.append(workloads.activations(1, K, seed=0, outliers=True).to(dev))
         outs.append(torch.empty((1, N), dtype=torch.float32, device=dev))
     set_bytes = sum(N * K // 4 for _, N, K in layer)
-    R = max(2, math.ceil(ROTATE_BYTES / set_bytes))
-    copies = [packed0] + [[p.clone() for p in packed0] for _ in range(R - 1)]
+    copies = rotation(packed0, set_bytes)
+    R = len(copies)
     torch.cuda.synchronize()
 
-    def launch_group(r, grp):
+    def launch_group(c, grp):
+        """One launch of group grp (indices into layer) on weight list c (by layer index)."""
         if len(grp) == 1:
             i = grp[0]
-            bw.quant_gemv(xs[i], copies[r][i], scales[i], "f32", out=outs[i])
+            bw.quant_gemv(xs[i], c[i], scales[i], "f32", out=outs[i])
         else:
-            bw.quant_gemv_grouped(xs[grp[0]], [copies[r][i] for i in grp],
-                                  [scales[i] for i in grp], "f32", out=[outs[i] for i in grp])
+            bw.quant_gemv_grouped(xs[grp[0]], [c[i] for i in grp], [scales[i] for i in grp],
+                                  "f32", out=[outs[i] for i in grp])
 
     def launch_set(r):
         for grp in groups:
-            launch_group(r, grp)
+            launch_group(copies[r], grp)
 
     def launch_set_ungrouped(r):
         for i in range(len(layer)):
@@ -163,8 +163,7 @@ def main():
         traffic_probe(torch, launch_set, R, dev)
         return
     if args.gemm_probe:
-        bench_gemm(bw, workloads, torch, np, dev, layer, R_bytes=ROTATE_BYTES,
-                   reps=args.kernel_reps, probe=True)
+        bench_gemm(bw, workloads, torch, dev, layer, reps=args.kernel_reps, probe=True)
         return
 
     # Steps are captured STEPS_PER_GRAPH at a time, each on the next weight copy, so the
@@ -178,34 +177,47 @@ def main():
     ms_step = run_steps(torch, launch_set, R, args.warmup, args.steps)
     value = set_bytes / (ms_step * 1e-3) / 1e9
     ms_step_ungrouped = run_steps(torch, launch_set_ungrouped, R, args.warmup, args.steps)
+    del copies
+    torch.cuda.empty_cache()
 
-    # ---- per-launch kernel durations: one graph per launch holding R back-to-back
-    # launches (one per weight copy); event time of the replay / R ----
-    per_group_us = [graph_launch_us(torch, lambda r, grp=grp: launch_group(r, grp), R,
-                                    args.kernel_reps) for grp in groups]
-    per_shape_us = [graph_launch_us(torch, lambda r, i=i: bw.quant_gemv(
-        xs[i], copies[r][i], scales[i], "f32", out=outs[i]), R, args.kernel_reps)
-        for i in range(len(layer))]
+    # ---- per-launch kernel durations: one graph per launch holding back-to-back
+    # launches over that launch's own weight copies (> 1 GiB together); event time of
+    # the replay / launches ----
+    shapes = {name: (N, K) for name, N, K in layer}
+
+    def group_us(grp):
+        nbytes = sum(shapes[layer[i][0]][0] * shapes[layer[i][0]][1] // 4 for i in grp)
+        cp = rotation([packed0[i] for i in grp], nbytes)
+
+        def launch(r):
+            c = dict(zip(grp, cp[r]))
+            launch_group(c, grp)
+
+        us = graph_launch_us(torch, launch, len(cp), args.kernel_reps)
+        del cp
+        torch.cuda.empty_cache()
+        return us
+
+    per_group_us = [group_us(grp) for grp in groups]
+    per_shape_us = [group_us([i]) for i in range(len(layer))]
     kern_us_total = sum(per_group_us)
     achieved = set_bytes / (kern_us_total * 1e-6) / 1e9
     # the floor of each launch's grid: a plain streaming read of the launch's packed
     # bytes with the same number of 256-thread blocks (one per 16 weight rows)
     from ternary_weight_linear_token_amd import ceilings
-    shapes = {name: (N, K) for name, N, K in layer}
     floor_us = [ceilings.same_grid_read_us(
         torch, dev, sum(shapes[n][0] * shapes[n][1] // 4 for n in grp),
         sum((shapes[n][0] + 15) // 16 for n in grp),
-        lambda launch, R: graph_launch_us(torch, launch, R, args.kernel_reps))
+        lambda launch, RR: graph_launch_us(torch, launch, RR, args.kernel_reps))
         for grp in workloads.DECODE_GROUPS]
-    kernel_hash = bw_build.kernel_hash("skinny.hip")
-    traffic_bytes = load_traffic(kernel_hash)
+    counters = load_summary(TRAFFIC_FILE, bw_build.kernel_hash("skinny.hip"))
     roofline = {
         "bound": "hbm",
         "achieved": round(achieved, 1),
         "peak": HBM_PEAK_GBS,
         "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBS, 4),
-        "traffic": traffic_bytes,
+        "traffic": float(counters["hbm_bytes_per_launch"]) if counters else None,
         "kernel": "skinny_kernel, fused quant+GEMV, M=1 specialization",
         "launches_per_step": len(groups),
         "mean_launch_us": round(kern_us_total / len(groups), 3),
@@ -219,16 +231,22 @@ def main():
                                    for (name, _, _), us in zip(layer, per_shape_us)},
         "ungrouped_achieved": round(set_bytes / (sum(per_shape_us) * 1e-6) / 1e9, 1),
     }
+    del packed0
+    torch.cuda.empty_cache()
 
     # ---- prefill GEMM, M = 512 ----
-    gemm = bench_gemm(bw, workloads, torch, np, dev, layer, R_bytes=ROTATE_BYTES,
-                      reps=args.kernel_reps)
+    gemm = bench_gemm(bw, workloads, torch, dev, layer, reps=args.kernel_reps)
 
     # ---- CPU oracle baseline ----
     cpu = None if args.no_cpu_baseline else cpu_baseline(workloads, layer, args.cpu_seconds)
 
-    # ---- the shapes where the bandwidth and matrix-core bars are reachable ----
+    # ---- every (shape, M) of the 8B-shaped sweep and the 70B-shaped chain ----
+    sweep = None if args.no_sweep else bench_sweep(bw, workloads, torch, dev, args.kernel_reps)
+
+    # ---- large-shape decode set, MLP chain, bf16 activations, measured ceilings ----
     extras = None if args.no_extras else bench_extras(bw, workloads, torch, dev, args.kernel_reps)
+    if extras is not None and sweep is not None:
+        extras.update(sweep_summaries(sweep))
 
     result = {
         "metric": METRIC,
@@ -259,6 +277,7 @@ def main():
         "roofline": roofline,
         "gemm": gemm,
         "cpu_baseline": cpu,
+        "sweep": sweep,
         "extras": extras,
     }
     print(json.dumps(result), flush=True)
@@ -311,11 +330,10 @@ def run_steps(torch, launch_step, R, warmup, steps):
     return t0.elapsed_time(t1) / steps
 
 
-def traffic_probe(torch, launch_set, R, dev):
-    """Launch pattern for the HBM counters: first three calibration launches of a plain
-    elementwise kernel that reads and writes a known number of bytes (torch.neg on int32,
-    profiling.COPY_BYTES each, twice the Infinity Cache), then the decode step once per
-    weight copy (so the weights come from HBM), eagerly."""
+def calibration_copies(torch, dev):
+    """Three launches of a plain elementwise kernel that reads and writes a known number
+    of bytes (torch.neg on int32, profiling.COPY_BYTES each, twice the Infinity Cache):
+    the reference the HBM byte counters are scaled by."""
     from ternary_weight_linear_token_amd import profiling
     n = profiling.COPY_BYTES // 4
     src = torch.arange(n, dtype=torch.int32, device=dev)
@@ -324,6 +342,12 @@ def traffic_probe(torch, launch_set, R, dev):
         torch.neg(src, out=dst)
     torch.cuda.synchronize()
     del src, dst
+
+
+def traffic_probe(torch, launch_set, R, dev):
+    """Launch pattern for the HBM counters: the calibration copies, then the decode step
+    once per weight copy (so the weights come from HBM), eagerly."""
+    calibration_copies(torch, dev)
     for r in range(R):
         launch_set(r)
     torch.cuda.synchronize()
@@ -354,11 +378,104 @@ def graph_launch_us(torch, launch, R, reps):
     return t0.elapsed_time(t1) * 1e3 / (reps * R)
 
 
+def roofline_entry(us, ops, nbytes):
+    """Bound, attainable rate and fractions of one launch of `ops` int8 operations over
+    `nbytes` algorithmic HBM bytes that took `us` microseconds.  The ideal time is the
+    larger of ops / int8-MFMA peak and bytes / HBM peak; attainable = min(peak, AI x BW)
+    in TOPS."""
+    t_mfma = ops / (INT8_MFMA_PEAK_TOPS * 1e6)
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e3)
+    bound = "mfma" if t_mfma >= t_hbm else "hbm"
+    ai = ops / nbytes
+    attainable = min(INT8_MFMA_PEAK_TOPS, ai * HBM_PEAK_GBS / 1e3)
+    e = {"bound": bound, "ops_per_byte": round(ai, 2), "attainable_TOPS": round(attainable, 1),
+         "frac_of_attainable": round(max(t_mfma, t_hbm) / us, 4)}
+    if bound == "hbm":
+        e["frac_hbm_peak"] = round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)
+    else:
+        e["frac_mfma_peak"] = round(ops / us / 1e6 / INT8_MFMA_PEAK_TOPS, 4)
+    return e
+
+
+def bench_sweep(bw, workloads, torch, dev, reps):
+    """Every (shape, M) of the 8B-shaped sweep and the 70B-shaped chain: M <= 16 through
+    the fused quant + GEMV entry point (bf16 in, fp32 out), larger M through the GEMM
+    entry point (int8 in, bf16 out; the quantization launch is timed beside it).  Each
+    launch is a graph of back-to-back launches over weight copies rotated past 1 GiB."""
+    entries = []
+    for wl, tag in (("8b_sweep", "8b"), ("70b_chain", "70b")):
+        spec = workloads.WORKLOADS[wl]
+        print(f"[bench] {tag}-shaped sweep, M in {spec['Ms']}", file=sys.stderr, flush=True)
+        for name, N, K in workloads.distinct_shapes(spec["layer"]):
+            W = workloads.latent_weights_on(dev, N, K, seed=0)
+            p, s = bw.pack_weights(W)
+            del W
+            torch.cuda.empty_cache()
+            cp = rotation([p], N * K // 4)
+            R = len(cp)
+            for M in spec["Ms"]:
+                x = workloads.activations(M, K, seed=0, outliers=True).to(dev)
+                if M <= bw.GEMV_MAX_M:
+                    o = torch.empty((M, N), dtype=torch.float32, device=dev)
+                    us = graph_launch_us(torch, lambda r: bw.quant_gemv(x, cp[r][0], s, "f32", out=o),
+                                         R, reps)
+                    nbytes = N * K // 4 + 4 * N + 2 * M * K + 4 * M * N
+                    entry, quant_us = "bitnet_quant_gemv", None
+                else:
+                    xq, a = bw.quant_act(x)
+                    o = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+                    us = graph_launch_us(torch, lambda r: bw.gemm(xq, a, cp[r][0], s, "bf16", out=o),
+                                         R, reps)
+                    quant_us = graph_launch_us(torch, lambda r: bw.quant_act(x, xq=xq, a_scale=a),
+                                               8, reps)
+                    nbytes = N * K // 4 + 4 * N + M * K + 4 * M + 2 * M * N
+                    entry = "bitnet_w2a8_gemm"
+                ops = 2.0 * M * N * K
+                e = {"workload": tag, "shape": name, "N": N, "K": K, "M": M, "entry": entry,
+                     "us": round(us, 3), "packed_GB/s": round(N * K / 4 / us / 1e3, 1),
+                     "TOPS": round(ops / us / 1e6, 1)}
+                e.update(roofline_entry(us, ops, nbytes))
+                if quant_us is not None:
+                    e["quant_us"] = round(quant_us, 3)
+                entries.append(e)
+                del o, x
+            del cp, p
+            torch.cuda.empty_cache()
+    return entries
+
+
+def sweep_summaries(sweep):
+    """Set-level figures from the sweep: the 8B MLP GEMMs at M = 2048 and the 70B chain's
+    seven projections at M = 1024 (int8 TOPS against 5.0 POPS)."""
+    def set_tops(tag, M, names):
+        by = {(e["workload"], e["shape"], e["M"]): e for e in sweep}
+        ops = us = 0.0
+        per = {}
+        for n in names:
+            e = by.get((tag, n, M)) or by.get((tag, {"v": "k", "up": "gate"}.get(n, n), M))
+            if e is None:
+                return None
+            ops += 2.0 * M * e["N"] * e["K"]
+            us += e["us"]
+            per[n] = {"us": e["us"], "TFLOP/s": e["TOPS"]}
+        t = ops / us / 1e6
+        return {"bound": "mfma", "achieved": round(t, 1), "peak": INT8_MFMA_PEAK_TOPS,
+                "unit": "TFLOP/s", "frac": round(t / INT8_MFMA_PEAK_TOPS, 4), "per_shape": per}
+
+    out = {}
+    s8 = set_tops("8b", 2048, ["gate", "down"])
+    if s8:
+        out["prefill_8b_m2048"] = s8
+    s70 = set_tops("70b", 1024, ["q", "k", "v", "o", "gate", "up", "down"])
+    if s70:
+        out["prefill_70b_m1024_chain"] = s70
+    return out
+
+
 def bench_extras(bw, workloads, torch, dev, reps):
-    """Per-launch rooflines at large shapes: the 70B-shaped decode layer set (M = 1, fused
-    quant + GEMV, packed GB/s against 8 TB/s) and the 8B-shaped prefill MLP GEMMs
-    (M = 2048, quant excluded, int8 TOPS against 5.0 POPS).  Same method as the
-    headline: graphs of back-to-back launches over weight copies rotated past 1 GiB."""
+    """The 70B-shaped decode layer set (M = 1, grouped fused quant + GEMV launches, packed
+    GB/s against 8 TB/s, with the same-grid read floors), the 2B decode MLP chain, the 2B
+    decode set with bf16 activations, and the measured ceilings."""
     out = {}
     print("[bench] 70B-shaped decode set, M=1", file=sys.stderr, flush=True)
     shapes = {name: (N, K) for name, N, K in workloads.LAYER_70B}
@@ -368,14 +485,14 @@ def bench_extras(bw, workloads, torch, dev, reps):
         K = shapes[grp[0]][1]
         ps, ss = [], []
         for name in grp:
-            W = workloads.latent_weights(shapes[name][0], K, seed=0).to(dev)
+            W = workloads.latent_weights_on(dev, shapes[name][0], K, seed=0)
             p, s = bw.pack_weights(W)
             del W
             ps.append(p)
             ss.append(s)
         nbytes = sum(shapes[name][0] * K // 4 for name in grp)
-        R = max(2, math.ceil(ROTATE_BYTES / nbytes))
-        copies = [ps] + [[p.clone() for p in ps] for _ in range(R - 1)]
+        copies = rotation(ps, nbytes)
+        R = len(copies)
         x = workloads.activations(1, K, seed=0, outliers=True).to(dev)
         os_ = [torch.empty((1, shapes[name][0]), dtype=torch.float32, device=dev) for name in grp]
         if len(grp) == 1:
@@ -399,29 +516,6 @@ def bench_extras(bw, workloads, torch, dev, reps):
                             "frac": round(tot_b / tot_us / 1e3 / HBM_PEAK_GBS, 4),
                             "packed_bytes": tot_b, "per_launch": per,
                             "frac_of_same_grid_plain_read": round(tot_floor / tot_us, 4)}
-    print("[bench] 8B-shaped prefill MLP, M=2048", file=sys.stderr, flush=True)
-    M, per, tot_ops, tot_us = 2048, {}, 0.0, 0.0
-    for name, N, K in workloads.LAYER_8B:
-        if name not in ("gate", "down"):
-            continue
-        W = workloads.latent_weights(N, K, seed=0).to(dev)
-        p, s = bw.pack_weights(W)
-        del W
-        R = max(2, math.ceil(ROTATE_BYTES / (N * K // 4)))
-        copies = [p] + [p.clone() for _ in range(R - 1)]
-        xq, a = bw.quant_act(workloads.activations(M, K, seed=0, outliers=True).to(dev))
-        o = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        us = graph_launch_us(torch, lambda r: bw.gemm(xq, a, copies[r], s, "bf16", out=o), R, reps)
-        ops = 2.0 * M * N * K
-        per[name] = {"us": round(us, 3), "TFLOP/s": round(ops / us / 1e6, 1)}
-        tot_ops += ops
-        tot_us += us
-        del copies, p
-        torch.cuda.empty_cache()
-    out["prefill_8b_m2048"] = {"bound": "mfma", "achieved": round(tot_ops / tot_us / 1e6, 1),
-                               "peak": INT8_MFMA_PEAK_TOPS, "unit": "TFLOP/s",
-                               "frac": round(tot_ops / tot_us / 1e6 / INT8_MFMA_PEAK_TOPS, 4),
-                               "per_shape": per}
     # the decode MLP as two launches: gate|up with the SwiGLU epilogue (h in bf16), then
     # down on h (fused quant + GEMV); 2B shapes, M = 1
     print("[bench] 2B decode MLP chain, M=1", file=sys.stderr, flush=True)
@@ -431,22 +525,23 @@ def bench_extras(bw, workloads, torch, dev, reps):
     for seed, name, (N, K) in ((0, "gate", (Ni, Kh)), (1, "up", (Ni, Kh)), (2, "down", (Nd, Kd))):
         mats[name] = bw.pack_weights(workloads.latent_weights(N, K, seed=seed).to(dev))
     nbytes = (2 * Ni * Kh + Nd * Kd) // 4
-    R = max(2, math.ceil(ROTATE_BYTES / nbytes))
-    copies = [mats] + [{k: (v[0].clone(), v[1]) for k, v in mats.items()} for _ in range(R - 1)]
+    order = ("gate", "up", "down")
+    cp = rotation([mats[k][0] for k in order], nbytes)
+    R = len(cp)
     x = workloads.activations(1, Kh, seed=0, outliers=True).to(dev)
     h = torch.empty((1, Ni), dtype=torch.bfloat16, device=dev)
     y = torch.empty((1, Nd), dtype=torch.float32, device=dev)
 
     def mlp(r):
-        c = copies[r]
-        bw.quant_gemv_swiglu(x, c["gate"][0], c["gate"][1], c["up"][0], c["up"][1], "bf16", out=h)
-        bw.quant_gemv(h, c["down"][0], c["down"][1], "f32", out=y)
+        g, u, d = cp[r]
+        bw.quant_gemv_swiglu(x, g, mats["gate"][1], u, mats["up"][1], "bf16", out=h)
+        bw.quant_gemv(h, d, mats["down"][1], "f32", out=y)
 
     us = graph_launch_us(torch, mlp, R, reps)
     out["mlp_decode_2b_m1"] = {"launches": 2, "us": round(us, 3),
                                "packed_GB/s": round(nbytes / us / 1e3, 1),
                                "packed_bytes": nbytes}
-    del copies, mats
+    del cp, mats
     torch.cuda.empty_cache()
 
     # bf16 activations times ternary weights (no activation quantization), 2B set at M = 1
@@ -454,22 +549,22 @@ def bench_extras(bw, workloads, torch, dev, reps):
     per, tot_b, tot_us = {}, 0, 0.0
     for name, N, K in workloads.LAYER_2B:
         p, sc = bw.pack_weights(workloads.latent_weights(N, K, seed=0).to(dev))
-        R = max(2, math.ceil(ROTATE_BYTES / (N * K // 4)))
-        copies = [p] + [p.clone() for _ in range(R - 1)]
+        cp = rotation([p], N * K // 4)
         x = workloads.activations(1, K, seed=0, outliers=True).to(dev)
         o = torch.empty((1, N), dtype=torch.float32, device=dev)
-        us = graph_launch_us(torch, lambda r: bw.a16_gemv(x, copies[r], sc, "f32", out=o), R, reps)
+        us = graph_launch_us(torch, lambda r: bw.a16_gemv(x, cp[r][0], sc, "f32", out=o),
+                             len(cp), reps)
         per[name] = round(us, 3)
         tot_b += N * K // 4
         tot_us += us
-        del copies, p
-    torch.cuda.empty_cache()
+        del cp, p
+        torch.cuda.empty_cache()
     out["a16_decode_2b_m1"] = {"achieved_GB/s": round(tot_b / tot_us / 1e3, 1),
                                "per_shape_us": per}
 
     # what this chip sustains (context for the fractions above)
     print("[bench] ceilings", file=sys.stderr, flush=True)
-    mfma = ceilings.mfma_i8_tops(torch, dev)
+    mfma, ghz = ceilings.mfma_i8_tops(torch, dev)
     read = ceilings.hbm_read_gbs(torch, dev)
     vendor = {f"{M}x{N}x{K}": (None if t is None else round(t, 1)) for (M, N, K), t in
               (((M, N, K), ceilings.vendor_int8_gemm_tops(torch, dev, M, N, K))
@@ -477,6 +572,9 @@ def bench_extras(bw, workloads, torch, dev, reps):
     out["ceilings"] = {
         "mfma_i8_register_loop_tops": round(mfma, 1),
         "mfma_i8_register_loop_frac_of_peak": round(mfma / INT8_MFMA_PEAK_TOPS, 4),
+        "mfma_i8_register_loop_core_clock_ghz": None if ghz is None else round(ghz, 3),
+        "mfma_i8_peak_at_that_clock_tops": (None if ghz is None else
+                                            round(INT8_MFMA_PEAK_TOPS * ghz / 2.4, 1)),
         "hbm_stream_read_2GiB_gbs": round(read, 1),
         "hbm_stream_read_frac_of_peak": round(read / HBM_PEAK_GBS, 4),
         "vendor_int8_gemm_tops_dense_int8_weights": vendor,
@@ -484,7 +582,7 @@ def bench_extras(bw, workloads, torch, dev, reps):
     return out
 
 
-def bench_gemm(bw, workloads, torch, np, dev, layer, R_bytes, reps, probe=False):
+def bench_gemm(bw, workloads, torch, dev, layer, reps, probe=False):
     M = 512
     print(f"[bench] prefill M={M}", file=sys.stderr, flush=True)
     packed0, scales, xs, xqs, avs, outs = [], [], [], [], [], []
@@ -501,42 +599,41 @@ def bench_gemm(bw, workloads, torch, np, dev, layer, R_bytes, reps, probe=False)
         avs.append(a)
         outs.append(torch.empty((M, N), dtype=torch.bfloat16, device=dev))
     set_bytes = sum(N * K // 4 for _, N, K in layer)
-    R = max(2, math.ceil(R_bytes / set_bytes))
-    copies = [packed0] + [[p.clone() for p in packed0] for _ in range(R - 1)]
     ops = sum(2.0 * M * N * K for _, N, K in layer)
 
     # projections that read the same activations share one quantization (q|k|v, gate|up)
     index = {name: i for i, (name, _, _) in enumerate(layer)}
     groups = [[index[n] for n in grp] for grp in workloads.DECODE_GROUPS]
 
-    def grouped(r, grp):
+    def grouped(c, grp):
+        """One grouped launch of grp on weight list c (by layer index)."""
         i0 = grp[0]
-        return bw.gemm_grouped(xqs[i0], avs[i0], [copies[r][i] for i in grp],
+        return bw.gemm_grouped(xqs[i0], avs[i0], [c[i] for i in grp],
                                [scales[i] for i in grp], "bf16", out=[outs[i] for i in grp])
+
+    def group_copies(grp):
+        cp = rotation([packed0[i] for i in grp], sum(layer[i][1] * layer[i][2] // 4 for i in grp))
+        return [dict(zip(grp, c)) for c in cp]
+
+    if probe:
+        # counter collection: the calibration copies, then the four grouped GEMM launches
+        # once per weight copy of the whole set (weights from HBM), eagerly
+        copies = rotation(packed0, set_bytes)
+        calibration_copies(torch, dev)
+        for c in copies:
+            for grp in groups:
+                grouped(c, grp)
+        torch.cuda.synchronize()
+        print(f"[bench] gemm probe: {len(copies)} prefill steps", file=sys.stderr)
+        return None
+
+    copies = rotation(packed0, set_bytes)
 
     def step(r):
         for grp in groups:
             i0 = grp[0]
             bw.quant_act(xs[i0], xq=xqs[i0], a_scale=avs[i0])
-            grouped(r, grp)
-
-    if probe:
-        # counter collection: the calibration copies of the traffic probe, then the four
-        # grouped GEMM launches once per weight copy (weights from HBM), eagerly
-        from ternary_weight_linear_token_amd import profiling
-        n = profiling.COPY_BYTES // 4
-        src = torch.arange(n, dtype=torch.int32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            torch.neg(src, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
-        for r in range(R):
-            for grp in groups:
-                grouped(r, grp)
-        torch.cuda.synchronize()
-        print(f"[bench] gemm probe: {R} prefill steps", file=sys.stderr)
-        return None
+            grouped(copies[r], grp)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -544,13 +641,26 @@ def bench_gemm(bw, workloads, torch, np, dev, layer, R_bytes, reps, probe=False)
         step(0)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    ms_step = run_steps(torch, step, R, 3, 40)
+    ms_step = run_steps(torch, step, len(copies), 3, 40)
+    del copies
+    torch.cuda.empty_cache()
 
-    per_group_us = [graph_launch_us(torch, lambda r, grp=grp: grouped(r, grp), R, reps)
-                    for grp in groups]
-    per_shape_us = [graph_launch_us(torch, lambda r, i=i: bw.gemm(
-        xqs[i], avs[i], copies[r][i], scales[i], "bf16", out=outs[i]), R, reps)
-        for i in range(len(layer))]
+    per_group_us = []
+    for grp in groups:
+        cp = group_copies(grp)
+        per_group_us.append(graph_launch_us(torch, lambda r, grp=grp: grouped(cp[r], grp),
+                                            len(cp), reps))
+        del cp
+    per_shape_us = []
+    for i in range(len(layer)):
+        cp = group_copies([i])
+        per_shape_us.append(graph_launch_us(torch, lambda r, i=i: bw.gemm(
+            xqs[i], avs[i], cp[r][i], scales[i], "bf16", out=outs[i]), len(cp), reps))
+        del cp
+    torch.cuda.empty_cache()
+    quant_us = {"|".join(g): round(graph_launch_us(
+        torch, lambda r, i0=index[g[0]]: bw.quant_act(xs[i0], xq=xqs[i0], a_scale=avs[i0]), 8,
+        reps), 3) for g in workloads.DECODE_GROUPS}
     tops = ops / (sum(per_group_us) * 1e-6) / 1e12
     # context: the vendor int8 GEMM (hipBLASLt, dense int8 weights) on the same four
     # products (each group's matrices concatenated along N)
@@ -564,6 +674,8 @@ def bench_gemm(bw, workloads, torch, np, dev, layer, R_bytes, reps, probe=False)
         vendor_us = None if (t is None or vendor_us is None) else vendor_us + 2.0 * M * N * K / t / 1e6
     from ternary_weight_linear_token_amd import build as bw_build
     counters = load_summary(GEMM_COUNTERS_FILE, bw_build.kernel_hash("tiled.hip"))
+    alg_bytes = sum(N * K // 4 + 4 * N + 2 * M * N for _, N, K in layer) + sum(
+        M * layer[g[0]][2] + 4 * M for g in groups)
     return {
         "metric": "GEMM int8 TOPS at M=512 (prefill layer set, bf16 out)",
         "workload": "bitnet-2b-prefill-layer-set",
@@ -574,6 +686,7 @@ def bench_gemm(bw, workloads, torch, np, dev, layer, R_bytes, reps, probe=False)
         "step": "one quant_act + one grouped tiled GEMM per shared input (q|k|v, o, gate|up, "
                 "down)",
         "ms_per_step_incl_quant": round(ms_step, 4),
+        "quant_act_us": quant_us,
         "value_ungrouped": round(ops / (sum(per_shape_us) * 1e-6) / 1e12, 2),
         "vendor_int8_gemm_same_products_tops": (None if vendor_us is None else
                                                 round(ops / (vendor_us * 1e-6) / 1e12, 2)),
@@ -583,6 +696,8 @@ def bench_gemm(bw, workloads, torch, np, dev, layer, R_bytes, reps, probe=False)
             "peak": INT8_MFMA_PEAK_TOPS,
             "unit": "TFLOP/s",
             "frac": round(tops / INT8_MFMA_PEAK_TOPS, 4),
+            "attainable_TOPS": round(min(INT8_MFMA_PEAK_TOPS,
+                                         ops / alg_bytes * HBM_PEAK_GBS / 1e3), 1),
             "traffic": float(counters["hbm_bytes_per_launch"]) if counters else None,
             "mfma_busy_frac_counters": (float(counters["mfma_busy_frac_weighted"])
                                         if counters else None),

@@ -19,10 +19,12 @@ def _probes():
             _build.build_probes()
         L = ctypes.CDLL(_build.PROBES_LIB)
         p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
-        L.bitnet_probe_mfma_i8.argtypes = [p, p, i32, i32, p]
+        L.bitnet_probe_mfma_i8.argtypes = [p, p, p, i32, i32, p]
         L.bitnet_probe_mfma_i8.restype = i32
         L.bitnet_probe_mfma_i8_ops.argtypes = [i32, i32]
         L.bitnet_probe_mfma_i8_ops.restype = ctypes.c_double
+        L.bitnet_probe_wall_clock_hz.argtypes = []
+        L.bitnet_probe_wall_clock_hz.restype = ctypes.c_double
         L.bitnet_probe_read.argtypes = [p, i64, p, i32, p]
         L.bitnet_probe_read.restype = i32
         _lib = L
@@ -43,21 +45,30 @@ def _time_us(torch, fn, reps):
 
 
 def mfma_i8_tops(torch, dev, blocks=2048, iters=2000, reps=5):
-    """int8 MFMA throughput (TOPS) of a register-only loop, seeded random operands."""
+    """int8 MFMA throughput (TOPS) of a register-only loop, seeded random operands, and the
+    core clock (GHz) the waves sustained during it (median over waves of core cycles per
+    wall-counter tick times the wall counter's rate; None if the rate is unknown)."""
     L = _probes()
     g = torch.Generator().manual_seed(1)
     seed = torch.randint(-2**31, 2**31 - 1, (4096,), generator=g, dtype=torch.int64)
     seed = seed.to(torch.int32).to(dev)
     out = torch.empty((blocks * 256,), dtype=torch.int32, device=dev)
+    clk = torch.zeros((blocks * 4 * 2,), dtype=torch.int64, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
 
     def run():
-        rc = L.bitnet_probe_mfma_i8(seed.data_ptr(), out.data_ptr(), blocks, iters, stream)
+        rc = L.bitnet_probe_mfma_i8(seed.data_ptr(), out.data_ptr(), clk.data_ptr(), blocks,
+                                    iters, stream)
         if rc:
             raise RuntimeError(f"bitnet_probe_mfma_i8: hip error {rc}")
 
     us = _time_us(torch, run, reps)
-    return L.bitnet_probe_mfma_i8_ops(blocks, iters) / us / 1e6
+    c = clk.view(-1, 2).cpu().double()
+    wall_hz = L.bitnet_probe_wall_clock_hz()
+    ghz = None
+    if wall_hz > 0 and bool((c[:, 1] > 0).all()):
+        ghz = float((c[:, 0] / c[:, 1]).median()) * wall_hz / 1e9
+    return L.bitnet_probe_mfma_i8_ops(blocks, iters) / us / 1e6, ghz
 
 
 def hbm_read_gbs(torch, dev, nbytes=2 << 30, blocks=2048, reps=5):

@@ -327,7 +327,8 @@ def test_ceiling_probes_library_exports():
     if not os.path.exists(b.PROBES_LIB):
         b.build_probes()
     L = ctypes.CDLL(b.PROBES_LIB)
-    for name in ("bitnet_probe_mfma_i8", "bitnet_probe_mfma_i8_ops", "bitnet_probe_read"):
+    for name in ("bitnet_probe_mfma_i8", "bitnet_probe_mfma_i8_ops", "bitnet_probe_read",
+                 "bitnet_probe_wall_clock_hz"):
         assert hasattr(L, name), name
     L.bitnet_probe_mfma_i8_ops.restype = ctypes.c_double
     L.bitnet_probe_mfma_i8_ops.argtypes = [ctypes.c_int, ctypes.c_int]

@@ -58,6 +58,14 @@ def latent_weights(N: int, K: int, seed: int = 0) -> torch.Tensor:
     return 0.02 * torch.randn(N, K, generator=g, dtype=torch.float32)
 
 
+def latent_weights_on(device, N: int, K: int, seed: int = 0):
+    """The same distribution as latent_weights, drawn on `device` by its own seeded
+    generator (a different stream of numbers: for timing runs, where only the shape and
+    the distribution matter and host-side draws of 10^8 values would dominate)."""
+    g = torch.Generator(device=device).manual_seed(seed)
+    return 0.02 * torch.randn(N, K, generator=g, dtype=torch.float32, device=device)
+
+
 def activations(M: int, K: int, seed: int = 0, outliers: bool = True) -> torch.Tensor:
     """bf16 activations ~ N(0, 1), with 1% of channels scaled by 20, shape (M, K), CPU."""
     g = torch.Generator().manual_seed(seed + 1)
