@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define BITNET_ABI_VERSION 1
+#define BITNET_ABI_VERSION 2
 /* Largest supported K: keeps every int32 partial sum exact with margin. */
 #define BITNET_MAX_K (1 << 20)
 
@@ -61,7 +61,7 @@ typedef enum {
     BITNET_OK = 0,
     BITNET_ERR_INVALID_ARG = 1, /* null pointer, negative size, K == 0, bad enum, M range */
     BITNET_ERR_UNALIGNED = 2,   /* K % 4 != 0, or a pointer not 16-byte aligned          */
-    BITNET_ERR_WORKSPACE = 3,   /* workspace smaller than the size query returned         */
+    BITNET_ERR_WORKSPACE = 3,   /* device scratch too small for the call                  */
     BITNET_ERR_HIP = 4,         /* a HIP runtime call or kernel launch failed             */
     BITNET_ERR_DEVICE = 5       /* the current device is not gfx950                       */
 } bitnet_status;
@@ -172,9 +172,17 @@ int bitnet_w2a8_gemv(const int8_t* xq, const float* a_scale, const uint8_t* pack
  *   algo : which kernel (bitnet_algo); an addition to the plain product signature that
  *          only selects among kernels with identical results.  BITNET_ALGO_SKINNY with
  *          M > BITNET_SKINNY_MAX_M returns BITNET_ERR_INVALID_ARG.
- * Workspace: reserved for kernels that need device scratch.  This version needs none:
- * bitnet_w2a8_gemm_workspace_size returns 0 and workspace may be NULL with ws_bytes 0
- * (a larger caller buffer is accepted and left untouched).
+ * Workspace (optional, caller-owned device memory, 16-byte aligned): when the tiled
+ * kernel runs and ws_bytes >= bitnet_w2a8_gemm_workspace_size(M, N, K) > 0, K is split
+ * into slices taken by different blocks -- for grids with too few output tiles to fill
+ * the chip, e.g. a few dozen tokens times a large K -- each writing its int32 partial
+ * sums into the workspace, and a second launch adds the slices (exact in int32) and
+ * rescales.  With a smaller workspace (or NULL and 0) the call runs unsplit.  Outputs are
+ * bit-identical either way.  The workspace is scratch: its contents on return are
+ * unspecified, and calls that share one must be ordered (e.g. on one stream).
+ * ws_bytes > 0 with workspace NULL returns BITNET_ERR_INVALID_ARG.
+ * bitnet_w2a8_gemm_workspace_size returns 0 for invalid sizes and when the best plan on
+ * the current device does not split (then no workspace is ever used).
  */
 size_t bitnet_w2a8_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
 int bitnet_w2a8_gemm(const int8_t* xq, const float* a_scale, const uint8_t* packed,
@@ -205,15 +213,18 @@ int bitnet_w2a8_gemm_grouped(const int8_t* xq, const float* a_scale, int64_t M, 
                              int out_dtype, void* stream);
 
 /*
- * bitnet_w2a8_gemm_plan -- the tile plan a tiled launch (BITNET_ALGO_TILED, or
- * bitnet_w2a8_gemm_grouped) takes for M tokens, K columns and `groups` weight matrices of
- * N[g] rows (HOST array), on a device with `cus` compute units (cus <= 0: the current
- * device's; with no device the count defaults to 256).  Host-only: launches nothing.
- *   plan : HOST int32[4] output = block rows, block columns, k-groups per block (waves
- *          per block / 4), k per LDS stage.
- * The plan is the compiled tile configuration with the least estimated time (rounds of
- * one block per CU times a per-configuration cost fitted on this chip); the environment
- * variable BITNET_TILED_CONFIG="bm,bn,g" (read once per process) overrides the shape.
+ * bitnet_w2a8_gemm_plan -- the tile plan a tiled launch takes for M tokens, K columns and
+ * `groups` weight matrices of N[g] rows (HOST array), on a device with `cus` compute
+ * units (cus <= 0: the current device's; with no device the count defaults to 256):
+ * groups == 1 describes bitnet_w2a8_gemm (BITNET_ALGO_TILED, or the tiled route of
+ * BITNET_ALGO_AUTO) given its workspace, groups > 1 bitnet_w2a8_gemm_grouped, which never
+ * splits K.  Host-only: launches nothing.
+ *   plan : HOST int32[5] output = block rows, block columns, k-groups per block (waves
+ *          per block / 4), k per LDS stage, slices of K across blocks (1: unsplit).
+ * The plan is the compiled tile configuration and K split with the least estimated time
+ * (rounds of one block per CU times a per-configuration cost fitted on this chip, plus
+ * the reduce launch of a split); the environment variable BITNET_TILED_CONFIG="bm,bn,g"
+ * or "bm,bn,g,slices" (read once per process) overrides the choice.
  * Returns BITNET_ERR_INVALID_ARG for M < 1, groups outside 1..BITNET_MAX_GROUPS, N[g] < 0,
  * no rows at all, or NULL arrays; BITNET_ERR_UNALIGNED for K % 4 != 0.
  */

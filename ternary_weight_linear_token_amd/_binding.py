@@ -222,20 +222,22 @@ def gemv(xq, a_scale, packed, w_scale, out_dtype="f32", out=None):
 def gemm(xq, a_scale, packed, w_scale, out_dtype="f32", algo="auto", out=None, workspace=None):
     """Product for any M: int8 xq x packed ternary -> (M, N).
 
-    The library's size query (bitnet_w2a8_gemm_workspace_size) decides whether a device
-    workspace is needed; a uint8 tensor of at least that many bytes may be passed in,
-    and when the query returns 0 (every kernel of this version) none is allocated."""
+    workspace: a uint8 device tensor the call may use to split K across blocks (int32
+    partial sums); by default one of the size the library asks for
+    (bitnet_w2a8_gemm_workspace_size) is allocated when that size is not 0.  Pass
+    workspace=False to run without one (unsplit; the same result)."""
     M, K = xq.shape
     N = packed.shape[0]
     code = _out_code(out_dtype)
     algo_code = _ALGO_NAMES[algo] if isinstance(algo, str) else int(algo)
     out = _alloc_out(out, M, N, code, xq.device)
     stream = _stream(xq)
-    ws_need = int(lib().bitnet_w2a8_gemm_workspace_size(M, N, K))
-    if workspace is None and ws_need:
-        workspace = torch.empty((ws_need,), dtype=torch.uint8, device=xq.device)
+    if workspace is None:
+        ws_need = int(lib().bitnet_w2a8_gemm_workspace_size(M, N, K))
+        if ws_need:
+            workspace = torch.empty((ws_need,), dtype=torch.uint8, device=xq.device)
     ws_ptr, ws_bytes = None, 0
-    if workspace is not None:
+    if workspace is not None and workspace is not False:
         ws_ptr = _tensor(workspace, torch.uint8, "workspace")
         ws_bytes = workspace.numel()
     _check(lib().bitnet_w2a8_gemm(_tensor(xq, torch.int8, "xq", (M, K)),
@@ -280,11 +282,12 @@ def gemm_grouped(xq, a_scale, packed, w_scale, out_dtype="f32", out=None):
 
 
 def gemm_plan(M, K, Ns, cus=0):
-    """Tile plan (block rows, block columns, k-groups, k per stage) of a tiled launch over
-    weight matrices of Ns rows; host-only."""
+    """Tile plan (block rows, block columns, k-groups, k per stage, K slices) of a tiled
+    launch over weight matrices of Ns rows (one matrix: gemm with its workspace; several:
+    gemm_grouped, never split); host-only."""
     G = len(Ns)
     NN = (ctypes.c_int64 * max(G, 1))(*[int(n) for n in Ns])
-    out = (ctypes.c_int32 * 4)()
+    out = (ctypes.c_int32 * 5)()
     _check(lib().bitnet_w2a8_gemm_plan(int(M), int(K), G, ctypes.cast(NN, ctypes.c_void_p),
                                        int(cus), ctypes.cast(out, ctypes.c_void_p)),
            "bitnet_w2a8_gemm_plan")

@@ -160,7 +160,6 @@ int bitnet_w2a8_gemm(const int8_t* xq, const float* a_scale, const uint8_t* pack
     if (algo == BITNET_ALGO_SKINNY && M > BITNET_SKINNY_MAX_M) return BITNET_ERR_INVALID_ARG;
     if (M == 0 || N == 0) return BITNET_OK;
     if (!xq || !a_scale || !packed || !w_scale || !out) return BITNET_ERR_INVALID_ARG;
-    if (ws_bytes < bitnet_w2a8_gemm_workspace_size(M, N, K)) return BITNET_ERR_WORKSPACE;
     if (ws_bytes > 0 && !workspace) return BITNET_ERR_INVALID_ARG;
     if (!aligned16(xq) || !aligned16(a_scale) || !aligned16(packed) || !aligned16(w_scale) ||
         !aligned16(out) || !aligned16(workspace))
@@ -191,7 +190,7 @@ int bitnet_w2a8_gemm(const int8_t* xq, const float* a_scale, const uint8_t* pack
                                                     as_stream(stream)));
     }
     return record_hip(bitnet::launch_tiled(xq, a_scale, packed, w_scale, M, N, K, out, out_dtype,
-                                           workspace, as_stream(stream)));
+                                           workspace, ws_bytes, as_stream(stream)));
 }
 
 int bitnet_w2a8_gemm_grouped(const int8_t* xq, const float* a_scale, int64_t M, int64_t K,
@@ -234,9 +233,9 @@ int bitnet_w2a8_gemm_plan(int64_t M, int64_t K, int64_t groups, const int64_t* N
         total_n += N[g];
     }
     if (total_n == 0 || total_n > INT32_MAX) return BITNET_ERR_INVALID_ARG;
-    int p[4];
+    int p[5];
     bitnet::tiled_plan(M, K, (int)groups, N, cus, p);
-    for (int i = 0; i < 4; ++i) plan[i] = p[i];
+    for (int i = 0; i < 5; ++i) plan[i] = p[i];
     return BITNET_OK;
 }
 

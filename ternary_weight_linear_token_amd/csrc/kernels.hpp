@@ -60,21 +60,25 @@ hipError_t launch_gemv_direct(const int8_t* xq, const float* a_scale, const uint
                               int64_t K, void* out, int out_dtype, int8_t* xq_out, float* a_out,
                               hipStream_t stream);
 
-// Tiled int8 matrix-core product for any M.  Device scratch it needs, in bytes (none:
-// every tile keeps its whole K range inside one block).
+// Tiled int8 matrix-core product for any M.  Device scratch with which a single-matrix
+// launch may split K across blocks (int32 partial tiles of every K slice), in bytes; 0
+// when the best plan does not split.
 size_t tiled_workspace_size(int64_t M, int64_t N, int64_t K);
 // The tiled product for 1 <= groups <= BITNET_MAX_GROUPS weight matrices (N[g] rows
 // each, all K columns) against the same activations, in one launch; the tile plan is
 // chosen for the launch's total tile count.
-// The tile plan of a tiled launch over `groups` matrices of N[g] rows: plan[0..3] = block
-// rows, block columns, k-groups per block, k per LDS stage; cus <= 0: the current device's.
+// The tile plan of a tiled launch over `groups` matrices of N[g] rows: plan[0..4] = block
+// rows, block columns, k-groups per block, k per LDS stage, K slices (groups == 1: the
+// plan with a workspace; more groups never split); cus <= 0: the current device's.
 void tiled_plan(int64_t M, int64_t K, int groups, const int64_t* N, int64_t cus, int* plan);
 hipError_t launch_tiled_grouped(const int8_t* xq, const float* a_scale, int groups,
                                 const uint8_t* const* packed, const float* const* w_scale,
                                 const int64_t* N, void* const* out, int64_t M, int64_t K,
                                 int out_dtype, hipStream_t stream);
+// workspace: NULL, or ws_bytes of device scratch; K is split across blocks only when
+// ws_bytes >= tiled_workspace_size(M, N, K) > 0 (the result is the same either way).
 hipError_t launch_tiled(const int8_t* xq, const float* a_scale, const uint8_t* packed,
                         const float* w_scale, int64_t M, int64_t N, int64_t K, void* out,
-                        int out_dtype, void* workspace, hipStream_t stream);
+                        int out_dtype, void* workspace, size_t ws_bytes, hipStream_t stream);
 
 }  // namespace bitnet

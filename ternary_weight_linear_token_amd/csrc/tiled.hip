@@ -71,8 +71,15 @@ struct TiledArgs {
     const float* g_wscale[kTdGroups];
     void* g_out[kTdGroups];
     int M, K;
-    int units;       // tiles of all groups
+    int units;       // tiles of all groups, times ksplit
     int units_per_xcd;
+    // split of K across blocks (one weight matrix only): unit u takes k-stages
+    // [s * split_stages, (s + 1) * split_stages) of tile u - s * (units / ksplit), s =
+    // u / (units / ksplit), and writes its int32 partial sums to g_out[0] + s * split_stride
+    // (the reduce kernel adds the ksplit partials and rescales)
+    int ksplit;
+    int split_stages;
+    int64_t split_stride;
     int gm;          // tile rows per panel of the unit order (see the kernel)
     int out_dtype;
 };
@@ -106,8 +113,12 @@ __global__ __launch_bounds__(kTdThreads * G) void tiled_kernel(TiledArgs p) {
 
     // ---- work unit of this block (XCD-contiguous) ----
     const int xcd = blockIdx.x % kXcds;
-    const int unit = xcd * p.units_per_xcd + blockIdx.x / kXcds;
-    if (unit >= p.units) return;
+    const int unit_all = xcd * p.units_per_xcd + blockIdx.x / kXcds;
+    if (unit_all >= p.units) return;
+    // split of K: the unit's slice s and its unit within the slice (scalar arithmetic)
+    const int per_split = p.units / p.ksplit;
+    const int split = unit_all / per_split;
+    const int unit = unit_all - split * per_split;
     // the unit's weight matrix: the last group whose first unit is at most `unit`
     // (scalar compares and selects on the kernel arguments)
     int first = p.first[0], N = p.g_N[0], tiles_n = p.g_tiles_n[0];
@@ -125,6 +136,7 @@ __global__ __launch_bounds__(kTdThreads * G) void tiled_kernel(TiledArgs p) {
             out = p.g_out[i];
         }
     }
+    if (DT == 2 && p.ksplit > 1) out = static_cast<int*>(out) + split * p.split_stride;
     // A group's tiles are ordered in panels of gm tile rows, column by column inside a
     // panel, so the run of consecutive units one XCD takes is a block of about gm x
     // (run / gm) tiles: its L2 holds gm activation row panels and run / gm weight column
@@ -152,7 +164,10 @@ __global__ __launch_bounds__(kTdThreads * G) void tiled_kernel(TiledArgs p) {
         reinterpret_cast<unsigned char (*)[BM * kAStride]>(smem + g * 2 * BM * kAStride);
     const int M = p.M, K = p.K;
     const int64_t row_bytes = K / 4;
-    const int nk = (K + BK - 1) / BK;
+    // the k-stages of this unit: all of K, or one slice of it when K is split
+    const int nk_all = (K + BK - 1) / BK;
+    const int k_first = split * p.split_stages;
+    const int nk = min(nk_all, k_first + p.split_stages);
 
     for (int i = (int)threadIdx.x; i < BM; i += kTdThreads * G) {
         const int m = m0 + i;
@@ -316,8 +331,8 @@ __global__ __launch_bounds__(kTdThreads * G) void tiled_kernel(TiledArgs p) {
     // Group g's stages are g, g + G, g + 2G, ...; every group runs nsteps steps, and a
     // step past the group's last stage multiplies zeros (see load_stage), so the matrix
     // products are unconditional and each step is one scheduling region.
-    const int nsteps = (nk + G - 1) / G;
-    auto stage_of = [&](int i) { return g + G * i; };
+    const int nsteps = (nk - k_first + G - 1) / G;
+    auto stage_of = [&](int i) { return k_first + g + G * i; };
     // One step: the A fragments of this step are read first; then this step's matrix
     // products are interleaved with the next step's weight unpack, the loads D steps
     // ahead and the transposed store of the next step's activations, so the vector ALU
@@ -538,8 +553,10 @@ __global__ __launch_bounds__(kTdThreads * G) void tiled_kernel(TiledArgs p) {
 }
 
 struct TilePlan {
-    int bm, bn, g;  // block tile and k-groups per block
-    int bk;         // k per LDS stage
+    int bm, bn, g;     // block tile and k-groups per block
+    int bk;            // k per LDS stage
+    int ksplit;        // slices of K across blocks (1: none)
+    int split_stages;  // k-stages per slice
 };
 
 // Compute units of the current device, queried once per device (atomics: concurrent
@@ -557,32 +574,36 @@ int device_cus() {
     return v;
 }
 
-// Optional override for tuning: BITNET_TILED_CONFIG="bm,bn,g", one of the compiled
-// configurations (256,256,1 / 256,128,1 / 128,128,2 / 64,128,4); read once
-// per process.
+// Optional override for tuning: BITNET_TILED_CONFIG="bm,bn,g" or "bm,bn,g,ksplit", one of
+// the compiled configurations (256,256,1 / 256,128,1 / 128,128,2 / 64,128,4), with an
+// optional number of K slices (used only where splitting is allowed); read once per
+// process.
 struct ConfigOverride {
     bool on = false;
-    int bm = 0, bn = 0, g = 0;
+    int bm = 0, bn = 0, g = 0, ksplit = 0;
 };
 
 const ConfigOverride& config_override() {
     static const ConfigOverride c = [] {
         ConfigOverride r;
         const char* e = std::getenv("BITNET_TILED_CONFIG");
-        int a = 0, b = 0, g = 0;
-        r.on = e && std::sscanf(e, "%d,%d,%d", &a, &b, &g) == 3 &&
+        int a = 0, b = 0, g = 0, ks = 0;
+        const int n = e ? std::sscanf(e, "%d,%d,%d,%d", &a, &b, &g, &ks) : 0;
+        r.on = n >= 3 &&
                ((a == 256 && b == 256 && g == 1) || (a == 256 && b == 128 && g == 1) ||
-                (a == 128 && b == 128 && g == 2) || (a == 64 && b == 128 && g == 4));
+                (a == 128 && b == 128 && g == 2) || (a == 64 && b == 128 && g == 4)) &&
+               (n == 3 || (ks >= 1 && ks <= 64));
         r.bm = a;
         r.bn = b;
         r.g = g;
+        r.ksplit = n == 4 ? ks : 0;
         return r;
     }();  // thread-safe initialization of a function-local static
     return c;
 }
 
 // Tile shape: the compiled configuration with the least estimated time.  Every
-// configuration runs one block per CU, so a launch takes ceil(tiles / CUs) rounds, and
+// configuration runs one block per CU, so a launch takes ceil(units / CUs) rounds, and
 // a round costs about the same whether it is full or not (a lone tile is bound by its
 // own latency, not by the matrix cores).  A round's cost is a fixed part plus a part per
 // unit of K, fitted to launches of each configuration on the 2B-shaped prefill products
@@ -591,6 +612,15 @@ const ConfigOverride& config_override() {
 // weight unpack and the activation transpose over more products per k.  128-k stages
 // (half the barriers and twice the bytes per load of 64-k stages) need K % 128 == 0;
 // the 256x256 tile keeps 64-k stages (128-k ones spill its registers).
+//
+// Where the caller provides a workspace, K may also be split into slices taken by
+// different blocks (more units per round, fewer k per unit): each unit writes its int32
+// partial tile, and a second launch adds the slices' partials (exact in int32, so the
+// result is bit-identical to the unsplit product) and rescales.  A split costs a fixed
+// part (the second launch) plus a part per byte of int32 partials (written by the first
+// launch, read by the second), fitted on M = 32 .. 256 products with K = 4096 .. 28672
+// and 1 to 16 slices: about 1 us per MB, far below streaming rate -- more active blocks
+// per round also raise every block's cost per K.
 struct TileCost {
     int bm, bn, g, bk;
     double fixed_us, per_k_us;
@@ -604,15 +634,30 @@ constexpr TileCost kTileCosts[] = {
     {256, 128, 1, 64, 7.0, 7.3e-3},
     {256, 256, 1, 64, 10.5, 11.7e-3},
 };
+constexpr double kSplitFixedUs = 1.5;      // the reduce launch
+constexpr double kSplitUsPerByte = 1.0e-6;  // per byte of int32 partials
+constexpr int kMaxSplit = 16;
+constexpr int64_t kMaxSplitBytes = int64_t(64) << 20;  // int32 partials of all slices
 
-TilePlan plan_tiles(int64_t M, int64_t K, const int64_t* N, int groups, int64_t cus) {
+TilePlan plan_tiles(int64_t M, int64_t K, const int64_t* N, int groups, int64_t cus,
+                    bool allow_split) {
     TilePlan t;
+    int64_t n_all = 0;
+    for (int i = 0; i < groups; ++i) n_all += N[i];
     const ConfigOverride& ov = config_override();
     if (ov.on) {
         t.bm = ov.bm;
         t.bn = ov.bn;
         t.g = ov.g;
         t.bk = (K % 128 == 0 && !(t.bm == 256 && t.bn == 256)) ? 128 : 64;
+        const int nk = (int)((K + t.bk - 1) / t.bk);
+        const int ks = allow_split && ov.ksplit > 1 ? ov.ksplit : 1;
+        t.split_stages = (nk + ks - 1) / ks;
+        t.ksplit = (nk + t.split_stages - 1) / t.split_stages;  // no empty slice
+        if (t.ksplit > 1 && t.ksplit * M * n_all * 4 > kMaxSplitBytes) {
+            t.ksplit = 1;
+            t.split_stages = nk;
+        }
         return t;
     }
     double best = -1.0;
@@ -621,20 +666,123 @@ TilePlan plan_tiles(int64_t M, int64_t K, const int64_t* N, int groups, int64_t 
         int64_t tiles_n = 0;
         for (int i = 0; i < groups; ++i) tiles_n += (N[i] + c.bn - 1) / c.bn;
         const int64_t tiles = ((M + c.bm - 1) / c.bm) * tiles_n;
-        const double est = (double)((tiles + cus - 1) / cus) * (c.fixed_us + c.per_k_us * (double)K);
-        if (best < 0.0 || est < best) {
-            best = est;
-            t.bm = c.bm;
-            t.bn = c.bn;
-            t.g = c.g;
-            t.bk = c.bk;
+        const int nk = (int)((K + c.bk - 1) / c.bk);
+        for (int ks = 1; ks <= (allow_split ? kMaxSplit : 1); ++ks) {
+            const int stages = (nk + ks - 1) / ks;
+            const int slices = (nk + stages - 1) / stages;
+            if (slices != ks) continue;                     // a slice would be empty
+            if (ks > 1 && stages < c.g) break;              // k-groups without a stage
+            const int64_t part_bytes = (int64_t)ks * M * n_all * 4;
+            if (ks > 1 && part_bytes > kMaxSplitBytes) break;
+            const int64_t units = tiles * ks;
+            double est = (double)((units + cus - 1) / cus) *
+                         (c.fixed_us + c.per_k_us * (double)stages * c.bk);
+            if (ks > 1) est += kSplitFixedUs + kSplitUsPerByte * (double)part_bytes;
+            if (best < 0.0 || est < best) {
+                best = est;
+                t.bm = c.bm;
+                t.bn = c.bn;
+                t.g = c.g;
+                t.bk = c.bk;
+                t.ksplit = ks;
+                t.split_stages = stages;
+            }
         }
     }
     return t;
 }
 
+// Adds the ksplit int32 partial products of every output (slice s at part + s * stride)
+// in slice order -- exact, so any order gives the same sum -- and rescales like the tiled
+// epilogue: ((float)acc * w_scale[n]) * (1 / a_scale[m]).  VEC: N % 4 == 0, four
+// consecutive outputs of one row per thread; else one output per thread.
+template <int DT, bool VEC>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const int* __restrict__ part, int ksplit,
+                                                            int64_t stride, int M, int N,
+                                                            const float* __restrict__ a_scale,
+                                                            const float* __restrict__ w_scale,
+                                                            void* __restrict__ out) {
+    constexpr int V = VEC ? 4 : 1;
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * V;  // first output
+    if (i >= (int64_t)M * N) return;
+    const int m = (int)(i / N), n = (int)(i - (int64_t)m * N);
+    // every slice's load is issued before the first add (the loop is unrolled over the
+    // largest slice count, the slice test is uniform), so the reads overlap
+    int acc[V];
+    if constexpr (VEC) {
+        int4 v[kMaxSplit];
+#pragma unroll
+        for (int s = 0; s < kMaxSplit; ++s)
+            if (s < ksplit) v[s] = *reinterpret_cast<const int4*>(part + s * stride + i);
+        int4 sum = v[0];
+#pragma unroll
+        for (int s = 1; s < kMaxSplit; ++s) {
+            if (s < ksplit) {
+                sum.x += v[s].x;
+                sum.y += v[s].y;
+                sum.z += v[s].z;
+                sum.w += v[s].w;
+            }
+        }
+        acc[0] = sum.x;
+        acc[1] = sum.y;
+        acc[2] = sum.z;
+        acc[3] = sum.w;
+    } else {
+        int v[kMaxSplit];
+#pragma unroll
+        for (int s = 0; s < kMaxSplit; ++s)
+            if (s < ksplit) v[s] = part[s * stride + i];
+        int sum = v[0];
+#pragma unroll
+        for (int s = 1; s < kMaxSplit; ++s)
+            if (s < ksplit) sum += v[s];
+        acc[0] = sum;
+    }
+    if constexpr (DT == 2) {
+        if constexpr (VEC)
+            *reinterpret_cast<int4*>(static_cast<int*>(out) + i) = make_int4(acc[0], acc[1], acc[2], acc[3]);
+        else
+            static_cast<int*>(out)[i] = acc[0];
+        return;
+    }
+    const float inv_a = 1.0f / a_scale[m];
+    float f[V];
+#pragma unroll
+    for (int t = 0; t < V; ++t) f[t] = ((float)acc[t] * w_scale[n + t]) * inv_a;
+    if constexpr (DT == 0) {
+        if constexpr (VEC)
+            *reinterpret_cast<float4*>(static_cast<float*>(out) + i) = make_float4(f[0], f[1], f[2], f[3]);
+        else
+            static_cast<float*>(out)[i] = f[0];
+    } else {
+        if constexpr (VEC)
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + i) =
+                make_uint2(f32x2_to_bf16x2_rne(f[0], f[1]), f32x2_to_bf16x2_rne(f[2], f[3]));
+        else
+            static_cast<uint16_t*>(out)[i] = f32_to_bf16_rne(f[0]);
+    }
+}
+
+template <int DT>
+hipError_t launch_reduce(const int* part, int ksplit, int M, int N, const float* a_scale,
+                         const float* w_scale, void* out, hipStream_t stream) {
+    const int64_t total = (int64_t)M * N;
+    const bool vec = N % 4 == 0;
+    const int64_t threads = vec ? total / 4 : total;
+    const dim3 grid((unsigned)((threads + 255) / 256));
+    if (vec)
+        hipLaunchKernelGGL((splitk_reduce_kernel<DT, true>), grid, dim3(256), 0, stream, part, ksplit,
+                           total, M, N, a_scale, w_scale, out);
+    else
+        hipLaunchKernelGGL((splitk_reduce_kernel<DT, false>), grid, dim3(256), 0, stream, part, ksplit,
+                           total, M, N, a_scale, w_scale, out);
+    return hipGetLastError();
+}
+
 template <int BM, int BN, int D, int G, int WGN, int BK>
-hipError_t launch_plan(TiledArgs a, const int64_t* N, hipStream_t stream) {
+hipError_t launch_plan(TiledArgs a, const int64_t* N, const TilePlan& t, int* part,
+                       hipStream_t stream) {
     const bool aligned = (a.K % BK) == 0;
     const int tiles_m = (a.M + BM - 1) / BM;
     int units = 0;
@@ -644,8 +792,20 @@ hipError_t launch_plan(TiledArgs a, const int64_t* N, hipStream_t stream) {
         a.g_tiles_n[i] = tn;
         units += tiles_m * tn;
     }
-    a.units = units;
     if (units == 0) return hipSuccess;
+    const bool split = t.ksplit > 1;
+    void* const final_out = a.g_out[0];
+    const int final_dtype = a.out_dtype;
+    a.ksplit = t.ksplit;
+    a.split_stages = t.split_stages;
+    a.split_stride = split ? (int64_t)a.M * a.g_N[0] : 0;
+    if (split) {
+        // the units write int32 partial tiles into the workspace; the reduce launch
+        // below adds them and writes the requested output
+        a.g_out[0] = part;
+        a.out_dtype = 2;
+    }
+    a.units = units * t.ksplit;
     a.units_per_xcd = (a.units + kXcds - 1) / kXcds;
     // panel height: an XCD's run of units_per_xcd tiles as gm rows by units_per_xcd / gm
     // columns reads gm * BM * K activation bytes and (units_per_xcd / gm) * BN * K / 4
@@ -662,40 +822,29 @@ hipError_t launch_plan(TiledArgs a, const int64_t* N, hipStream_t stream) {
             case 1: hipLaunchKernelGGL((tiled_kernel<BM, BN, D, G, WGN, BK, true, 1>), grid, blk, 0, stream, a); break;
             default: hipLaunchKernelGGL((tiled_kernel<BM, BN, D, G, WGN, BK, true, 2>), grid, blk, 0, stream, a); break;
         }
-        return hipGetLastError();
+    } else {
+        switch (a.out_dtype * 2 + (aligned ? 1 : 0)) {
+            case 0: hipLaunchKernelGGL((tiled_kernel<BM, BN, D, G, WGN, BK, false, 0>), grid, blk, 0, stream, a); break;
+            case 1: hipLaunchKernelGGL((tiled_kernel<BM, BN, D, G, WGN, BK, true, 0>), grid, blk, 0, stream, a); break;
+            case 2: hipLaunchKernelGGL((tiled_kernel<BM, BN, D, G, WGN, BK, false, 1>), grid, blk, 0, stream, a); break;
+            case 3: hipLaunchKernelGGL((tiled_kernel<BM, BN, D, G, WGN, BK, true, 1>), grid, blk, 0, stream, a); break;
+            case 4: hipLaunchKernelGGL((tiled_kernel<BM, BN, D, G, WGN, BK, false, 2>), grid, blk, 0, stream, a); break;
+            default: hipLaunchKernelGGL((tiled_kernel<BM, BN, D, G, WGN, BK, true, 2>), grid, blk, 0, stream, a); break;
+        }
     }
-    switch (a.out_dtype * 2 + (aligned ? 1 : 0)) {
-        case 0: hipLaunchKernelGGL((tiled_kernel<BM, BN, D, G, WGN, BK, false, 0>), grid, blk, 0, stream, a); break;
-        case 1: hipLaunchKernelGGL((tiled_kernel<BM, BN, D, G, WGN, BK, true, 0>), grid, blk, 0, stream, a); break;
-        case 2: hipLaunchKernelGGL((tiled_kernel<BM, BN, D, G, WGN, BK, false, 1>), grid, blk, 0, stream, a); break;
-        case 3: hipLaunchKernelGGL((tiled_kernel<BM, BN, D, G, WGN, BK, true, 1>), grid, blk, 0, stream, a); break;
-        case 4: hipLaunchKernelGGL((tiled_kernel<BM, BN, D, G, WGN, BK, false, 2>), grid, blk, 0, stream, a); break;
-        default: hipLaunchKernelGGL((tiled_kernel<BM, BN, D, G, WGN, BK, true, 2>), grid, blk, 0, stream, a); break;
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !split) return e;
+    switch (final_dtype) {
+        case 0: return launch_reduce<0>(part, t.ksplit, a.M, a.g_N[0], a.a_scale, a.g_wscale[0], final_out, stream);
+        case 1: return launch_reduce<1>(part, t.ksplit, a.M, a.g_N[0], a.a_scale, a.g_wscale[0], final_out, stream);
+        default: return launch_reduce<2>(part, t.ksplit, a.M, a.g_N[0], a.a_scale, a.g_wscale[0], final_out, stream);
     }
-    return hipGetLastError();
 }
 
-}  // namespace
-
-size_t tiled_workspace_size(int64_t M, int64_t N, int64_t K) {
-    (void)M;
-    (void)N;
-    (void)K;
-    return 0;
-}
-
-void tiled_plan(int64_t M, int64_t K, int groups, const int64_t* N, int64_t cus, int* plan) {
-    const TilePlan t = plan_tiles(M, K, N, groups, cus > 0 ? cus : device_cus());
-    plan[0] = t.bm;
-    plan[1] = t.bn;
-    plan[2] = t.g;
-    plan[3] = t.bk;
-}
-
-hipError_t launch_tiled_grouped(const int8_t* xq, const float* a_scale, int groups,
-                                const uint8_t* const* packed, const float* const* w_scale,
-                                const int64_t* N, void* const* out, int64_t M, int64_t K,
-                                int out_dtype, hipStream_t stream) {
+hipError_t launch_tiled_impl(const int8_t* xq, const float* a_scale, int groups,
+                             const uint8_t* const* packed, const float* const* w_scale,
+                             const int64_t* N, void* const* out, int64_t M, int64_t K,
+                             int out_dtype, int* part, size_t part_bytes, hipStream_t stream) {
     if (groups < 1 || groups > kTdGroups) return hipErrorInvalidValue;
     TiledArgs a;
     a.xq = xq;
@@ -713,27 +862,57 @@ hipError_t launch_tiled_grouped(const int8_t* xq, const float* a_scale, int grou
     a.out_dtype = out_dtype;
     int64_t n_all[kTdGroups];
     for (int i = 0; i < kTdGroups; ++i) n_all[i] = i < groups ? N[i] : 0;
-    const TilePlan t = plan_tiles(M, K, n_all, groups, device_cus());
+    // K is split only for one matrix and a workspace that holds the planned partials
+    bool allow_split = groups == 1 && part != nullptr;
+    if (allow_split) {
+        const TilePlan ts = plan_tiles(M, K, n_all, 1, device_cus(), true);
+        allow_split = ts.ksplit > 1 && (size_t)ts.ksplit * (size_t)M * (size_t)N[0] * 4 <= part_bytes;
+    }
+    const TilePlan t = plan_tiles(M, K, n_all, groups, device_cus(), allow_split);
     // register sets in flight: 64-k stages 4 (2 for 256x256); 128-k stages 2, or 4 for
     // the 256x128 tile (its accumulators live in the matrix-core registers)
-    if (t.bm == 256 && t.bn == 256) return launch_plan<256, 256, 2, 1, 4, 64>(a, n_all, stream);
+    if (t.bm == 256 && t.bn == 256) return launch_plan<256, 256, 2, 1, 4, 64>(a, n_all, t, part, stream);
     if (t.bk == 128) {
-        if (t.bm == 256) return launch_plan<256, 128, 4, 1, 2, 128>(a, n_all, stream);
-        if (t.bm == 64) return launch_plan<64, 128, 2, 4, 4, 128>(a, n_all, stream);
-        return launch_plan<128, 128, 2, 2, 2, 128>(a, n_all, stream);
+        if (t.bm == 256) return launch_plan<256, 128, 4, 1, 2, 128>(a, n_all, t, part, stream);
+        if (t.bm == 64) return launch_plan<64, 128, 2, 4, 4, 128>(a, n_all, t, part, stream);
+        return launch_plan<128, 128, 2, 2, 2, 128>(a, n_all, t, part, stream);
     }
-    if (t.bm == 256) return launch_plan<256, 128, 4, 1, 2, 64>(a, n_all, stream);
-    if (t.bm == 64) return launch_plan<64, 128, 4, 4, 4, 64>(a, n_all, stream);
-    return launch_plan<128, 128, 4, 2, 2, 64>(a, n_all, stream);
+    if (t.bm == 256) return launch_plan<256, 128, 4, 1, 2, 64>(a, n_all, t, part, stream);
+    if (t.bm == 64) return launch_plan<64, 128, 4, 4, 4, 64>(a, n_all, t, part, stream);
+    return launch_plan<128, 128, 4, 2, 2, 64>(a, n_all, t, part, stream);
+}
+
+}  // namespace
+
+size_t tiled_workspace_size(int64_t M, int64_t N, int64_t K) {
+    if (M < 1 || N < 1) return 0;
+    const TilePlan t = plan_tiles(M, K, &N, 1, device_cus(), true);
+    return t.ksplit > 1 ? (size_t)t.ksplit * (size_t)M * (size_t)N * 4 : 0;
+}
+
+void tiled_plan(int64_t M, int64_t K, int groups, const int64_t* N, int64_t cus, int* plan) {
+    const TilePlan t = plan_tiles(M, K, N, groups, cus > 0 ? cus : device_cus(), groups == 1);
+    plan[0] = t.bm;
+    plan[1] = t.bn;
+    plan[2] = t.g;
+    plan[3] = t.bk;
+    plan[4] = t.ksplit;
+}
+
+hipError_t launch_tiled_grouped(const int8_t* xq, const float* a_scale, int groups,
+                                const uint8_t* const* packed, const float* const* w_scale,
+                                const int64_t* N, void* const* out, int64_t M, int64_t K,
+                                int out_dtype, hipStream_t stream) {
+    return launch_tiled_impl(xq, a_scale, groups, packed, w_scale, N, out, M, K, out_dtype,
+                             nullptr, 0, stream);
 }
 
 hipError_t launch_tiled(const int8_t* xq, const float* a_scale, const uint8_t* packed,
                         const float* w_scale, int64_t M, int64_t N, int64_t K, void* out,
-                        int out_dtype, void* workspace, hipStream_t stream) {
-    (void)workspace;
+                        int out_dtype, void* workspace, size_t ws_bytes, hipStream_t stream) {
     void* outs[1] = {out};
-    return launch_tiled_grouped(xq, a_scale, 1, &packed, &w_scale, &N, outs, M, K, out_dtype,
-                                stream);
+    return launch_tiled_impl(xq, a_scale, 1, &packed, &w_scale, &N, outs, M, K, out_dtype,
+                             static_cast<int*>(workspace), ws_bytes, stream);
 }
 
 }  // namespace bitnet

@@ -56,7 +56,8 @@ def test_library_has_gfx950_code_only():
 
 
 def test_abi_version_and_status_strings(L):
-    assert bw.abi_version() == 1
+    declared = int(re.search(r"#define BITNET_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert bw.abi_version() == declared == 2
     for s in range(6):
         assert bw.status_str(s) not in ("", "unknown status")
     assert bw.status_str(99) == "unknown status"
@@ -111,10 +112,13 @@ def test_gemm_validation(L):
     assert f(A, B, C, D, 64, 16, 256, E, 0, 0, F + 8, 16, None) == UNALIGNED
     assert f(A, B, C, D, 64, 16, 256, E, 0, 0, None, 16, None) == INVALID    # bytes but no buffer
     assert f(A, B, C, D, 0, 16, 256, E, 0, 2, None, 0, None) == OK
-    # no kernel of this version needs device scratch
+    # device scratch only where the plan splits K: int32 partials of every slice (no
+    # device here, so the plan is the one for 256 CUs)
     assert L.bitnet_w2a8_gemm_workspace_size(512, 2560, 2560) == 0
     assert L.bitnet_w2a8_gemm_workspace_size(4096, 28672, 8192) == 0
+    assert L.bitnet_w2a8_gemm_workspace_size(32, 8192, 4096) == 3 * 32 * 8192 * 4
     assert L.bitnet_w2a8_gemm_workspace_size(-1, 16, 256) == 0
+    assert L.bitnet_w2a8_gemm_workspace_size(32, 8192, 4098) == 0  # K % 4
 
 def test_quant_gemv_validation(L):
     f = L.bitnet_quant_gemv
@@ -195,7 +199,7 @@ def test_gemm_plan_validation(L):
     f = L.bitnet_w2a8_gemm_plan
     P = ctypes.c_void_p
     ns = (ctypes.c_int64 * 2)(640, 2560)
-    out = (ctypes.c_int32 * 4)()
+    out = (ctypes.c_int32 * 5)()
     assert f(512, 2560, 2, ctypes.cast(ns, P), 256, ctypes.cast(out, P)) == OK
     assert f(0, 2560, 2, ctypes.cast(ns, P), 256, ctypes.cast(out, P)) == INVALID     # M < 1
     assert f(512, 2560, 0, ctypes.cast(ns, P), 256, ctypes.cast(out, P)) == INVALID   # groups
@@ -213,20 +217,24 @@ def test_gemm_plan_validation(L):
 # launches of the 2B prefill step and the 8B/70B prefill shapes, and the shapes the GPU
 # parity tests use to reach every compiled (tile, k-stage) pair.
 PLAN_CASES = [
-    ((512, 2560, [2560, 640, 640]), (64, 128, 4, 128)),    # 2B q|k|v: 240 tiles, one round
-    ((512, 2560, [2560]), (64, 128, 4, 128)),              # 2B o
-    ((512, 2560, [6912, 6912]), (256, 128, 1, 128)),       # 2B gate|up: 216 tiles, one round
-    ((512, 6912, [2560]), (64, 128, 4, 128)),              # 2B down
-    ((2048, 4096, [14336]), (256, 256, 1, 64)),            # 8B gate: two rounds of 256x256
-    ((2048, 14336, [4096]), (256, 128, 1, 128)),           # 8B down
-    ((1024, 8192, [28672, 28672]), (256, 256, 1, 64)),     # 70B gate|up
-    ((130, 320, [257, 64, 0, 96]), (64, 128, 4, 64)),      # K % 128 != 0: 64-k stages
-    ((512, 2560, [2560, 640, 640]), (64, 128, 4, 128)),
-    ((600, 256, [6912, 6912]), (256, 256, 1, 64)),
-    ((500, 2048, [6000, 7000]), (256, 128, 1, 128)),
-    ((1024, 128, [4096, 1024, 1024, 300]), (256, 128, 1, 64)),
-    ((257, 320, [5000, 4000]), (128, 128, 2, 64)),
-    ((300, 384, [4100, 4100]), (128, 128, 2, 128)),
+    ((512, 2560, [2560, 640, 640]), (64, 128, 4, 128, 1)),    # 2B q|k|v: 240 tiles, one round
+    ((512, 2560, [2560]), (64, 128, 4, 128, 1)),              # 2B o
+    ((512, 2560, [6912, 6912]), (256, 128, 1, 128, 1)),       # 2B gate|up: 216 tiles, one round
+    ((512, 6912, [2560]), (64, 128, 4, 128, 1)),              # 2B down
+    ((2048, 4096, [14336]), (256, 256, 1, 64, 1)),            # 8B gate: two rounds of 256x256
+    ((2048, 14336, [4096]), (256, 128, 1, 128, 1)),           # 8B down
+    ((1024, 8192, [28672, 28672]), (256, 256, 1, 64, 1)),     # 70B gate|up
+    ((130, 320, [257, 64, 0, 96]), (64, 128, 4, 64, 1)),      # K % 128 != 0: 64-k stages
+    ((512, 2560, [2560, 640, 640]), (64, 128, 4, 128, 1)),
+    ((600, 256, [6912, 6912]), (256, 256, 1, 64, 1)),
+    ((500, 2048, [6000, 7000]), (256, 128, 1, 128, 1)),
+    ((1024, 128, [4096, 1024, 1024, 300]), (256, 128, 1, 64, 1)),
+    ((257, 320, [5000, 4000]), (128, 128, 2, 64, 1)),
+    ((300, 384, [4100, 4100]), (128, 128, 2, 128, 1)),
+    ((32, 8192, [8192]), (64, 128, 4, 128, 4)),            # 70B q, M=32: 64 tiles, 4 slices
+    ((32, 28672, [8192]), (64, 128, 4, 128, 4)),           # 70B down, M=32
+    ((32, 8192, [8192, 1024]), (64, 128, 4, 128, 1)),      # grouped launches never split
+    ((2048, 4096, [1024]), (64, 128, 4, 128, 1)),          # 512 tiles: no split
 ]
 
 
@@ -244,7 +252,7 @@ def test_gemm_plan_covers_every_compiled_configuration():
         for K in (128, 192, 320, 384, 1024, 2048, 2560, 4096, 6912, 14336):
             for Ns in ([640], [2560], [6912, 6912], [4096, 1024, 1024], [14336], [28672]):
                 p = bw.gemm_plan(M, K, Ns, cus=256)
-                seen.add(p)
+                seen.add(p[:4])
                 if K % 128:
                     assert p[3] == 64, (M, K, Ns, p)
     assert seen == {(64, 128, 4, 128), (128, 128, 2, 128), (256, 128, 1, 128),

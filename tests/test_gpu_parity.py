@@ -563,18 +563,67 @@ def test_graph_replay_of_grouped_swiglu_and_a16_launches():
         check_out(to_np(out), o["acc"], o["ref"], "f32", f"graph replay grouped N={pb.N}")
 
 
-def test_gemm_small_and_large_tile_grids_with_caller_workspace():
+def test_gemm_small_and_large_tile_grids():
     # Shapes that select each tile configuration (64x128 with four k-groups, 128x128 with
     # two, 256x128, 256x256; 64-k and 128-k stages), including grids far smaller than
-    # the CU count and ragged edges; a caller workspace is accepted and left untouched.
-    ws = torch.full((1 << 20,), 0x5A, dtype=torch.uint8, device="cuda")
+    # the CU count and ragged edges, with and without a workspace (with one, the small
+    # grids split K across blocks)
     for (M, N, K) in [(300, 257, 2560), (512, 2560, 2560), (130, 640, 6912), (17, 1024, 4096),
                       (1024, 8192, 512), (600, 16384, 256), (257, 9000, 320), (520, 33000, 320),
                       (520, 33024, 128), (264, 65560, 192), (300, 8200, 384), (64, 4096, 1024)]:
         pb = Problem(M, N, K, seed=M + N + K)
         xq, a, packed, s, o = product_inputs(pb)
-        out = bw.gemm(xq, a, packed, s, "i32", algo="tiled", workspace=ws)
+        out = bw.gemm(xq, a, packed, s, "i32", algo="tiled")
         check_out(to_np(out), o["acc"], o["ref"], "i32", f"tiles {M}x{N}x{K}")
-        out = bw.gemm(xq, a, packed, s, "bf16", algo="tiled")
+        out = bw.gemm(xq, a, packed, s, "bf16", algo="tiled", workspace=False)
         check_out(to_np(out), o["acc"], o["ref"], "bf16", f"tiles {M}x{N}x{K} bf16")
-    assert int((ws != 0x5A).count_nonzero()) == 0
+
+
+# (M, N, K) whose tiled plan splits K across blocks (on 256 CUs): aligned and ragged N
+# (vector and element-wise reduce), 64-k and 128-k stages, up to 16 slices
+SPLIT_CASES = [(32, 8192, 4096), (64, 1024, 4096), (17, 300, 2560), (33, 1000, 6912),
+               (96, 130, 8192), (5, 2000, 2048), (1, 640, 2560), (300, 257, 2560),
+               (128, 512, 16384), (256, 4096, 14336)]
+
+
+@pytest.mark.parametrize("M,N,K", SPLIT_CASES)
+def test_split_k_matches_oracle_and_unsplit(M, N, K):
+    assert bw.gemm_plan(M, K, [N])[4] > 1, "shape no longer splits on this device"
+    need = int(bw.lib().bitnet_w2a8_gemm_workspace_size(M, N, K))
+    assert need > 0
+    pb = Problem(M, N, K, seed=M * 3 + N + K)
+    xq, a, packed, s, o = product_inputs(pb)
+    ws = torch.full((need + 64,), 0x7F, dtype=torch.uint8, device="cuda")
+    for dt in DT:
+        split = bw.gemm(xq, a, packed, s, dt, algo="tiled", workspace=ws)
+        check_out(to_np(split), o["acc"], o["ref"], dt, f"split {M}x{N}x{K} {dt}")
+        whole = bw.gemm(xq, a, packed, s, dt, algo="tiled", workspace=False)
+        assert torch.equal(split, whole), f"split and unsplit differ {M}x{N}x{K} {dt}"
+        # a workspace one byte short of the plan's partials runs unsplit, same result
+        short = bw.gemm(xq, a, packed, s, dt, algo="tiled", workspace=ws[:need - 16])
+        assert torch.equal(short, whole), f"short workspace {M}x{N}x{K} {dt}"
+
+
+def test_split_k_in_graph_replays():
+    # the two launches of a split product (partials, then reduce) captured in a graph and
+    # replayed several times with eager work in between, every replay checked
+    M, N, K = 32, 8192, 4096
+    pb = Problem(M, N, K, seed=5)
+    xq, a, packed, s, o = product_inputs(pb)
+    ws = torch.empty((int(bw.lib().bitnet_w2a8_gemm_workspace_size(M, N, K)),),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        bw.gemm(xq, a, packed, s, "f32", algo="tiled", out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        bw.gemm(xq, a, packed, s, "f32", algo="tiled", out=out, workspace=ws)
+    for rep in range(4):
+        out.zero_()
+        ws.fill_(rep)
+        g.replay()
+        torch.cuda.synchronize()
+        check_out(to_np(out), o["acc"], o["ref"], "f32", f"split graph replay {rep}")
