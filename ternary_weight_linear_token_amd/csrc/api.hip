@@ -74,6 +74,37 @@ hipError_t launch_small_m(const int8_t* xq, const float* a_scale, const uint8_t*
                                  nullptr, nullptr, stream);
 }
 
+// The product of bitnet_w2a8_gemm once its arguments are validated.  Auto: the
+// weight-streaming kernels while the product is small enough that one round of their
+// blocks beats the tiled kernel (whose single-round grids cost about the same for any M
+// up to 64): always up to 4 tokens, up to 16 while the weights are at most 16 MB, the
+// direct kernel up to 32 tokens while N * K <= 2^25, and the staged kernel's token tiles
+// up to 32 while M * N is small; else the tiled kernel, which may split K through the
+// workspace.
+int gemm_launch(const int8_t* xq, const float* a_scale, const uint8_t* packed,
+                const float* w_scale, int64_t M, int64_t N, int64_t K, void* out, int out_dtype,
+                int algo, void* workspace, size_t ws_bytes, hipStream_t stream) {
+    if (algo == BITNET_ALGO_SKINNY)
+        return record_hip(bitnet::launch_skinny(xq, a_scale, nullptr, packed, w_scale, M, N, K,
+                                                out, out_dtype, nullptr, nullptr, stream));
+    if (algo == BITNET_ALGO_AUTO) {
+        if (M <= 4 || (M <= 16 && N * K <= ((int64_t)1 << 26)))
+            return record_hip(launch_small_m(xq, a_scale, packed, w_scale, M, N, K, out,
+                                             out_dtype, stream));
+        // 17 to 32 tokens: the direct kernel's two token tiles while the activations it
+        // re-reads per 16-row block (M * K bytes each) stay cheap next to the weights
+        if (M <= 32 && K % 64 == 0 && N * K <= ((int64_t)1 << 25))
+            return record_hip(bitnet::launch_gemv_direct(xq, a_scale, nullptr, packed, w_scale,
+                                                         M, N, K, out, out_dtype, nullptr,
+                                                         nullptr, stream));
+        if (M <= 32 && M * N <= 131072)
+            return record_hip(bitnet::launch_skinny(xq, a_scale, nullptr, packed, w_scale, M, N,
+                                                    K, out, out_dtype, nullptr, nullptr, stream));
+    }
+    return record_hip(bitnet::launch_tiled(xq, a_scale, packed, w_scale, M, N, K, out, out_dtype,
+                                           workspace, ws_bytes, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -165,32 +196,8 @@ int bitnet_w2a8_gemm(const int8_t* xq, const float* a_scale, const uint8_t* pack
         !aligned16(out) || !aligned16(workspace))
         return BITNET_ERR_UNALIGNED;
     if ((st = check_device())) return st;
-    // Auto: the weight-streaming kernels while the product is small enough that one
-    // round of their blocks beats the tiled kernel (whose single-round grids cost about
-    // the same for any M up to 64): always up to 4 tokens, up to 16 while the weights
-    // are at most 16 MB, the direct kernel up to 32 tokens while N * K <= 2^25, and the
-    // staged kernel's token tiles up to 32 while M * N is small.
-    if (algo == BITNET_ALGO_SKINNY)
-        return record_hip(bitnet::launch_skinny(xq, a_scale, nullptr, packed, w_scale, M, N, K,
-                                                out, out_dtype, nullptr, nullptr,
-                                                as_stream(stream)));
-    if (algo == BITNET_ALGO_AUTO) {
-        if (M <= 4 || (M <= 16 && N * K <= ((int64_t)1 << 26)))
-            return record_hip(launch_small_m(xq, a_scale, packed, w_scale, M, N, K, out,
-                                             out_dtype, as_stream(stream)));
-        // 17 to 32 tokens: the direct kernel's two token tiles while the activations it
-        // re-reads per 16-row block (M * K bytes each) stay cheap next to the weights
-        if (M <= 32 && K % 64 == 0 && N * K <= ((int64_t)1 << 25))
-            return record_hip(bitnet::launch_gemv_direct(xq, a_scale, nullptr, packed, w_scale,
-                                                         M, N, K, out, out_dtype, nullptr,
-                                                         nullptr, as_stream(stream)));
-        if (M <= 32 && M * N <= 131072)
-            return record_hip(bitnet::launch_skinny(xq, a_scale, nullptr, packed, w_scale, M, N,
-                                                    K, out, out_dtype, nullptr, nullptr,
-                                                    as_stream(stream)));
-    }
-    return record_hip(bitnet::launch_tiled(xq, a_scale, packed, w_scale, M, N, K, out, out_dtype,
-                                           workspace, ws_bytes, as_stream(stream)));
+    return gemm_launch(xq, a_scale, packed, w_scale, M, N, K, out, out_dtype, algo, workspace,
+                       ws_bytes, as_stream(stream));
 }
 
 int bitnet_w2a8_gemm_grouped(const int8_t* xq, const float* a_scale, int64_t M, int64_t K,
