@@ -190,6 +190,25 @@ int bitnet_w2a8_gemm(const int8_t* xq, const float* a_scale, const uint8_t* pack
                      int out_dtype, int algo, void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * bitnet_w2a8_gemm_noalloc -- bitnet_w2a8_gemm for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments minus the workspace, the same kernels and bit-identical
+ * outputs, with the split-K partial sums in a fixed device scratch array that the
+ * library holds on every GPU it runs on until the process ends
+ * (BITNET_NOALLOC_SCRATCH_BYTES, 32 MB).  The call allocates nothing.
+ *   Returns BITNET_ERR_WORKSPACE, before any HIP call, when the tiled plan for (M, N, K)
+ *   needs more partials than the scratch holds (only with K in the tens of thousands
+ *   and M, N in the thousands).
+ *   All calls on one GPU share its scratch: calls that overlap on a GPU (different
+ *   streams, or different host threads without ordering) race and give undefined
+ *   outputs; order them, e.g. on one stream.  Nothing in the scratch needs clearing.
+ */
+#define BITNET_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int bitnet_w2a8_gemm_noalloc(const int8_t* xq, const float* a_scale, const uint8_t* packed,
+                             const float* w_scale, int64_t M, int64_t N, int64_t K, void* out,
+                             int out_dtype, int algo, void* stream);
+
+/*
  * bitnet_w2a8_gemm_grouped -- the tiled product (BITNET_ALGO_TILED) for several weight
  * matrices that read the same int8 activations, in one launch: a prefill-sized batch
  * through q, k and v, or through gate and up, of the LLaMA block in "BitNet 深度实战" §3.2

@@ -22,6 +22,7 @@ from ._binding import (  # noqa: F401
     bitlinear,
     gemm,
     gemm_grouped,
+    gemm_noalloc,
     gemm_plan,
     gemv,
     lib,

@@ -64,6 +64,7 @@ def lib():
             "bitnet_quant_gemv": ([p, p, p, i64, i64, i64, p, i32, p, p, p], i32),
             "bitnet_quant_gemv_grouped": ([p, i64, i64, i64, p, p, p, p, i32, p, p, p], i32),
             "bitnet_w2a8_gemm_grouped": ([p, p, i64, i64, i64, p, p, p, p, i32, p], i32),
+            "bitnet_w2a8_gemm_noalloc": ([p, p, p, p, i64, i64, i64, p, i32, i32, p], i32),
             "bitnet_w2a8_gemm_plan": ([i64, i64, i64, p, i64, p], i32),
             "bitnet_quant_gemv_swiglu": ([p, p, p, p, p, i64, i64, i64, p, i32, p, p, p], i32),
             "bitnet_quant_act_per_tensor": ([p, i64, i64, p, p, p], i32),
@@ -247,6 +248,25 @@ def gemm(xq, a_scale, packed, w_scale, out_dtype="f32", algo="auto", out=None, w
                                   _tensor(out, _OUT_TORCH[code], "out", (M, N)), code, algo_code,
                                   ws_ptr, ws_bytes, stream),
            "bitnet_w2a8_gemm")
+    return out
+
+
+def gemm_noalloc(xq, a_scale, packed, w_scale, out_dtype="f32", algo="auto", out=None):
+    """gemm through the entry point that allocates nothing: split-K partials go to the
+    library's fixed device scratch (calls on one GPU must not overlap).  Pass `out` to
+    keep the call free of torch allocations as well."""
+    M, K = xq.shape
+    N = packed.shape[0]
+    code = _out_code(out_dtype)
+    algo_code = _ALGO_NAMES[algo] if isinstance(algo, str) else int(algo)
+    out = _alloc_out(out, M, N, code, xq.device)
+    _check(lib().bitnet_w2a8_gemm_noalloc(_tensor(xq, torch.int8, "xq", (M, K)),
+                                          _tensor(a_scale, torch.float32, "a_scale", (M,)),
+                                          _tensor(packed, torch.uint8, "packed", (N, K // 4)),
+                                          _tensor(w_scale, torch.float32, "w_scale", (N,)), M, N,
+                                          K, _tensor(out, _OUT_TORCH[code], "out", (M, N)), code,
+                                          algo_code, _stream(xq)),
+           "bitnet_w2a8_gemm_noalloc")
     return out
 
 

@@ -6,6 +6,7 @@
 #include <atomic>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "bitnet_w2a8.h"
 #include "kernels.hpp"
@@ -105,6 +106,42 @@ int gemm_launch(const int8_t* xq, const float* a_scale, const uint8_t* packed,
                                            workspace, ws_bytes, stream));
 }
 
+// ---- device scratch of the allocation-free product (bitnet_w2a8_gemm_noalloc) ----
+// The int32 partial sums of a split-K product live in this file-scope array: one copy on
+// every GPU the library runs on, allocated with the code object and held until the
+// process ends.  In host code `scratch` names a host-side stand-in, never the device
+// memory: its address on a device is taken once per device with hipGetSymbolAddress
+// (that device current) and only that address reaches kernels.  Every call on a GPU
+// shares its copy, so calls that overlap on one GPU (different streams) race; the
+// partials need no clearing, as every call writes each one before reading it.
+constexpr size_t kScratchBytes = BITNET_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) int scratch[kScratchBytes / sizeof(int)];
+
+struct ScratchSlot {
+    std::mutex lock;
+    std::atomic<void*> ptr{nullptr};
+};
+ScratchSlot g_scratch_slot[kMaxDevices];
+
+// This device's scratch address (dev is the current device), looked up on the first
+// call on the device; a failed lookup is retried by the next call.
+hipError_t scratch_address(int dev, void** out) {
+    ScratchSlot& slot = g_scratch_slot[dev];
+    void* p = slot.ptr.load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> guard(slot.lock);
+        p = slot.ptr.load(std::memory_order_relaxed);
+        if (!p) {
+            const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (!p) return hipErrorInvalidSymbol;
+            slot.ptr.store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -198,6 +235,33 @@ int bitnet_w2a8_gemm(const int8_t* xq, const float* a_scale, const uint8_t* pack
     if ((st = check_device())) return st;
     return gemm_launch(xq, a_scale, packed, w_scale, M, N, K, out, out_dtype, algo, workspace,
                        ws_bytes, as_stream(stream));
+}
+
+int bitnet_w2a8_gemm_noalloc(const int8_t* xq, const float* a_scale, const uint8_t* packed,
+                             const float* w_scale, int64_t M, int64_t N, int64_t K, void* out,
+                             int out_dtype, int algo, void* stream) {
+    if (!valid_dtype(out_dtype)) return BITNET_ERR_INVALID_ARG;
+    if (algo != BITNET_ALGO_AUTO && algo != BITNET_ALGO_SKINNY && algo != BITNET_ALGO_TILED)
+        return BITNET_ERR_INVALID_ARG;
+    int st = check_shape(M, N, K);
+    if (st) return st;
+    if (algo == BITNET_ALGO_SKINNY && M > BITNET_SKINNY_MAX_M) return BITNET_ERR_INVALID_ARG;
+    if (M == 0 || N == 0) return BITNET_OK;
+    if (!xq || !a_scale || !packed || !w_scale || !out) return BITNET_ERR_INVALID_ARG;
+    if (!aligned16(xq) || !aligned16(a_scale) || !aligned16(packed) || !aligned16(w_scale) ||
+        !aligned16(out))
+        return BITNET_ERR_UNALIGNED;
+    // the planned partials must fit the fixed scratch (never the case below 32 MB: the
+    // planner itself keeps partials under 64 MB)
+    if (bitnet::tiled_workspace_size(M, N, K) > kScratchBytes) return BITNET_ERR_WORKSPACE;
+    if ((st = check_device())) return st;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return record_hip(e);
+    void* ws = nullptr;
+    if ((e = scratch_address(dev, &ws)) != hipSuccess) return record_hip(e);
+    return gemm_launch(xq, a_scale, packed, w_scale, M, N, K, out, out_dtype, algo, ws,
+                       kScratchBytes, as_stream(stream));
 }
 
 int bitnet_w2a8_gemm_grouped(const int8_t* xq, const float* a_scale, int64_t M, int64_t K,

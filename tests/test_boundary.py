@@ -120,6 +120,20 @@ def test_gemm_validation(L):
     assert L.bitnet_w2a8_gemm_workspace_size(-1, 16, 256) == 0
     assert L.bitnet_w2a8_gemm_workspace_size(32, 8192, 4098) == 0  # K % 4
 
+def test_gemm_noalloc_validation(L):
+    f = L.bitnet_w2a8_gemm_noalloc
+    assert f(A, B, C, D, 64, 16, 256, E, 0, 7, None) == INVALID     # bad algo
+    assert f(A, B, C, D, 65, 16, 256, E, 0, 1, None) == INVALID     # skinny with M > 64
+    assert f(A, B, C, D, 64, 16, 256, E, 5, 0, None) == INVALID     # bad dtype
+    assert f(A, B, C, D + 4, 64, 16, 256, E, 0, 0, None) == UNALIGNED
+    assert f(A, B, C, D, 64, 16, 254, E, 0, 0, None) == UNALIGNED   # K % 4
+    assert f(None, B, C, D, 64, 16, 256, E, 0, 0, None) == INVALID
+    assert f(A, B, C, D, 0, 16, 256, E, 0, 2, None) == OK
+    # a plan whose partials exceed the 32 MB scratch is refused before any HIP call
+    assert L.bitnet_w2a8_gemm_workspace_size(1024, 8192, 131072) > 32 << 20
+    assert f(A, B, C, D, 1024, 8192, 131072, E, 0, 2, None) == WORKSPACE
+
+
 def test_quant_gemv_validation(L):
     f = L.bitnet_quant_gemv
     assert f(None, B, C, 1, 16, 256, D, 0, None, None, None) == INVALID
