@@ -22,6 +22,9 @@ Functions and the pages they follow (page titles abbreviated):
   swiglu        -- "BitNet 深度实战" §3.2: the MLP's silu(gate(x)) * up(x).
   a16           -- "将 BitNet 三元查找表集成到自定义 Triton 内核中" / "BitNet 深度实战" §2.2:
                    16-bit activations times ternary weights, no activation quantization.
+  pack_b3 / unpack_b3 / accumulate_b3 -- "将 BitNet 三元查找表集成到自定义 Triton 内核中"
+                   (4-5 ternary values per byte) / "BitNet 1-bit LLM推理优化" §2.1: five
+                   weights per byte in base 3, 1.6 bits per weight.
 
 Every function is pinned by tests/test_oracle_pins.py (worked example, closed forms,
 invariants, library matmul on unpacked codes, brute force on tiny inputs).
@@ -85,6 +88,9 @@ def _load():
             "oracle_swiglu": [p, p, i64, p],
             "oracle_act_quant_per_tensor": [p, i64, i64, p, p],
             "oracle_a16": [p, p, p, i64, i64, i64, p, p],
+            "oracle_pack_b3": [p, i64, i64, p],
+            "oracle_unpack_b3": [p, i64, i64, p],
+            "oracle_accumulate_b3": [p, p, i64, i64, i64, p],
         }
         for name, args in sig.items():
             fn = getattr(lib, name)
@@ -92,6 +98,8 @@ def _load():
             fn.restype = ctypes.c_int if name != "oracle_f64_to_bf16" else None
         lib.oracle_repack.argtypes = [p, i64, i64, ctypes.c_int, ctypes.c_int, p]
         lib.oracle_repack.restype = i64
+        lib.oracle_b3_row_bytes.argtypes = [i64]
+        lib.oracle_b3_row_bytes.restype = i64
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
         _lib = lib
@@ -153,6 +161,49 @@ def pack_weights(W: np.ndarray):
     """O1 + pack: float32 (N, K) -> (packed uint8 (N, K/4), scale float32 (N,))."""
     q, s = weight_quant(W)
     return pack(q), s
+
+
+# ------------------------------------------------ five weights per byte (1.6 bits)
+
+
+def b3_row_bytes(K: int) -> int:
+    """Bytes per row of the five-per-byte format: K padded to a multiple of 320, / 5."""
+    r = int(_load().oracle_b3_row_bytes(int(K)))
+    if r < 0:
+        raise OracleError("b3_row_bytes: bad K")
+    return r
+
+
+def pack_b3(q: np.ndarray) -> np.ndarray:
+    """Ternary codes int8 (N, K) -> (N, b3_row_bytes(K)) uint8, five weights per byte
+    ("将 BitNet 三元查找表集成到自定义 Triton 内核中": 4-5 ternary values per byte;
+    "BitNet 1-bit LLM推理优化" §2.1: below 2 bits per weight)."""
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    N, K = q.shape
+    out = np.empty((N, b3_row_bytes(K)), np.uint8)
+    _check(_load().oracle_pack_b3(_ptr(q), N, K, _ptr(out)), "pack_b3")
+    return out
+
+
+def unpack_b3(b3: np.ndarray, K: int) -> np.ndarray:
+    """Inverse of pack_b3 -> int8 (N, K); raises if a padding weight is not 0."""
+    b3 = np.ascontiguousarray(b3, dtype=np.uint8)
+    N = b3.shape[0]
+    assert b3.shape[1] == b3_row_bytes(K)
+    q = np.empty((N, K), np.int8)
+    _check(_load().oracle_unpack_b3(_ptr(b3), N, K, _ptr(q)), "unpack_b3")
+    return q
+
+
+def accumulate_b3(xq: np.ndarray, b3: np.ndarray, K: int) -> np.ndarray:
+    """acc[m, n] = sum_k xq[m, k] * w[n, k] with w decoded from the five-per-byte format."""
+    xq = np.ascontiguousarray(xq, dtype=np.int8)
+    b3 = np.ascontiguousarray(b3, dtype=np.uint8)
+    M, N = xq.shape[0], b3.shape[0]
+    assert xq.shape[1] == K and b3.shape[1] == b3_row_bytes(K)
+    acc = np.empty((M, N), np.int32)
+    _check(_load().oracle_accumulate_b3(_ptr(xq), _ptr(b3), M, N, K, _ptr(acc)), "accumulate_b3")
+    return acc
 
 
 # --------------------------------------------------------------------------- O2

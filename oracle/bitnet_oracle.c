@@ -134,6 +134,93 @@ int oracle_unpack(const uint8_t* packed, int64_t N, int64_t K, int8_t* q) {
     return bad;
 }
 
+/* ------------------------------------- 1.6-bit packing: five weights per byte --- */
+
+/*
+ * [LUT] (its three integration steps): ternary weights go into a packed uint8 bitmap,
+ * four to five of them per 8-bit byte.  [Layout] §2.1 / §3.1: the TL encoding packs
+ * three weights into 5 bits (1.67 bits per weight) to beat the 2 bits of a plain code.
+ * Five per byte is possible because 3^5 = 243 <= 256.
+ *
+ * Readings where the pages are silent:
+ *   - byte j of a row holds weights k = 5j .. 5j+4; their codes c = w + 1 in {0, 1, 2}
+ *     are the base-3 digits of v = c[5j]*81 + c[5j+1]*27 + c[5j+2]*9 + c[5j+3]*3 +
+ *     c[5j+4] (the first weight the most significant digit);
+ *   - the stored byte is ceil(256 v / 243), i.e. v/243 rounded up to a multiple of
+ *     1/256: then v = floor(byte * 243 / 256), and the digits also come out by repeated
+ *     multiplication by 3 (each digit is the integer part, the byte-wide fraction stays);
+ *   - a row holds B3_CHUNK-weight chunks (64 bytes): K is padded up to a multiple of 320
+ *     with weights 0, so rows start 64-byte aligned.
+ */
+#define B3_CHUNK 320
+static int64_t b3_row_bytes(int64_t K) { return (K + B3_CHUNK - 1) / B3_CHUNK * 64; }
+
+int64_t oracle_b3_row_bytes(int64_t K) { return K < 1 ? -1 : b3_row_bytes(K); }
+
+int oracle_pack_b3(const int8_t* q, int64_t N, int64_t K, uint8_t* out) {
+    if (!q || !out || N < 0 || K < 1) return -1;
+    const int64_t RB = b3_row_bytes(K);
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t j = 0; j < RB; ++j) {
+            int v = 0;
+            for (int i = 0; i < 5; ++i) {
+                const int64_t k = 5 * j + i;
+                const int w = k < K ? q[n * K + k] : 0;
+                if (w < -1 || w > 1) return -1;
+                v = 3 * v + (w + 1);
+            }
+            out[n * RB + j] = (uint8_t)((256 * v + 242) / 243); /* ceil(256 v / 243) */
+        }
+    }
+    return 0;
+}
+
+/* Inverse of oracle_pack_b3: v = floor(byte * 243 / 256), digits by division.  Returns 1
+ * if a padding weight (k >= K) is not 0. */
+int oracle_unpack_b3(const uint8_t* b3, int64_t N, int64_t K, int8_t* q) {
+    if (!b3 || !q || N < 0 || K < 1) return -1;
+    const int64_t RB = b3_row_bytes(K);
+    int bad = 0;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t j = 0; j < RB; ++j) {
+            const int v = (b3[n * RB + j] * 243) / 256;
+            for (int i = 0; i < 5; ++i) {
+                int p = 1;
+                for (int t = i; t < 4; ++t) p *= 3;
+                const int w = (v / p) % 3 - 1; /* digit i, the first the most significant */
+                const int64_t k = 5 * j + i;
+                if (k < K) q[n * K + k] = (int8_t)w;
+                else if (w != 0) bad = 1;
+            }
+        }
+    }
+    return bad;
+}
+
+/* O3 on the five-per-byte format: acc[m, n] = sum_k xq[m, k] * w[n, k], each w decoded
+ * from its byte as above. */
+int oracle_accumulate_b3(const int8_t* xq, const uint8_t* b3, int64_t M, int64_t N, int64_t K,
+                         int32_t* acc) {
+    if (!xq || !b3 || !acc || M < 0 || N < 0 || K < 1) return -1;
+    const int64_t RB = b3_row_bytes(K);
+    int overflow = 0;
+#pragma omp parallel for schedule(static) reduction(| : overflow)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t m = 0; m < M; ++m) {
+            int64_t sum = 0;
+            for (int64_t k = 0; k < K; ++k) {
+                const int v = (b3[n * RB + k / 5] * 243) / 256;
+                int p = 1;
+                for (int t = (int)(k % 5); t < 4; ++t) p *= 3;
+                sum += (int64_t)xq[m * K + k] * ((v / p) % 3 - 1);
+            }
+            if (sum > INT32_MAX || sum < INT32_MIN) overflow = 1;
+            acc[m * N + n] = (int32_t)sum;
+        }
+    }
+    return overflow ? -1 : 0;
+}
+
 /* -------------------------------------- O2: per-token absmax int8 activations --- */
 
 /*

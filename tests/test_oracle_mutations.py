@@ -56,6 +56,14 @@ MUTATIONS = {
                            "h[t] = g[t] / (1.0 + exp(g[t])) * u[t];"),
     "swiglu_sigmoid_only": ("h[t] = g[t] / (1.0 + exp(-g[t])) * u[t];",
                             "h[t] = 1.0 / (1.0 + exp(-g[t])) * u[t];"),
+    "b3_round_down": ("out[n * RB + j] = (uint8_t)((256 * v + 242) / 243);",
+                      "out[n * RB + j] = (uint8_t)((256 * v) / 243);"),
+    "b3_pack_code_table": ("v = 3 * v + (w + 1);", "v = 3 * v + (w + 2) % 3;"),
+    "b3_unpack_scale": ("const int v = (b3[n * RB + j] * 243) / 256;",
+                        "const int v = (b3[n * RB + j] * 242) / 256;"),
+    "b3_accumulate_digit_order": ("for (int t = (int)(k % 5); t < 4; ++t) p *= 3;",
+                                  "for (int t = 0; t < (int)(k % 5); ++t) p *= 3;"),
+    "b3_row_padding": ("return (K + B3_CHUNK - 1) / B3_CHUNK * 64;", "return (K + 4) / 5;"),
     "swiglu_swapped_operands": ("h[t] = g[t] / (1.0 + exp(-g[t])) * u[t];",
                                 "h[t] = u[t] / (1.0 + exp(-u[t])) * g[t];"),
 }

@@ -433,3 +433,54 @@ def test_a16_linearity_and_zero_weights():
     zero = oracle.pack(np.zeros((5, 64), np.int8))
     rz, sz = oracle.a16(workloads.bf16_bits(X), zero, s, 64)
     assert not rz.any() and not sz.any()
+
+
+# ------------------------------------------- five weights per byte (1.6 bits/weight)
+
+
+def test_b3_hand_worked_bytes():
+    # weights (+1, 0, -1, +1, 0) -> codes (2, 1, 0, 2, 1) -> v = 2*81 + 1*27 + 0*9 + 2*3 + 1
+    # = 196 -> byte ceil(256 * 196 / 243) = ceil(206.49...) = 207; all zero weights: v =
+    # 121 -> ceil(127.47...) = 128; all -1: v = 0 -> 0; all +1: v = 242 -> ceil(254.95) = 255
+    rows = np.array([[1, 0, -1, 1, 0], [0, 0, 0, 0, 0], [-1] * 5, [1] * 5], np.int8)
+    b = oracle.pack_b3(rows)
+    assert b.shape == (4, 64)
+    assert b[:, 0].tolist() == [207, 128, 0, 255]
+    assert np.all(b[:, 1:] == 128)  # padding weights are 0
+    assert np.array_equal(oracle.unpack_b3(b, 5), rows)
+
+
+def test_b3_state_count_and_digit_extraction():
+    # all 3^5 = 243 <= 256 digit patterns map to distinct bytes and back; the digits also
+    # come out, first weight first, as the integer parts of repeated multiplication of
+    # the byte by 3 (keeping the byte-wide fraction), which is what a decoder may use
+    pats = np.array([[(p // 3 ** (4 - i)) % 3 - 1 for i in range(5)] for p in range(243)], np.int8)
+    b = oracle.pack_b3(pats)[:, 0].astype(np.int64)
+    assert len(set(b.tolist())) == 243 and b.max() <= 255
+    assert np.array_equal(oracle.unpack_b3(oracle.pack_b3(pats), 5), pats)
+    t = b.copy()
+    for i in range(5):
+        t = t * 3
+        assert np.array_equal(t >> 8, pats[:, i].astype(np.int64) + 1)
+        t &= 255
+
+
+@pytest.mark.parametrize("N,K", [(37, 1000), (3, 320), (5, 4), (2, 641)])
+def test_b3_round_trip_and_row_size(N, K):
+    rng = np.random.default_rng(N * K)
+    q = rng.integers(-1, 2, size=(N, K), dtype=np.int8)
+    b = oracle.pack_b3(q)
+    assert b.shape == (N, 64 * ((K + 319) // 320)) == (N, oracle.b3_row_bytes(K))
+    assert np.array_equal(oracle.unpack_b3(b, K), q)
+    if K % 320 == 0:
+        assert b.size * 8 / q.size == 1.6
+
+
+@pytest.mark.parametrize("M,N,K", [(3, 17, 640), (1, 40, 1000), (5, 9, 964)])
+def test_b3_accumulate_matches_two_bit_path_and_matmul(M, N, K):
+    rng = np.random.default_rng(M + N + K)
+    q = rng.integers(-1, 2, size=(N, K), dtype=np.int8)
+    xq = rng.integers(-127, 128, size=(M, K), dtype=np.int8)
+    acc3 = oracle.accumulate_b3(xq, oracle.pack_b3(q), K)
+    assert np.array_equal(acc3, oracle.accumulate(xq, oracle.pack(q), K))
+    assert np.array_equal(acc3, xq.astype(np.int64) @ q.astype(np.int64).T)
