@@ -562,6 +562,8 @@ def bench_extras(bw, workloads, torch, dev, reps):
     out["a16_decode_2b_m1"] = {"achieved_GB/s": round(tot_b / tot_us / 1e3, 1),
                                "per_shape_us": per}
 
+    out["b3_decode_70b_m1"] = bench_b3(bw, workloads, torch, dev, reps)
+
     # what this chip sustains (context for the fractions above)
     print("[bench] ceilings", file=sys.stderr, flush=True)
     mfma, ghz = ceilings.mfma_i8_tops(torch, dev)
@@ -580,6 +582,43 @@ def bench_extras(bw, workloads, torch, dev, reps):
         "vendor_int8_gemm_tops_dense_int8_weights": vendor,
     }
     return out
+
+
+def bench_b3(bw, workloads, torch, dev, reps):
+    """The 70B-shaped decode layer (seven projections, one launch each, M = 1, fused
+    quantization) with weights five per byte (1.6 bits) against the same launches on the
+    2-bit format; weight copies rotated past 1 GiB for both."""
+    print("[bench] 70B decode set, 1.6-bit weights against 2-bit, M=1", file=sys.stderr,
+          flush=True)
+    per, t2, t3, b2, b3b = {}, 0.0, 0.0, 0, 0
+    for name, N, K in workloads.distinct_shapes(workloads.LAYER_70B):
+        count = sum(1 for n, NN, KK in workloads.LAYER_70B if (NN, KK) == (N, K))
+        W = workloads.latent_weights_on(dev, N, K, seed=0)
+        p, s = bw.pack_weights(W)
+        del W
+        q = bw.pack_b3(p, K)
+        x = workloads.activations(1, K, seed=0, outliers=True).to(dev)
+        o = torch.empty((1, N), dtype=torch.float32, device=dev)
+        cp = rotation([p], N * K // 4)
+        us2 = graph_launch_us(torch, lambda r: bw.quant_gemv(x, cp[r][0], s, "f32", out=o),
+                              len(cp), reps)
+        del cp
+        cq = rotation([q], q.numel())
+        us3 = graph_launch_us(torch, lambda r: bw.quant_gemv_b3(x, cq[r][0], s, "f32", out=o),
+                              len(cq), reps)
+        del cq, p, q
+        torch.cuda.empty_cache()
+        per[name] = {"us_2bit": round(us2, 3), "us_1p6bit": round(us3, 3),
+                     "launches_per_layer": count}
+        t2 += count * us2
+        t3 += count * us3
+        b2 += count * N * K // 4
+        b3b += count * N * bw.b3_row_bytes(K)
+    return {"packed_bytes_2bit": b2, "packed_bytes_1p6bit": b3b,
+            "us_2bit": round(t2, 3), "us_1p6bit": round(t3, 3),
+            "speedup_1p6_over_2bit": round(t2 / t3, 4),
+            "GB/s_2bit": round(b2 / t2 / 1e3, 1), "GB/s_1p6bit_bytes": round(b3b / t3 / 1e3, 1),
+            "per_shape": per}
 
 
 def bench_gemm(bw, workloads, torch, dev, layer, reps, probe=False):

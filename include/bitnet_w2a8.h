@@ -325,6 +325,42 @@ int bitnet_quant_gemv_swiglu(const uint16_t* x, const uint8_t* packed_gate,
 int bitnet_a16_gemv(const uint16_t* x, const uint8_t* packed, const float* w_scale, int64_t M,
                     int64_t N, int64_t K, void* out, int out_dtype, void* stream);
 
+/*
+ * Ternary weights at 1.6 bits per weight, five per byte ("将 BitNet 三元查找表集成到自定义
+ * Triton 内核中": a uint8 bitmap of four to five ternary values per byte; "BitNet 1-bit
+ * LLM推理优化" §2.1 / §3.1: packing below 2 bits per weight, 3 weights in 5 bits).
+ * Layout: (N, BITNET_B3_ROW_BYTES(K)) uint8, rows padded with weights 0 to whole chunks
+ * of 320 weights (64 bytes).  Byte j of row n holds weights k = 5j .. 5j+4: with codes
+ * c = w + 1, v = 81 c[5j] + 27 c[5j+1] + 9 c[5j+2] + 3 c[5j+3] + c[5j+4] (0 .. 242) is
+ * stored as ceil(256 v / 243), so v = floor(byte * 243 / 256).  20% fewer weight bytes
+ * than the 2-bit format (a 70B-class layer set: 171 MB instead of 214 MB).
+ */
+#define BITNET_B3_ROW_BYTES(K) (64 * (((K) + 319) / 320))
+#define BITNET_B3_MAX_K 30720
+
+/*
+ * bitnet_pack_b3 -- convert a packed (N, K/4) array of the 2-bit format above into the
+ * five-per-byte format.
+ *   packed : uint8 (N, K/4), as produced by bitnet_pack_weights.  A field holding the
+ *            unused code 0b11 becomes weight 0.
+ *   b3     : uint8 (N, BITNET_B3_ROW_BYTES(K)) output.
+ */
+int bitnet_pack_b3(const uint8_t* packed, int64_t N, int64_t K, uint8_t* b3, void* stream);
+
+/*
+ * bitnet_quant_gemv_b3 -- bitnet_quant_gemv on weights in the five-per-byte format, for
+ * one token (M = 1, the decode step): the per-token int8 quantization of x fused into
+ * the product, int32 accumulation, the same rescale and outputs as bitnet_quant_gemv
+ * (fp32 within 3 roundings of the exact value, bf16 its RNE, int32 the exact acc).
+ *   x       : bf16 (1, K) as uint16; K % 8 == 0 (else BITNET_ERR_UNALIGNED) and
+ *             K <= BITNET_B3_MAX_K; M other than 0 or 1 returns BITNET_ERR_INVALID_ARG.
+ *   b3      : uint8 (N, BITNET_B3_ROW_BYTES(K)), as produced by bitnet_pack_b3.
+ *   w_scale : float (N), as produced by bitnet_pack_weights.
+ *   out     : (1, N) of out_dtype.
+ */
+int bitnet_quant_gemv_b3(const uint16_t* x, const uint8_t* b3, const float* w_scale, int64_t M,
+                         int64_t N, int64_t K, void* out, int out_dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

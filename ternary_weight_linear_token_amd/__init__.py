@@ -23,6 +23,9 @@ from ._binding import (  # noqa: F401
     gemm,
     gemm_grouped,
     gemm_noalloc,
+    b3_row_bytes,
+    pack_b3,
+    quant_gemv_b3,
     gemm_plan,
     gemv,
     lib,

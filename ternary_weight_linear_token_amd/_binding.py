@@ -70,6 +70,8 @@ def lib():
             "bitnet_quant_act_per_tensor": ([p, i64, i64, p, p, p], i32),
             "bitnet_a16_gemv": ([p, p, p, i64, i64, i64, p, i32, p], i32),
             "bitnet_repack_codes": ([p, i64, i64, i32, i32, p, p, p], i32),
+            "bitnet_pack_b3": ([p, i64, i64, p, p], i32),
+            "bitnet_quant_gemv_b3": ([p, p, p, i64, i64, i64, p, i32, p], i32),
         }
         for name, (args, res) in sigs.items():
             fn = getattr(L, name)
@@ -411,6 +413,38 @@ def a16_gemv(x, packed, w_scale, out_dtype="f32", out=None):
                                  _tensor(w_scale, torch.float32, "w_scale", (N,)), M, N, K,
                                  _tensor(out, _OUT_TORCH[code], "out", (M, N)), code, _stream(x)),
            "bitnet_a16_gemv")
+    return out
+
+
+def b3_row_bytes(K: int) -> int:
+    """Bytes per row of the five-per-byte (1.6-bit) weight format."""
+    return 64 * ((int(K) + 319) // 320)
+
+
+def pack_b3(packed: torch.Tensor, K: int, out: torch.Tensor | None = None):
+    """2-bit packed (N, K/4) -> five-per-byte (N, b3_row_bytes(K)) uint8."""
+    N = packed.shape[0]
+    RB = b3_row_bytes(K)
+    if out is None:
+        out = torch.empty((N, RB), dtype=torch.uint8, device=packed.device)
+    _check(lib().bitnet_pack_b3(_tensor(packed, torch.uint8, "packed", (N, K // 4)), N, K,
+                                _tensor(out, torch.uint8, "b3", (N, RB)), _stream(packed)),
+           "bitnet_pack_b3")
+    return out
+
+
+def quant_gemv_b3(x, b3, w_scale, out_dtype="f32", out=None):
+    """Fused int8 quantization + product for one token with five-per-byte weights."""
+    M, K = x.shape
+    N = b3.shape[0]
+    code = _out_code(out_dtype)
+    out = _alloc_out(out, M, N, code, x.device)
+    _check(lib().bitnet_quant_gemv_b3(_tensor(x, torch.bfloat16, "x", (M, K)),
+                                      _tensor(b3, torch.uint8, "b3", (N, b3_row_bytes(K))),
+                                      _tensor(w_scale, torch.float32, "w_scale", (N,)), M, N, K,
+                                      _tensor(out, _OUT_TORCH[code], "out", (M, N)), code,
+                                      _stream(x)),
+           "bitnet_quant_gemv_b3")
     return out
 
 

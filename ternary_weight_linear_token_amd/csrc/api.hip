@@ -264,6 +264,32 @@ int bitnet_w2a8_gemm_noalloc(const int8_t* xq, const float* a_scale, const uint8
                        kScratchBytes, as_stream(stream));
 }
 
+int bitnet_pack_b3(const uint8_t* packed, int64_t N, int64_t K, uint8_t* b3, void* stream) {
+    int st = check_shape(0, N, K);
+    if (st) return st;
+    if (N == 0) return BITNET_OK;
+    if (!packed || !b3) return BITNET_ERR_INVALID_ARG;
+    if (!aligned16(packed) || !aligned16(b3)) return BITNET_ERR_UNALIGNED;
+    if ((st = check_device())) return st;
+    return record_hip(bitnet::launch_pack_b3(packed, N, K, b3, as_stream(stream)));
+}
+
+int bitnet_quant_gemv_b3(const uint16_t* x, const uint8_t* b3, const float* w_scale, int64_t M,
+                         int64_t N, int64_t K, void* out, int out_dtype, void* stream) {
+    if (!valid_dtype(out_dtype)) return BITNET_ERR_INVALID_ARG;
+    int st = check_shape(M, N, K);
+    if (st) return st;
+    if (K % 8 != 0) return BITNET_ERR_UNALIGNED;
+    if (M > 1 || K > BITNET_B3_MAX_K) return BITNET_ERR_INVALID_ARG;
+    if (M == 0 || N == 0) return BITNET_OK;
+    if (!x || !b3 || !w_scale || !out) return BITNET_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(b3) || !aligned16(w_scale) || !aligned16(out))
+        return BITNET_ERR_UNALIGNED;
+    if ((st = check_device())) return st;
+    return record_hip(bitnet::launch_quant_gemv_b3(x, b3, w_scale, N, K, out, out_dtype,
+                                                   as_stream(stream)));
+}
+
 int bitnet_w2a8_gemm_grouped(const int8_t* xq, const float* a_scale, int64_t M, int64_t K,
                              int64_t groups, const uint8_t* const* packed,
                              const float* const* w_scale, const int64_t* N, void* const* out,

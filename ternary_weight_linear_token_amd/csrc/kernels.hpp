@@ -60,6 +60,16 @@ hipError_t launch_gemv_direct(const int8_t* xq, const float* a_scale, const uint
                               int64_t K, void* out, int out_dtype, int8_t* xq_out, float* a_out,
                               hipStream_t stream);
 
+// Five ternary weights per byte (1.6 bits): bytes per row of the format, the conversion
+// from the 2-bit interface format, and the decode product with fused quantization for
+// one token (K % 8 == 0, K <= BITNET_B3_MAX_K).
+int64_t b3_row_bytes(int64_t K);
+hipError_t launch_pack_b3(const uint8_t* packed, int64_t N, int64_t K, uint8_t* b3,
+                          hipStream_t stream);
+hipError_t launch_quant_gemv_b3(const uint16_t* x, const uint8_t* b3, const float* w_scale,
+                                int64_t N, int64_t K, void* out, int out_dtype,
+                                hipStream_t stream);
+
 // Tiled int8 matrix-core product for any M.  Device scratch with which a single-matrix
 // launch may split K across blocks (int32 partial tiles of every K slice), in bytes; 0
 // when the best plan does not split.

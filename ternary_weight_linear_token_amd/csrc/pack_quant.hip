@@ -106,11 +106,13 @@ __global__ __launch_bounds__(256) void unpack_kernel(const uint8_t* __restrict__
 }
 
 // ------------------------------------------------------- activation quantization ---
-// One 256-thread block per token row.  Pass 1: max |x| as the integer max of the bf16
-// magnitude bits (monotone in |x| for finite values), V = 8 elements (16 bytes) per load
-// when K % 8 == 0, else 4 (8 bytes).  Pass 2: a = 127 / max(amax, 1e-5) (IEEE division),
-// q = clamp(rne(x * a), +-127).  Rows up to G * 256 * V elements keep their loads in
-// registers between the passes; longer rows (G == 0) read the row twice.
+// One wave per token row, four rows per 256-thread block, no block barrier: lane l takes
+// the V-element groups l, l + 64, l + 128, ... of its row (V = 8, 16-byte loads, when
+// K % 8 == 0, else 4).  Pass 1: max |x| as the integer max of the bf16 magnitude bits
+// (monotone in |x| for finite values), reduced across the wave.  Pass 2: a = 127 /
+// max(amax, 1e-5) (IEEE division), q = clamp(rne(x * a), +-127).  Rows of up to G * 64
+// groups keep their loads in registers between the passes (all issued before the first
+// use); longer rows (G == 0) read the row twice, the second time from cache.
 // MODE 0: per-token scale (both passes).  Per-tensor scale, three launches: MODE 1 runs
 // pass 1 only and leaves the row's max magnitude bits in a_scale[m]; tensor_scale_kernel
 // reduces them and writes the common scale to every a_scale[m]; MODE 2 runs pass 2 with
@@ -143,14 +145,17 @@ __device__ __forceinline__ uint32_t qvec_max_bits(const QVec<V>& v, uint32_t mx)
     return mx;
 }
 
+constexpr int kQaRowsPerBlock = 4;  // one wave per row
+
 template <int G, int MODE, int V>
 __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restrict__ x,
-                                                        int64_t K, int8_t* __restrict__ xq,
+                                                        int64_t M, int64_t K,
+                                                        int8_t* __restrict__ xq,
                                                         float* __restrict__ a_scale) {
     static_assert(V == 4 || V == 8, "elements per load");
-    __shared__ uint32_t s_max[4];
-    const int64_t m = blockIdx.x;
-    const int tid = threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int64_t m = (int64_t)blockIdx.x * kQaRowsPerBlock + (threadIdx.x >> 6);
+    if (m >= M) return;  // uniform over the wave; no block-wide synchronization below
     const int64_t groups = K / V;
     const uint16_t* row = x + m * K;
 
@@ -159,7 +164,7 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restri
     if (G > 0) {
 #pragma unroll
         for (int i = 0; i < G; ++i) {
-            const int64_t g = tid + (int64_t)i * 256;
+            const int64_t g = lane + (int64_t)i * 64;
             if (g < groups) {
                 held[i] = load_qvec<V>(row, g);
             } else {
@@ -172,24 +177,21 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restri
             for (int i = 0; i < G; ++i) mx = qvec_max_bits<V>(held[i], mx);
         }
     } else if (MODE != 2) {
-        for (int64_t g = tid; g < groups; g += 256) mx = qvec_max_bits<V>(load_qvec<V>(row, g), mx);
+        for (int64_t g = lane; g < groups; g += 64) mx = qvec_max_bits<V>(load_qvec<V>(row, g), mx);
     }
     float a;
     if constexpr (MODE == 2) {
         a = a_scale[m];
     } else {
         mx = wave_max_u32(mx);
-        if ((tid & 63) == 0) s_max[tid >> 6] = mx;
-        __syncthreads();
-        mx = max(max(s_max[0], s_max[1]), max(s_max[2], s_max[3]));
         if constexpr (MODE == 1) {
-            if (tid == 0) reinterpret_cast<uint32_t*>(a_scale)[m] = mx;  // bits of max |x|
+            if (lane == 0) reinterpret_cast<uint32_t*>(a_scale)[m] = mx;  // bits of max |x|
             return;
         }
         float amax = bf16_bits_to_f32(mx);
         amax = amax < 1e-5f ? 1e-5f : amax;
         a = 127.0f / amax;
-        if (tid == 0) a_scale[m] = a;
+        if (lane == 0) a_scale[m] = a;
     }
 
     // V codes per group: one word (V = 4) or two (V = 8)
@@ -217,7 +219,7 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restri
     if (G > 0) {
 #pragma unroll
         for (int i = 0; i < G; ++i) {
-            const int64_t g = tid + (int64_t)i * 256;
+            const int64_t g = lane + (int64_t)i * 64;
             if (g < groups) {
                 uint32_t packed[V / 4];
                 quantv(held[i], packed);
@@ -225,7 +227,7 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restri
             }
         }
     } else {
-        for (int64_t g = tid; g < groups; g += 256) {
+        for (int64_t g = lane; g < groups; g += 64) {
             uint32_t packed[V / 4];
             quantv(load_qvec<V>(row, g), packed);
             store(g, packed);
@@ -318,20 +320,20 @@ template <int MODE, int V>
 hipError_t launch_quant_rows_v(const uint16_t* x, int64_t M, int64_t K, int8_t* xq,
                                float* a_scale, hipStream_t stream) {
     const int64_t groups = K / V;
-    const int64_t per_thread = (groups + 255) / 256;
-    dim3 grid((unsigned)M), blk(256);
-    if (per_thread <= 1)
-        hipLaunchKernelGGL((quant_act_kernel<1, MODE, V>), grid, blk, 0, stream, x, K, xq, a_scale);
-    else if (per_thread <= 2)
-        hipLaunchKernelGGL((quant_act_kernel<2, MODE, V>), grid, blk, 0, stream, x, K, xq, a_scale);
-    else if (per_thread <= 4)
-        hipLaunchKernelGGL((quant_act_kernel<4, MODE, V>), grid, blk, 0, stream, x, K, xq, a_scale);
-    else if (per_thread <= 8)
-        hipLaunchKernelGGL((quant_act_kernel<8, MODE, V>), grid, blk, 0, stream, x, K, xq, a_scale);
-    else if (per_thread <= 16)
-        hipLaunchKernelGGL((quant_act_kernel<16, MODE, V>), grid, blk, 0, stream, x, K, xq, a_scale);
+    const int64_t per_lane = (groups + 63) / 64;
+    dim3 grid((unsigned)((M + kQaRowsPerBlock - 1) / kQaRowsPerBlock)), blk(256);
+    if (per_lane <= 2)
+        hipLaunchKernelGGL((quant_act_kernel<2, MODE, V>), grid, blk, 0, stream, x, M, K, xq, a_scale);
+    else if (per_lane <= 4)
+        hipLaunchKernelGGL((quant_act_kernel<4, MODE, V>), grid, blk, 0, stream, x, M, K, xq, a_scale);
+    else if (per_lane <= 8)
+        hipLaunchKernelGGL((quant_act_kernel<8, MODE, V>), grid, blk, 0, stream, x, M, K, xq, a_scale);
+    else if (per_lane <= 16)
+        hipLaunchKernelGGL((quant_act_kernel<16, MODE, V>), grid, blk, 0, stream, x, M, K, xq, a_scale);
+    else if (per_lane <= 32)
+        hipLaunchKernelGGL((quant_act_kernel<32, MODE, V>), grid, blk, 0, stream, x, M, K, xq, a_scale);
     else
-        hipLaunchKernelGGL((quant_act_kernel<0, MODE, V>), grid, blk, 0, stream, x, K, xq, a_scale);
+        hipLaunchKernelGGL((quant_act_kernel<0, MODE, V>), grid, blk, 0, stream, x, M, K, xq, a_scale);
     return hipGetLastError();
 }
 

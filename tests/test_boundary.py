@@ -134,6 +134,25 @@ def test_gemm_noalloc_validation(L):
     assert f(A, B, C, D, 1024, 8192, 131072, E, 0, 2, None) == WORKSPACE
 
 
+def test_b3_validation(L):
+    f = L.bitnet_quant_gemv_b3
+    assert f(A, B, C, 2, 16, 256, D, 0, None) == INVALID           # one token only
+    assert f(A, B, C, 1, 16, 260, D, 0, None) == UNALIGNED         # K % 8
+    assert f(A, B, C, 1, 16, 30720 + 8, D, 0, None) == INVALID     # K above the maximum
+    assert f(A, B, C, 1, 16, 256, D, 5, None) == INVALID           # dtype
+    assert f(None, B, C, 1, 16, 256, D, 0, None) == INVALID
+    assert f(A, B + 4, C, 1, 16, 256, D, 0, None) == UNALIGNED
+    assert f(A, B, C, 0, 16, 256, D, 0, None) == OK
+    g = L.bitnet_pack_b3
+    assert g(None, 4, 256, B, None) == INVALID
+    assert g(A, 4, 254, B, None) == UNALIGNED
+    assert g(A, 4, 256, B + 8, None) == UNALIGNED
+    assert g(A, 0, 256, B, None) == OK
+    text = open(HEADER).read()
+    assert "#define BITNET_B3_ROW_BYTES(K) (64 * (((K) + 319) / 320))" in text
+    assert bw.b3_row_bytes(320) == 64 and bw.b3_row_bytes(321) == 128
+
+
 def test_quant_gemv_validation(L):
     f = L.bitnet_quant_gemv
     assert f(None, B, C, 1, 16, 256, D, 0, None, None, None) == INVALID

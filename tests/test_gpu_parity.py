@@ -345,6 +345,52 @@ def test_a16_gemv_matches_oracle(M, N, K):
     assert np.all(np.abs(outi - exact) <= 2.0 ** -24 * np.abs(exact)), f"a16 integer M={M} N={N} K={K}"
 
 
+# ------------------------------------------------- five weights per byte (1.6 bits)
+
+
+@pytest.mark.parametrize("N,K", [(1, 4), (3, 12), (129, 260), (640, 2560), (33, 8192),
+                                 (7, 28672)])
+def test_pack_b3_matches_oracle(N, K):
+    rng = np.random.default_rng(N + K)
+    # every 2-bit field value, the unused code 3 included (it becomes weight 0)
+    packed = rng.integers(0, 256, size=(N, K // 4), dtype=np.uint8)
+    cleared, _ = oracle.repack(packed, K, oracle.CODES_OFFSET, oracle.CODES_OFFSET)
+    want = oracle.pack_b3(oracle.unpack(cleared, K))
+    got = bw.pack_b3(dev(packed), K)
+    assert np.array_equal(to_np(got), want)
+
+
+@pytest.mark.parametrize("N,K", [(16, 256), (37, 264), (300, 1024), (129, 2560), (50, 6912),
+                                 (33, 8192), (17, 30720), (1, 8), (640, 2560), (4100, 320)])
+def test_quant_gemv_b3_matches_oracle(N, K):
+    pb = Problem(1, N, K, seed=N * 7 + K)
+    o = pb.oracle(full=False)
+    q = oracle.unpack(o["packed"], K)
+    b3 = oracle.pack_b3(q)
+    acc = oracle.accumulate_b3(o["xq"], b3, K)
+    ref, _, _ = oracle.rescale(acc, o["a_scale"], o["w_scale"])
+    b3_dev, s = dev(b3), dev(o["w_scale"])
+    for dt in DT:
+        out = bw.quant_gemv_b3(pb.x_dev, b3_dev, s, dt)
+        check_out(to_np(out), acc, ref, dt, f"b3 N={N} K={K} {dt}")
+    # the same weights in the 2-bit format give the same exact accumulators
+    two_bit = bw.quant_gemv(pb.x_dev, dev(o["packed"]), s, "i32")
+    assert np.array_equal(to_np(two_bit), acc)
+
+
+def test_b3_chain_from_latent_weights():
+    # pack on the GPU (2-bit, then five per byte), then the product, against the oracle
+    N, K = 515, 4096
+    pb = Problem(1, N, K, seed=21)
+    packed, s = bw.pack_weights(pb.w_dev)
+    b3 = bw.pack_b3(packed, K)
+    o = pb.oracle(full=False)
+    assert np.array_equal(to_np(b3), oracle.pack_b3(oracle.unpack(o["packed"], K)))
+    acc = oracle.accumulate_b3(o["xq"], to_np(b3), K)
+    ref, _, _ = oracle.rescale(acc, o["a_scale"], o["w_scale"])
+    check_out(to_np(bw.quant_gemv_b3(pb.x_dev, b3, s, "f32")), acc, ref, "f32", "b3 chain")
+
+
 def test_extreme_accumulators():
     # every activation at +-127 and every weight +1 / -1: |acc| = 127 K, the largest sums
     M, N, K = 3, 40, 28672

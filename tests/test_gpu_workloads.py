@@ -65,3 +65,31 @@ def test_workload_shape(wl, name, N, K, Ms, outliers):
         for dt, out in outs.items():
             check_out(out, acc, ref, dt, f"{wl} {name} M={M} {dt} full")
         print(f"  M={M} ok (oracle {t_oracle:.1f} s)", flush=True)
+
+
+def b3_cases():
+    out = []
+    for wl in ("2b_decode", "8b_sweep", "70b_chain"):
+        for name, N, K in workloads.distinct_shapes(workloads.WORKLOADS[wl]["layer"]):
+            out.append(pytest.param(N, K, id=f"{wl}-{name}-{N}x{K}"))
+    return out
+
+
+@pytest.mark.parametrize("N,K", b3_cases())
+def test_b3_decode_shape(N, K):
+    # the five-per-byte weights of every decode shape at M = 1, whole output compared
+    print(f"\n[b3] N={N} K={K}", flush=True)
+    W = workloads.latent_weights(N, K, seed=0)
+    p_ref, s_ref = oracle.pack_weights(W.numpy())
+    packed, w_scale = bw.pack_weights(W.cuda())
+    del W
+    b3 = bw.pack_b3(packed, K)
+    b3_ref = oracle.pack_b3(oracle.unpack(p_ref, K))
+    assert np.array_equal(to_np(b3), b3_ref), "b3 bytes"
+    X = workloads.activations(1, K, seed=0, outliers=True)
+    xq_ref, a_ref = oracle.act_quant(workloads.bf16_bits(X))
+    acc = oracle.accumulate_b3(xq_ref, b3_ref, K)
+    ref, _, _ = oracle.rescale(acc, a_ref, s_ref)
+    for dt in ("f32", "bf16", "i32"):
+        out = to_np(bw.quant_gemv_b3(X.cuda(), b3, w_scale, dt))
+        check_out(out, acc, ref, dt, f"b3 {N}x{K} {dt}")
