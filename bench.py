@@ -83,6 +83,9 @@ def parse():
                     help="run the counter-collection launch pattern and exit (no timing)")
     ap.add_argument("--gemm-probe", action="store_true",
                     help="run the prefill GEMM launches for counter collection and exit")
+    ap.add_argument("--large-probe", action="store_true",
+                    help="run the 8B M=2048 / 70B M=1024 GEMMs and the 70B M=1 decode "
+                         "launches for counter collection and exit")
     return ap.parse_args()
 
 
@@ -161,6 +164,10 @@ def main():
 
     if args.traffic_probe:
         traffic_probe(torch, launch_set, R, dev)
+        return
+    if args.large_probe:
+        del copies
+        large_probe(bw, workloads, torch, dev)
         return
     if args.gemm_probe:
         bench_gemm(bw, workloads, torch, dev, layer, reps=args.kernel_reps, probe=True)
@@ -352,6 +359,56 @@ def traffic_probe(torch, launch_set, R, dev):
         launch_set(r)
     torch.cuda.synchronize()
     print(f"[bench] traffic probe: {R} decode steps", file=sys.stderr)
+
+
+# the launches of --large-probe, in order: (name, M, N per group, K); each runs once per
+# weight copy of a rotation past 1 GiB, eagerly, after the calibration copies
+LARGE_PROBE_GEMM = [("8b_gate_m2048", 2048, (14336,), 4096), ("8b_down_m2048", 2048, (4096,), 14336),
+                    ("70b_gate_up_m1024", 1024, (28672, 28672), 8192),
+                    ("70b_down_m1024", 1024, (8192,), 28672)]
+
+
+def large_probe(bw, workloads, torch, dev):
+    """Counter-collection pattern for the large shapes: the calibration copies, the 70B
+    decode set at M = 1 (grouped fused quant + GEMV launches), then the large prefill
+    GEMMs (int8 in, bf16 out), each over weight copies rotated past 1 GiB."""
+    calibration_copies(torch, dev)
+    shapes = {name: (N, K) for name, N, K in workloads.LAYER_70B}
+    for grp in workloads.DECODE_GROUPS:
+        K = shapes[grp[0]][1]
+        ps, ss = [], []
+        for name in grp:
+            p, s = bw.pack_weights(workloads.latent_weights_on(dev, shapes[name][0], K, seed=0))
+            ps.append(p)
+            ss.append(s)
+        cp = rotation(ps, sum(shapes[n][0] * K // 4 for n in grp))
+        x = workloads.activations(1, K, seed=0, outliers=True).to(dev)
+        for c in cp:
+            if len(grp) == 1:
+                bw.quant_gemv(x, c[0], ss[0], "f32")
+            else:
+                bw.quant_gemv_grouped(x, c, ss, "f32")
+        torch.cuda.synchronize()
+        del cp, ps
+        torch.cuda.empty_cache()
+    for name, M, Ns, K in LARGE_PROBE_GEMM:
+        ps, ss = [], []
+        for N in Ns:
+            p, s = bw.pack_weights(workloads.latent_weights_on(dev, N, K, seed=0))
+            ps.append(p)
+            ss.append(s)
+        cp = rotation(ps, sum(N * K // 4 for N in Ns))
+        xq, a = bw.quant_act(workloads.activations(M, K, seed=0, outliers=True).to(dev))
+        outs = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for N in Ns]
+        for c in cp:
+            if len(Ns) == 1:
+                bw.gemm(xq, a, c[0], ss[0], "bf16", out=outs[0])
+            else:
+                bw.gemm_grouped(xq, a, c, ss, "bf16", out=outs)
+        torch.cuda.synchronize()
+        del cp, ps
+        torch.cuda.empty_cache()
+    print("[bench] large probe done", file=sys.stderr)
 
 
 def graph_launch_us(torch, launch, R, reps):
@@ -567,6 +624,9 @@ def bench_extras(bw, workloads, torch, dev, reps):
     # what this chip sustains (context for the fractions above)
     print("[bench] ceilings", file=sys.stderr, flush=True)
     mfma, ghz = ceilings.mfma_i8_tops(torch, dev)
+    # the same loop on 16 CUs only: little power drawn, so the clock it reads is the
+    # unthrottled one (checks the clock reading itself)
+    _, ghz_light = ceilings.mfma_i8_tops(torch, dev, blocks=16, iters=20000)
     read = ceilings.hbm_read_gbs(torch, dev)
     vendor = {f"{M}x{N}x{K}": (None if t is None else round(t, 1)) for (M, N, K), t in
               (((M, N, K), ceilings.vendor_int8_gemm_tops(torch, dev, M, N, K))
@@ -577,6 +637,7 @@ def bench_extras(bw, workloads, torch, dev, reps):
         "mfma_i8_register_loop_core_clock_ghz": None if ghz is None else round(ghz, 3),
         "mfma_i8_peak_at_that_clock_tops": (None if ghz is None else
                                             round(INT8_MFMA_PEAK_TOPS * ghz / 2.4, 1)),
+        "core_clock_ghz_same_loop_on_16_cus": None if ghz_light is None else round(ghz_light, 3),
         "hbm_stream_read_2GiB_gbs": round(read, 1),
         "hbm_stream_read_frac_of_peak": round(read / HBM_PEAK_GBS, 4),
         "vendor_int8_gemm_tops_dense_int8_weights": vendor,

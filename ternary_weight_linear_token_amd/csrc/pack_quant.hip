@@ -106,12 +106,14 @@ __global__ __launch_bounds__(256) void unpack_kernel(const uint8_t* __restrict__
 }
 
 // ------------------------------------------------------- activation quantization ---
-// One wave per token row, four rows per 256-thread block, no block barrier: lane l takes
-// the V-element groups l, l + 64, l + 128, ... of its row (V = 8, 16-byte loads, when
-// K % 8 == 0, else 4).  Pass 1: max |x| as the integer max of the bf16 magnitude bits
-// (monotone in |x| for finite values), reduced across the wave.  Pass 2: a = 127 /
-// max(amax, 1e-5) (IEEE division), q = clamp(rne(x * a), +-127).  Rows of up to G * 64
-// groups keep their loads in registers between the passes (all issued before the first
+// A token row is taken by WPR waves (1, 2 or 4) of a 256-thread block, 4 / WPR rows per
+// block: few rows get more waves each, so that a launch has enough waves in flight.  Lane
+// l of the row's waves takes the V-element groups l, l + 64 WPR, ... (V = 8, 16-byte
+// loads, when K % 8 == 0, else 4).  Pass 1: max |x| as the integer max of the bf16
+// magnitude bits (monotone in |x| for finite values), reduced across the wave and, with
+// WPR > 1, across the row's waves through LDS (one barrier).  Pass 2: a = 127 /
+// max(amax, 1e-5) (IEEE division), q = clamp(rne(x * a), +-127).  Rows of up to G groups
+// per lane keep their loads in registers between the passes (all issued before the first
 // use); longer rows (G == 0) read the row twice, the second time from cache.
 // MODE 0: per-token scale (both passes).  Per-tensor scale, three launches: MODE 1 runs
 // pass 1 only and leaves the row's max magnitude bits in a_scale[m]; tensor_scale_kernel
@@ -145,26 +147,31 @@ __device__ __forceinline__ uint32_t qvec_max_bits(const QVec<V>& v, uint32_t mx)
     return mx;
 }
 
-constexpr int kQaRowsPerBlock = 4;  // one wave per row
-
-template <int G, int MODE, int V>
+template <int G, int MODE, int V, int WPR>
 __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restrict__ x,
                                                         int64_t M, int64_t K,
                                                         int8_t* __restrict__ xq,
                                                         float* __restrict__ a_scale) {
     static_assert(V == 4 || V == 8, "elements per load");
-    const int lane = threadIdx.x & 63;
-    const int64_t m = (int64_t)blockIdx.x * kQaRowsPerBlock + (threadIdx.x >> 6);
-    if (m >= M) return;  // uniform over the wave; no block-wide synchronization below
-    const int64_t groups = K / V;
-    const uint16_t* row = x + m * K;
+    static_assert(WPR == 1 || WPR == 2 || WPR == 4, "waves per row");
+    constexpr int kRows = 4 / WPR, kStride = 64 * WPR;
+    __shared__ uint32_t s_max[4];
+    const int wave = threadIdx.x >> 6;
+    const int lr = (wave % WPR) * 64 + (threadIdx.x & 63);  // lane within the row's waves
+    const int64_t m = (int64_t)blockIdx.x * kRows + wave / WPR;
+    // with one wave per row a finished wave leaves; with more, every wave reaches the
+    // barrier and rows past M only skip their loads and stores
+    if (WPR == 1 && m >= M) return;
+    const bool live = m < M;
+    const int64_t groups = live ? K / V : 0;
+    const uint16_t* row = x + (live ? m : 0) * K;
 
     QVec<V> held[G > 0 ? G : 1];
     uint32_t mx = 0;
     if (G > 0) {
 #pragma unroll
         for (int i = 0; i < G; ++i) {
-            const int64_t g = lane + (int64_t)i * 64;
+            const int64_t g = lr + (int64_t)i * kStride;
             if (g < groups) {
                 held[i] = load_qvec<V>(row, g);
             } else {
@@ -177,21 +184,29 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restri
             for (int i = 0; i < G; ++i) mx = qvec_max_bits<V>(held[i], mx);
         }
     } else if (MODE != 2) {
-        for (int64_t g = lane; g < groups; g += 64) mx = qvec_max_bits<V>(load_qvec<V>(row, g), mx);
+        for (int64_t g = lr; g < groups; g += kStride) mx = qvec_max_bits<V>(load_qvec<V>(row, g), mx);
     }
-    float a;
+    float a = 0.0f;
     if constexpr (MODE == 2) {
-        a = a_scale[m];
+        if (live) a = a_scale[m];
     } else {
         mx = wave_max_u32(mx);
+        if constexpr (WPR > 1) {
+            if ((threadIdx.x & 63) == 0) s_max[wave] = mx;
+            __syncthreads();
+            const int w0 = wave - wave % WPR;
+            mx = s_max[w0];
+#pragma unroll
+            for (int w = 1; w < WPR; ++w) mx = max(mx, s_max[w0 + w]);
+        }
         if constexpr (MODE == 1) {
-            if (lane == 0) reinterpret_cast<uint32_t*>(a_scale)[m] = mx;  // bits of max |x|
+            if (live && lr == 0) reinterpret_cast<uint32_t*>(a_scale)[m] = mx;  // bits of max |x|
             return;
         }
         float amax = bf16_bits_to_f32(mx);
         amax = amax < 1e-5f ? 1e-5f : amax;
         a = 127.0f / amax;
-        if (lane == 0) a_scale[m] = a;
+        if (live && lr == 0) a_scale[m] = a;
     }
 
     // V codes per group: one word (V = 4) or two (V = 8)
@@ -219,7 +234,7 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restri
     if (G > 0) {
 #pragma unroll
         for (int i = 0; i < G; ++i) {
-            const int64_t g = lane + (int64_t)i * 64;
+            const int64_t g = lr + (int64_t)i * kStride;
             if (g < groups) {
                 uint32_t packed[V / 4];
                 quantv(held[i], packed);
@@ -227,7 +242,7 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restri
             }
         }
     } else {
-        for (int64_t g = lane; g < groups; g += 64) {
+        for (int64_t g = lr; g < groups; g += kStride) {
             uint32_t packed[V / 4];
             quantv(load_qvec<V>(row, g), packed);
             store(g, packed);
@@ -316,25 +331,34 @@ hipError_t launch_unpack_weights(const uint8_t* packed, int64_t N, int64_t K, in
     return hipGetLastError();
 }
 
+template <int MODE, int V, int WPR>
+hipError_t launch_quant_rows_w(const uint16_t* x, int64_t M, int64_t K, int8_t* xq,
+                               float* a_scale, hipStream_t stream) {
+    const int64_t groups = K / V;
+    const int64_t per_lane = (groups + 64 * WPR - 1) / (64 * WPR);
+    constexpr int kRows = 4 / WPR;
+    dim3 grid((unsigned)((M + kRows - 1) / kRows)), blk(256);
+    if (per_lane <= 2)
+        hipLaunchKernelGGL((quant_act_kernel<2, MODE, V, WPR>), grid, blk, 0, stream, x, M, K, xq, a_scale);
+    else if (per_lane <= 4)
+        hipLaunchKernelGGL((quant_act_kernel<4, MODE, V, WPR>), grid, blk, 0, stream, x, M, K, xq, a_scale);
+    else if (per_lane <= 8)
+        hipLaunchKernelGGL((quant_act_kernel<8, MODE, V, WPR>), grid, blk, 0, stream, x, M, K, xq, a_scale);
+    else if (per_lane <= 16)
+        hipLaunchKernelGGL((quant_act_kernel<16, MODE, V, WPR>), grid, blk, 0, stream, x, M, K, xq, a_scale);
+    else
+        hipLaunchKernelGGL((quant_act_kernel<0, MODE, V, WPR>), grid, blk, 0, stream, x, M, K, xq, a_scale);
+    return hipGetLastError();
+}
+
+// Waves per row: enough waves in the launch (about 2048, eight per CU) to cover the
+// memory latency, one per row once M alone provides them.
 template <int MODE, int V>
 hipError_t launch_quant_rows_v(const uint16_t* x, int64_t M, int64_t K, int8_t* xq,
                                float* a_scale, hipStream_t stream) {
-    const int64_t groups = K / V;
-    const int64_t per_lane = (groups + 63) / 64;
-    dim3 grid((unsigned)((M + kQaRowsPerBlock - 1) / kQaRowsPerBlock)), blk(256);
-    if (per_lane <= 2)
-        hipLaunchKernelGGL((quant_act_kernel<2, MODE, V>), grid, blk, 0, stream, x, M, K, xq, a_scale);
-    else if (per_lane <= 4)
-        hipLaunchKernelGGL((quant_act_kernel<4, MODE, V>), grid, blk, 0, stream, x, M, K, xq, a_scale);
-    else if (per_lane <= 8)
-        hipLaunchKernelGGL((quant_act_kernel<8, MODE, V>), grid, blk, 0, stream, x, M, K, xq, a_scale);
-    else if (per_lane <= 16)
-        hipLaunchKernelGGL((quant_act_kernel<16, MODE, V>), grid, blk, 0, stream, x, M, K, xq, a_scale);
-    else if (per_lane <= 32)
-        hipLaunchKernelGGL((quant_act_kernel<32, MODE, V>), grid, blk, 0, stream, x, M, K, xq, a_scale);
-    else
-        hipLaunchKernelGGL((quant_act_kernel<0, MODE, V>), grid, blk, 0, stream, x, M, K, xq, a_scale);
-    return hipGetLastError();
+    if (M <= 512) return launch_quant_rows_w<MODE, V, 4>(x, M, K, xq, a_scale, stream);
+    if (M <= 1024) return launch_quant_rows_w<MODE, V, 2>(x, M, K, xq, a_scale, stream);
+    return launch_quant_rows_w<MODE, V, 1>(x, M, K, xq, a_scale, stream);
 }
 
 // 16-byte loads when rows are whole 8-element groups (K % 8 == 0), else 8-byte ones

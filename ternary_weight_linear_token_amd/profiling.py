@@ -233,6 +233,86 @@ def gemm(util_dir: str, fetch_dir: str, write_dir: str, out: str, cmd: str, sour
     return text
 
 
+def _durations(d: str):
+    """{dispatch id: duration in ns} from the kernel traces under d (runs with --kernel-trace)."""
+    out = {}
+    for path in sorted(glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)):
+        for r in csv.DictReader(open(path)):
+            out[r["Dispatch_Id"]] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    return out
+
+
+def large(util_dir: str, fetch_dir: str, write_dir: str, out: str, cmd: str, hashes: dict,
+          launches) -> str:
+    """Counters of `bench.py --large-probe`: per launch configuration (kernel, grid) in
+    dispatch order -- `launches` gives their names and algorithmic bytes and operations --
+    the mean duration under counter collection, the core clock (GRBM_GUI_ACTIVE per XCD /
+    duration), matrix-core busy fraction, VALU per matrix product and calibrated HBM
+    bytes against the algorithmic ones."""
+    util = {c: _per_dispatch(_counter_rows(util_dir, c)) for c in
+            ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "GRBM_GUI_ACTIVE")}
+    fetch = _per_dispatch(_counter_rows(fetch_dir, "FETCH_SIZE"))
+    write = _per_dispatch(_counter_rows(write_dir, "WRITE_SIZE"))
+    dur = _durations(util_dir)
+
+    def calib(table):
+        vals = [v for n, g, v in table.values()
+                if COPY_KERNEL in n and COPY_TAG in n and "bitnet" not in n]
+        if not vals:
+            raise RuntimeError("the calibration copy was not found in the counter output")
+        vals = vals[1:] if len(vals) > 1 else vals
+        return COPY_BYTES / (statistics.median(vals) * 1024.0)
+
+    f_fetch, f_write = calib(fetch), calib(write)
+
+    def groups(table):
+        """[(kernel, grid, [dispatch ids])] of library product kernels in first-dispatch order"""
+        order, by = [], collections.defaultdict(list)
+        for k in sorted(table, key=int):
+            n, g, _ = table[k]
+            if "skinny_kernel" not in n and "tiled_kernel" not in n:
+                continue
+            key = (_short(n), g)
+            if key not in by:
+                order.append(key)
+            by[key].append(k)
+        return [(k[0], k[1], by[k]) for k in order]
+
+    gu, gf, gw = groups(util["SQ_INSTS_MFMA"]), groups(fetch), groups(write)
+    if not (len(gu) == len(gf) == len(gw) == len(launches)):
+        raise RuntimeError(f"expected {len(launches)} launch configurations, found "
+                           f"{len(gu)} / {len(gf)} / {len(gw)}")
+    lines = ["# Counters of the large-shape launches: 70B decode set at M = 1, 8B and 70B "
+             "prefill GEMMs",
+             f"# command: {cmd}",
+             f"# calibration: FETCH_SIZE reads {1 / f_fetch:.4f}x, WRITE_SIZE "
+             f"{1 / f_write:.4f}x of a {COPY_BYTES}-byte copy",
+             "# per launch: name, kernel, launches, mean us (under counters), core GHz, "
+             "matrix-core busy, VALU per product, HBM read MB, write MB, algorithmic MB, "
+             "traffic / algorithmic"]
+    for (name, alg_bytes), (kern, grid, ids), (_, _, fid), (_, _, wid) in zip(launches, gu, gf, gw):
+        mean = lambda tbl, ks: statistics.mean(tbl[k][2] for k in ks)
+        us = statistics.mean(dur[k] for k in ids if k in dur) / 1e3 if dur else float("nan")
+        gui = mean(util["GRBM_GUI_ACTIVE"], ids) / XCDS
+        ghz = gui / (us * 1e3) if us == us else float("nan")
+        busy = mean(util["SQ_VALU_MFMA_BUSY_CYCLES"], ids) / (gui * SIMDS)
+        vpm = mean(util["SQ_INSTS_VALU"], ids) / max(1.0, mean(util["SQ_INSTS_MFMA"], ids))
+        rd = mean(fetch, fid) * 1024.0 * f_fetch
+        wr = mean(write, wid) * 1024.0 * f_write
+        lines.append(f"#   {name:18s} {kern[:44]:44s} {len(ids):4d} {us:9.2f} {ghz:6.3f} {busy:6.3f} "
+                     f"{vpm:6.2f} {rd / 1e6:9.2f} {wr / 1e6:8.2f} {alg_bytes / 1e6:9.2f} "
+                     f"{(rd + wr) / alg_bytes:6.3f}")
+        lines.append(f"{name}.traffic_over_algorithmic = {(rd + wr) / alg_bytes:.4f}")
+        lines.append(f"{name}.mfma_busy_frac = {busy:.4f}")
+        lines.append(f"{name}.core_clock_ghz = {ghz:.4f}")
+    for k, v in hashes.items():
+        lines.append(f"{k} = {v}")
+    text = "\n".join(lines) + "\n"
+    with open(out, "w") as f:
+        f.write(text)
+    return text
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(prog="python -m ternary_weight_linear_token_amd.profiling")
     sub = ap.add_subparsers(dest="what", required=True)
@@ -251,9 +331,28 @@ def main(argv=None):
     gm.add_argument("--write", required=True)
     gm.add_argument("--out", required=True)
     gm.add_argument("--cmd", required=True)
+    lg = sub.add_parser("large")
+    lg.add_argument("--util", required=True)
+    lg.add_argument("--fetch", required=True)
+    lg.add_argument("--write", required=True)
+    lg.add_argument("--out", required=True)
+    lg.add_argument("--cmd", required=True)
     a = ap.parse_args(argv)
     if a.what == "kernels":
         sys.stdout.write(kernels(a.dir, a.out, a.cmd))
+    elif a.what == "large":
+        from . import build
+        sys.path.insert(0, build.ROOT)
+        import workloads
+        import bench
+        shapes = {name: (N, K) for name, N, K in workloads.LAYER_70B}
+        launches = [("70b_m1_" + "_".join(g), sum(shapes[n][0] * shapes[n][1] // 4 for n in g))
+                    for g in workloads.DECODE_GROUPS]
+        launches += [(name, sum(N * K / 4 + 2 * M * N for N in Ns) + M * K)
+                     for name, M, Ns, K in bench.LARGE_PROBE_GEMM]
+        hashes = {"skinny_source_sha256": build.kernel_hash("skinny.hip"),
+                  "tiled_source_sha256": build.kernel_hash("tiled.hip")}
+        sys.stdout.write(large(a.util, a.fetch, a.write, a.out, a.cmd, hashes, launches))
     elif a.what == "gemm":
         from . import build
         sys.path.insert(0, build.ROOT)
