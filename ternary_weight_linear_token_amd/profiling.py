@@ -247,7 +247,7 @@ def large(util_dir: str, fetch_dir: str, write_dir: str, out: str, cmd: str, has
     """Counters of `bench.py --large-probe`: per launch configuration (kernel, grid) in
     dispatch order -- `launches` gives their names and algorithmic bytes and operations --
     the mean duration under counter collection, the core clock (GRBM_GUI_ACTIVE per XCD /
-    duration), matrix-core busy fraction, VALU per matrix product and calibrated HBM
+    duration, for dispatches of 50 us or more), matrix-core busy fraction, VALU per matrix product and calibrated HBM
     bytes against the algorithmic ones."""
     util = {c: _per_dispatch(_counter_rows(util_dir, c)) for c in
             ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "GRBM_GUI_ACTIVE")}
@@ -266,17 +266,19 @@ def large(util_dir: str, fetch_dir: str, write_dir: str, out: str, cmd: str, has
     f_fetch, f_write = calib(fetch), calib(write)
 
     def groups(table):
-        """[(kernel, grid, [dispatch ids])] of library product kernels in first-dispatch order"""
-        order, by = [], collections.defaultdict(list)
+        """[(kernel, grid, [dispatch ids])] of library product kernels: runs of consecutive
+        dispatches with the same kernel and grid, in dispatch order (the probe runs each
+        launch configuration over all its weight copies before the next)"""
+        runs = []
         for k in sorted(table, key=int):
             n, g, _ = table[k]
             if "skinny_kernel" not in n and "tiled_kernel" not in n:
                 continue
             key = (_short(n), g)
-            if key not in by:
-                order.append(key)
-            by[key].append(k)
-        return [(k[0], k[1], by[k]) for k in order]
+            if not runs or runs[-1][0] != key:
+                runs.append((key, []))
+            runs[-1][1].append(k)
+        return [(key[0], key[1], ids) for key, ids in runs]
 
     gu, gf, gw = groups(util["SQ_INSTS_MFMA"]), groups(fetch), groups(write)
     if not (len(gu) == len(gf) == len(gw) == len(launches)):
@@ -294,7 +296,9 @@ def large(util_dir: str, fetch_dir: str, write_dir: str, out: str, cmd: str, has
         mean = lambda tbl, ks: statistics.mean(tbl[k][2] for k in ks)
         us = statistics.mean(dur[k] for k in ids if k in dur) / 1e3 if dur else float("nan")
         gui = mean(util["GRBM_GUI_ACTIVE"], ids) / XCDS
-        ghz = gui / (us * 1e3) if us == us else float("nan")
+        # short dispatches: the busy window counted around them exceeds their duration,
+        # so the clock is read on long ones only
+        ghz = gui / (us * 1e3) if us == us and us >= 50.0 else float("nan")
         busy = mean(util["SQ_VALU_MFMA_BUSY_CYCLES"], ids) / (gui * SIMDS)
         vpm = mean(util["SQ_INSTS_VALU"], ids) / max(1.0, mean(util["SQ_INSTS_MFMA"], ids))
         rd = mean(fetch, fid) * 1024.0 * f_fetch
@@ -304,7 +308,8 @@ def large(util_dir: str, fetch_dir: str, write_dir: str, out: str, cmd: str, has
                      f"{(rd + wr) / alg_bytes:6.3f}")
         lines.append(f"{name}.traffic_over_algorithmic = {(rd + wr) / alg_bytes:.4f}")
         lines.append(f"{name}.mfma_busy_frac = {busy:.4f}")
-        lines.append(f"{name}.core_clock_ghz = {ghz:.4f}")
+        if ghz == ghz:
+            lines.append(f"{name}.core_clock_ghz = {ghz:.4f}")
     for k, v in hashes.items():
         lines.append(f"{k} = {v}")
     text = "\n".join(lines) + "\n"
