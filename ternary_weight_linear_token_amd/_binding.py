@@ -7,6 +7,7 @@ allocated with torch unless passed in.
 from __future__ import annotations
 
 import ctypes
+import os
 import threading
 
 import torch
@@ -47,9 +48,15 @@ def lib():
     with _lock:
         if _lib is not None:
             return _lib
-        if not _build.is_current():
-            _build.build()
-        L = ctypes.CDLL(_build.LIB_PATH)
+        override = os.environ.get("BITNET_LIBRARY")
+        if override:
+            # a differently built copy of the same sources (the sanitizer build of the
+            # host-side validation layer, run by tests/test_sanitized_boundary.py)
+            L = ctypes.CDLL(override)
+        else:
+            if not _build.is_current():
+                _build.build()
+            L = ctypes.CDLL(_build.LIB_PATH)
         p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         sigs = {
             "bitnet_abi_version": ([], i32),
