@@ -472,12 +472,23 @@ def bench_sweep(bw, workloads, torch, dev, reps):
             R = len(cp)
             for M in spec["Ms"]:
                 x = workloads.activations(M, K, seed=0, outliers=True).to(dev)
+                two_launch_us = None
                 if M <= bw.GEMV_MAX_M:
                     o = torch.empty((M, N), dtype=torch.float32, device=dev)
                     us = graph_launch_us(torch, lambda r: bw.quant_gemv(x, cp[r][0], s, "f32", out=o),
                                          R, reps)
                     nbytes = N * K // 4 + 4 * N + 2 * M * K + 4 * M * N
                     entry, quant_us = "bitnet_quant_gemv", None
+                    if M > 1:
+                        # the same product as two launches: quantization, then the int8
+                        # product (what the bitlinear helper runs above 4 tokens)
+                        xq, a = bw.quant_act(x)
+
+                        def two(r):
+                            bw.quant_act(x, xq=xq, a_scale=a)
+                            bw.gemm(xq, a, cp[r][0], s, "f32", out=o)
+
+                        two_launch_us = graph_launch_us(torch, two, R, reps)
                 else:
                     xq, a = bw.quant_act(x)
                     o = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
@@ -494,6 +505,8 @@ def bench_sweep(bw, workloads, torch, dev, reps):
                 e.update(roofline_entry(us, ops, nbytes))
                 if quant_us is not None:
                     e["quant_us"] = round(quant_us, 3)
+                if two_launch_us is not None:
+                    e["quant_then_gemm_us"] = round(two_launch_us, 3)
                 entries.append(e)
                 del o, x
             del cp, p
@@ -509,7 +522,8 @@ def sweep_summaries(sweep):
         ops = us = 0.0
         per = {}
         for n in names:
-            e = by.get((tag, n, M)) or by.get((tag, {"v": "k", "up": "gate"}.get(n, n), M))
+            # projections of equal shape are measured once (v as k, o as q, up as gate)
+            e = by.get((tag, n, M)) or by.get((tag, {"v": "k", "o": "q", "up": "gate"}.get(n, n), M))
             if e is None:
                 return None
             ops += 2.0 * M * e["N"] * e["K"]
