@@ -481,7 +481,7 @@ def bench_sweep(bw, workloads, torch, dev, reps):
                     entry, quant_us = "bitnet_quant_gemv", None
                     if M > 1:
                         # the same product as two launches: quantization, then the int8
-                        # product (what the bitlinear helper runs above 4 tokens)
+                        # product (what the bitlinear helper runs above 4 tokens or M * K = 32768)
                         xq, a = bw.quant_act(x)
 
                         def two(r):

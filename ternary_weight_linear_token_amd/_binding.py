@@ -455,13 +455,18 @@ def quant_gemv_b3(x, b3, w_scale, out_dtype="f32", out=None):
     return out
 
 
-FUSED_MAX_M = 4  # above this, one quantization launch beats requantizing in every block
+# The fused launch quantizes the activations in every block of 16 output rows, so its
+# cost grows with the bf16 bytes each block re-reads (M * K); past these limits one
+# quantization launch followed by the int8 product is faster.
+FUSED_MAX_M = 4
+FUSED_MAX_MK = 32768
 
 
 def bitlinear(x, packed, w_scale, out_dtype="f32"):
-    """One BitLinear forward: fused quant+GEMV for a few tokens, else quant + GEMM."""
-    M = x.shape[0]
-    if M <= FUSED_MAX_M:
+    """One BitLinear forward: fused quant+GEMV for one token, or a few tokens of a short
+    row, else quant + GEMM."""
+    M, K = x.shape
+    if M == 1 or (M <= FUSED_MAX_M and M * K <= FUSED_MAX_MK):
         return quant_gemv(x, packed, w_scale, out_dtype)
     xq, a_scale = quant_act(x)
     return gemm(xq, a_scale, packed, w_scale, out_dtype)

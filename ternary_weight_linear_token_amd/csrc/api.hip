@@ -11,6 +11,12 @@
 #include "bitnet_w2a8.h"
 #include "kernels.hpp"
 
+// Fewest tokens the fused quant + GEMV entry point sends to the register-quantizing
+// kernel (K % 64 == 0); fewer go to the staged kernel.
+#ifndef BITNET_FUSED_DIRECT_MIN_M
+#define BITNET_FUSED_DIRECT_MIN_M 12
+#endif
+
 namespace {
 
 thread_local char g_last_hip_error[256] = "";
@@ -351,7 +357,7 @@ int bitnet_quant_gemv(const uint16_t* x, const uint8_t* packed, const float* w_s
     if ((st = check_device())) return st;
     // 12 to 16 tokens: the kernel that quantizes in registers (its whole-row max scan is
     // cheaper there than the staged kernel's LDS copy); fewer: the staged kernel
-    if (M >= 12 && K % 64 == 0)
+    if (M >= BITNET_FUSED_DIRECT_MIN_M && K % 64 == 0)
         return record_hip(bitnet::launch_gemv_direct(nullptr, nullptr, x, packed, w_scale, M, N,
                                                      K, out, out_dtype, xq_out, a_scale_out,
                                                      as_stream(stream)));

@@ -121,6 +121,62 @@ __device__ __forceinline__ uint32_t absmax_bits16(const uint32_t h[8]) {
     return max((uint32_t)m.x, (uint32_t)m.y);
 }
 
+// Per-token max |x| of bf16 activations as bf16 bits with the sign cleared.  x is a
+// buffer resource over the (M, K) rows (M * K * 2 bytes).  Wave w of W scans rows w,
+// w + W, ...; lane 0 writes the maximum of row m to slot[m].  A lane asks for a batch of
+// 8 loads (16 bytes each when W16, i.e. K % 8 == 0, else 8 bytes; zeros past the row)
+// and for the next batch before it reduces the current one, so the scan waits about
+// once per batch pair instead of once per load of every row.
+template <bool W16>
+__device__ __forceinline__ void scan_absmax_rows(__amdgpu_buffer_rsrc_t x, int M, int K, int w,
+                                                 int W, uint32_t* slot) {
+    constexpr int PE = W16 ? 8 : 4;   // bf16 values per load
+    constexpr int NB = 8;             // loads per lane per batch
+    constexpr int NWD = NB * PE / 2;  // words per lane per batch
+    const int lane = threadIdx.x & 63;
+    const int span = 64 * NB * PE;          // row elements per batch
+    const int bpr = (K + span - 1) / span;  // batches per row
+    const int items = (w < M ? (M - 1 - w) / W + 1 : 0) * bpr;
+    auto load = [&](int t, uint32_t (&v)[NWD]) {
+        const int r = t / bpr;
+        const int m = w + W * r, kb = (t - r * bpr) * span;
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const int k = kb + PE * (lane + 64 * i);
+            // K % PE == 0: a load is wholly inside its row or wholly past its end
+            const uint32_t off =
+                (t < items && k < K) ? (uint32_t)(((int64_t)m * K + k) * 2) : 0x80000000u;
+            if constexpr (W16) {
+                const auto u = __builtin_amdgcn_raw_buffer_load_b128(x, off, 0, 0);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) v[4 * i + j] = u[j];
+            } else {
+                const auto u = __builtin_amdgcn_raw_buffer_load_b64(x, off, 0, 0);
+                v[2 * i] = u[0];
+                v[2 * i + 1] = u[1];
+            }
+        }
+    };
+    uint32_t mx = 0;
+    auto reduce = [&](int t, const uint32_t (&v)[NWD]) {
+#pragma unroll
+        for (int i = 0; i < NWD; i += 8) mx = max(mx, absmax_bits16(v + i));
+        if ((t + 1) % bpr == 0) {  // the last batch of its row (uniform)
+            const uint32_t r = wave_max_u32(mx);
+            if (lane == 0) slot[w + W * (t / bpr)] = r;
+            mx = 0;
+        }
+    };
+    uint32_t a[NWD], b[NWD];
+    load(0, a);
+    for (int t = 0; t < items; t += 2) {
+        load(t + 1, b);  // past the wave's rows: zeros, never reduced
+        reduce(t, a);
+        load(t + 2, a);
+        if (t + 1 < items) reduce(t + 1, b);
+    }
+}
+
 // Element-order codes of a transposed group (for the optional copy of the codes).
 __device__ __forceinline__ void untranspose(const uint32_t e[4], uint32_t d[4]) {
     transpose4x4_bytes(e, d);  // the 4x4 byte transpose is its own inverse

@@ -21,8 +21,9 @@
 //    is requested before the current one is multiplied; chunks past the end read zeros
 //    through out-of-range buffer offsets.
 //  * int32 partials of the four waves are added through LDS, then rescaled.
-//  * Fused variant (bf16 activations): the block first finds every token's max |x| (all
-//    threads scan the M rows, wave reductions, one barrier), then each lane quantizes
+//  * Fused variant (bf16 activations): the block first finds every token's max |x| (wave
+//    w scans rows w, w + 4, ... with batched loads, one barrier; the first batch of
+//    weights is already on its way), then each lane quantizes
 //    its 16 activations per operand in registers (fp32 multiply, round half to even by
 //    the 1.5 * 2^23 addition), already in the transposed order.  The first block also
 //    writes the codes and scales when asked.
@@ -85,31 +86,6 @@ __global__ __launch_bounds__(64 * kDrWaves) void gemv_direct_kernel(DirectArgs p
     const bool x_row = l16 < M;   // this lane's token of the first tile
     constexpr int XW = FUSED ? 2 : 1;  // 16-byte loads per 16-activation group
 
-    // fused: every token's scale 127 / max|x| from a scan of its row by the whole block
-    float a_row = 0.f;  // scale of this lane's token (fused)
-    if constexpr (FUSED) {
-        const int pieces = K / 8;  // 16-byte pieces (8 bf16) per row
-        for (int m = 0; m < M; ++m) {
-            uint32_t mx = 0;
-            for (int i = tid; i < pieces; i += 64 * kDrWaves) {
-                const u32x4_d v = dr_load16(x_rsrc, (uint32_t)((m * K + 8 * i) * 2));
-                const uint32_t h[8] = {v[0], v[1], v[2], v[3], 0u, 0u, 0u, 0u};
-                mx = max(mx, absmax_bits16(h));
-            }
-            mx = wave_max_u32(mx);
-            if (lane == 0) s_max[wave][m] = mx;
-        }
-        __syncthreads();
-        const int mr = x_row ? l16 : 0;
-        uint32_t mx = s_max[0][mr];
-#pragma unroll
-        for (int w = 1; w < kDrWaves; ++w) mx = max(mx, s_max[w][mr]);
-        float amax = bf16_bits_to_f32(mx);
-        amax = amax < 1e-5f ? 1e-5f : amax;
-        a_row = 127.0f / amax;
-        if (blockIdx.x == 0 && p.a_out && lane < M && tid < 64) p.a_out[lane] = a_row;
-    }
-
     // chunk j of this wave: 16 packed bytes and, per token tile, the four 16-activation
     // groups
     auto load = [&](int j, u32x4_d& w, u32x4_d (&X)[MT][4][XW]) {
@@ -128,6 +104,26 @@ __global__ __launch_bounds__(64 * kDrWaves) void gemv_direct_kernel(DirectArgs p
                     X[t][s][h] = dr_load16(x_rsrc, ok ? (uint32_t)((mrow * K + k0) * XW + 16 * h) : kDrOOB);
             }
     };
+
+    // batches of U chunks, two in flight: batch t + 1 is requested before batch t is
+    // multiplied; batches past the wave's chunks read zeros.  The first batch is requested
+    // before the fused scan, so its trip from memory overlaps the scan.
+    const int nj = (nch - wave + kDrWaves - 1) / kDrWaves;  // chunks of this wave
+    u32x4_d wA[U], XA[U][MT][4][XW], wB[U], XB[U][MT][4][XW];
+#pragma unroll
+    for (int u = 0; u < U; ++u) load(u, wA[u], XA[u]);
+
+    // fused: every token's scale 127 / max|x| from a scan of its row by one wave
+    float a_row = 0.f;  // scale of this lane's token (fused)
+    if constexpr (FUSED) {
+        scan_absmax_rows<true>(x_rsrc, M, K, wave, kDrWaves, s_max[wave]);
+        __syncthreads();
+        const int mr = x_row ? l16 : 0;
+        float amax = bf16_bits_to_f32(s_max[mr % kDrWaves][mr]);  // written by wave mr % 4
+        amax = amax < 1e-5f ? 1e-5f : amax;
+        a_row = 127.0f / amax;
+        if (blockIdx.x == 0 && p.a_out && lane < M && tid < 64) p.a_out[lane] = a_row;
+    }
 
     v4i_d acc[MT];
 #pragma unroll
@@ -161,12 +157,6 @@ __global__ __launch_bounds__(64 * kDrWaves) void gemv_direct_kernel(DirectArgs p
             }
         }
     };
-    // batches of U chunks, two in flight: batch t + 1 is requested before batch t is
-    // multiplied; batches past the wave's chunks read zeros
-    const int nj = (nch - wave + kDrWaves - 1) / kDrWaves;  // chunks of this wave
-    u32x4_d wA[U], XA[U][MT][4][XW], wB[U], XB[U][MT][4][XW];
-#pragma unroll
-    for (int u = 0; u < U; ++u) load(u, wA[u], XA[u]);
     for (int j0 = 0; j0 < nj; j0 += 2 * U) {
 #pragma unroll
         for (int u = 0; u < U; ++u) load(j0 + U + u, wB[u], XB[u]);
@@ -198,10 +188,7 @@ __global__ __launch_bounds__(64 * kDrWaves) void gemv_direct_kernel(DirectArgs p
             // 1/a: v_rcp_f32 is within 1 ulp, and the rescale stays within 3 ulp
             float a_m;
             if constexpr (FUSED) {
-                uint32_t mx = s_max[0][m];
-#pragma unroll
-                for (int w = 1; w < kDrWaves; ++w) mx = max(mx, s_max[w][m]);
-                float amax = bf16_bits_to_f32(mx);
+                float amax = bf16_bits_to_f32(s_max[m % kDrWaves][m]);
                 amax = amax < 1e-5f ? 1e-5f : amax;
                 a_m = 127.0f / amax;
             } else {

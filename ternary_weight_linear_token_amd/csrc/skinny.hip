@@ -18,7 +18,11 @@
 //    quantization run, so it overlaps the weights' trip from memory.  The loads are
 //    unconditional: a chunk or row outside the problem gets an offset past the buffer
 //    resource's range, which reads as zeros, so the compiler counts the loads in flight
-//    exactly and never has to drain them all before the first use.
+//    exactly and never has to drain them all before the first use.  When the
+//    activations are staged in loops instead (more than fit in registers), the first
+//    weight batch is requested before them.
+//  * Fused max |x| scan of the staged variant: wave w reads rows w, w + 4, ... with
+//    batches of independent loads, two batches in flight, before one block barrier.
 //  * The activations (M <= 16 rows) sit in LDS; each chunk feeds int8 matrix-core
 //    products v_mfma_i32_16x16x64_i8 with the activations as operand A (rows m) and
 //    the weight codes as operand B (columns n).
@@ -420,21 +424,18 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
             }
         }
         if (MC == 1) wsum_m1 = wave_sum_uniform(rsum);
-    } else if constexpr (FUSED) {
-        // ---- max |x| per token over the whole row, 4 elements per load ----
-        const int groups = K / 4;
-        for (int m = 0; m < M; ++m) {
-            const uint2* row = reinterpret_cast<const uint2*>(p.xb + (int64_t)m * K);
-            uint32_t mx = 0;
-            for (int g = tid; g < groups; g += kSkThreads) {
-                const uint2 v = row[g];
-                const uint32_t a = v.x & 0x7FFF7FFFu, b = v.y & 0x7FFF7FFFu;
-                mx = max(mx, max(max(a & 0xFFFFu, a >> 16), max(b & 0xFFFFu, b >> 16)));
-            }
-            mx = row16_max(mx);
-            if (row_leader) atomicMax(&s_wmax[wave * kSkMaxM + m], mx);
+    } else {
+        // the first weights of stage 0 are requested before the activations are read
+        load_batch(wa, 0, 0, nch0);
+        if constexpr (FUSED) {
+            // ---- max |x| per token over the whole row: wave w scans rows w, w + 4, ... ----
+            const __amdgpu_buffer_rsrc_t x_rsrc = make_rsrc(p.xb, (uint32_t)(M * K * 2));
+            if (K % 8 == 0)
+                scan_absmax_rows<true>(x_rsrc, M, K, wave, kSkWaves, s_wmax + wave * kSkMaxM);
+            else
+                scan_absmax_rows<false>(x_rsrc, M, K, wave, kSkWaves, s_wmax + wave * kSkMaxM);
+            __syncthreads();
         }
-        __syncthreads();
     }
 
     auto run_stage = [&](int ks) {
@@ -504,7 +505,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
                     }
                 }
             }
-            load_batch(wa, 0, stage_off, nch);
+            if (ks > 0) load_batch(wa, 0, stage_off, nch);  // stage 0's: before the scan
         }
         // The activations this wave multiplies are its own LDS writes, and the LDS
         // operations of a wave complete in order; keep the compiler from hoisting reads.

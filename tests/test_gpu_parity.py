@@ -226,6 +226,34 @@ def test_quant_gemv_matches_oracle(M, N, K):
         check_out(to_np(out), o["acc"], o["ref"], dt, f"quant_gemv M={M} N={N} K={K} {dt}")
 
 
+@pytest.mark.parametrize("M,N,K", [
+    (3, 40, 14340),    # staged kernel, 8-byte scan loads (K % 8 != 0), one row per wave
+    (6, 70, 14340),    # two K stages, waves with two rows
+    (11, 33, 8200),    # 16-byte scan loads, three batches per row, odd batch counts
+    (16, 50, 12292),   # 16 tokens on the staged kernel (K % 64 != 0)
+    (13, 100, 14336),  # the direct kernel, four batches per row
+    (16, 300, 4096),   # the direct kernel, one batch per row
+])
+def test_fused_scan_finds_each_rows_peak(M, N, K):
+    """The fused launches scan every token's max |x| before they quantize: row m gets
+    its largest magnitude at a position of its own (the last element for one row, the
+    first for another), with a sign and size of its own, so a row mixed up with another
+    or a batch left out changes a scale."""
+    gen = torch.Generator().manual_seed(M * 31 + K)
+    X = (torch.rand(M, K, generator=gen) * 2 - 1).to(torch.bfloat16)
+    for m in range(M):
+        pos = K - 1 if m == 1 else (0 if m == 2 else (m * 7919 + 13) % K)
+        X[m, pos] = (-1) ** m * (4.0 + 0.75 * m)
+    pb = Problem(M, N, K, seed=M + K, X=X)
+    o = pb.oracle()
+    packed, s = dev(o["packed"]), dev(o["w_scale"])
+    for dt in DT:
+        out, xq, a = bw.quant_gemv(pb.x_dev, packed, s, dt, return_quant=True)
+        assert np.array_equal(to_np(a), o["a_scale"]), f"a_scale M={M} K={K}"
+        assert np.array_equal(to_np(xq), o["xq"]), f"xq M={M} K={K}"
+        check_out(to_np(out), o["acc"], o["ref"], dt, f"fused scan M={M} N={N} K={K} {dt}")
+
+
 @pytest.mark.parametrize("M", [1, 3, 16])
 @pytest.mark.parametrize("K,Ns", [(1024, [300, 37, 16]), (2560, [640, 640, 2560]),
                                   (260, [129, 0, 50]), (256, [16]),
@@ -504,8 +532,9 @@ def test_tiny_workload_chain(dt):
 @pytest.mark.parametrize("M", [1, 4, 5, 16, 17, 40, 64, 65, 200])
 def test_bitlinear_every_route(M):
     # bitlinear picks the fused decode launch, or quantization plus the skinny or tiled
-    # product, by M and N; every route must give the oracle's result.
-    for N, K in ((300, 1024), (4096, 256)):
+    # product, by M, N and K (a long row sends 4 tokens to the two-launch route); every
+    # route must give the oracle's result.
+    for N, K in ((300, 1024), (4096, 256), (64, 16384)):
         pb = Problem(M, N, K, seed=M * 11 + N)
         o = pb.oracle()
         packed, s = dev(o["packed"]), dev(o["w_scale"])
