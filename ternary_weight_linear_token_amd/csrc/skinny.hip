@@ -37,6 +37,9 @@
 //  * Per-row maxima and code sums are reduced per wave (wave reductions at M = 1, atomics
 //    on the wave's own LDS slots otherwise), so no block-wide atomic is contended.
 //  * Per-wave int32 partials are combined through LDS; one pass writes the outputs.
+//  * One token over a large grid (768+ blocks of 16 rows): a block takes two 16-row
+//    tiles, whose weight operands share each activation operand, so half as many
+//    blocks read and quantize the activations.
 //  * Grouped launches: up to kSkGroups weight matrices that read the same activations
 //    (q, k and v of an attention block; gate and up of an MLP) share one launch.  The
 //    grid is the concatenation of the groups' row blocks; a block picks its group with
@@ -89,6 +92,12 @@ __device__ __forceinline__ T pick(const T (&a)[4], int i) {
 }
 
 constexpr int kSkGroups = BITNET_MAX_GROUPS;
+// Fewest 16-row blocks (three per CU of a 256-CU chip) at which a one-token launch
+// switches to 32-row blocks: with fewer, the halved grid leaves CUs idle.
+#ifndef BITNET_SKINNY_TWO_TILE_MIN_BLOCKS
+#define BITNET_SKINNY_TWO_TILE_MIN_BLOCKS 768
+#endif
+constexpr int64_t kSkTwoTileMinBlocks = BITNET_SKINNY_TWO_TILE_MIN_BLOCKS;
 
 struct SkinnyArgs {
     const int8_t* xq;
@@ -199,9 +208,13 @@ __device__ __forceinline__ int put_group_t(unsigned char* x_lds, int KSP, int m,
 //  MT     - 16-row tiles of tokens (M <= 16 MT); the weights of a chunk feed all of them
 //  PAIR   - SwiGLU pair: the block multiplies the same 16 rows of two matrices (gate =
 //           group 0, up = group 1) and writes silu(gate) * up
-template <bool FUSED, bool FAST, int XH, int U, bool SINGLE, int MC, int MT = 1, bool PAIR = false>
+//  NR     - 16-row tiles of one matrix per block (1 or 2; 2 with one token only): the
+//           tiles share the block's copy of the activations
+template <bool FUSED, bool FAST, int XH, int U, bool SINGLE, int MC, int MT = 1, bool PAIR = false,
+          int NR = 1>
 __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
-    constexpr int NW = PAIR ? 2 : 1;  // weight matrices per block
+    static_assert(NR == 1 || (NR == 2 && MC == 1 && FAST && !PAIR), "two row tiles: one token");
+    constexpr int NW = PAIR ? 2 : NR;  // weight operands per chunk (matrices or row tiles)
     extern __shared__ __align__(16) unsigned char smem[];
     const int KSP = p.KS + 16;  // padded LDS row stride: spreads rows over the banks
     const int M = MC > 0 ? MC : p.M;
@@ -219,6 +232,9 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
     if constexpr (PAIR) {
         packed_v[1] = p.g_packed[1];
         w_scale_v[1] = p.g_wscale[1];
+    } else if constexpr (NR == 2) {
+        packed_v[1] = packed_v[0];
+        w_scale_v[1] = w_scale_v[0];
     }
     void* const out = pick(p.g_out, gi);
     unsigned char* x_lds = smem;
@@ -231,18 +247,25 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
     const int row_bytes = K / 4;
-    const int n0 = ((int)blockIdx.x - pick(p.first, gi)) * 16;
-    const int rows = min(16, N - n0);
+    const int n0 = ((int)blockIdx.x - pick(p.first, gi)) * 16 * NR;
+    // first row and row count (0 past the end of N) of operand v's 16-row tile
+    int nv0[NW], rows_v[NW];
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+        nv0[v] = min(n0 + (PAIR ? 0 : 16 * v), N);
+        rows_v[v] = min(16, N - nv0[v]);
+    }
+    const int rows = rows_v[0];
     const int mrow = lane & 15;  // operand-A row (token) and operand-B column of this lane
     const int q = lane >> 4;     // k-group of this lane inside a 256-weight chunk
     const bool row_leader = (lane & 15) == 0;
 
-    // scales needed at the end, requested first (threads tid < 16 M write outputs)
+    // scales needed at the end, requested first (threads tid < 16 M NR write outputs)
     float ws_n[NW];
 #pragma unroll
     for (int v = 0; v < NW; ++v)
-        ws_n[v] = buf_load_f32(make_rsrc(w_scale_v[v] + n0, (uint32_t)(rows * 4)),
-                               tid < 16 * M ? (uint32_t)(4 * (tid & 15)) : kOOB);
+        ws_n[v] = buf_load_f32(make_rsrc(w_scale_v[v] + nv0[v], (uint32_t)(rows_v[v] * 4)),
+                               tid < 16 * M * NR ? (uint32_t)(4 * (tid & 15)) : kOOB);
     float a_in = 0.0f;  // M = 1: every thread holds the token's scale
     if constexpr (!FUSED)
         a_in = buf_load_f32(make_rsrc(p.a_scale, (uint32_t)(M * 4)),
@@ -252,7 +275,8 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
     __amdgpu_buffer_rsrc_t w_rsrc[NW];
 #pragma unroll
     for (int v = 0; v < NW; ++v)
-        w_rsrc[v] = make_rsrc(packed_v[v] + (int64_t)n0 * row_bytes, (uint32_t)(rows * row_bytes));
+        w_rsrc[v] = make_rsrc(packed_v[v] + (int64_t)nv0[v] * row_bytes,
+                              (uint32_t)(rows_v[v] * row_bytes));
     const uint32_t w_lane = (uint32_t)(mrow * row_bytes + 16 * q);
 
     // chunks c = wave + 4 * (j0 + uu), uu < U, of the stage starting at byte stage_off;
@@ -567,6 +591,22 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
         }
     }
     __syncthreads();
+    if constexpr (NR == 2) {
+        // one token, two row tiles: thread tid < 32 writes column tid % 16 of tile tid / 16
+        if (tid < 32) {
+            const bool hi = tid >= 16;
+            const int col = tid & 15;
+            if (col < (hi ? rows_v[1] : rows_v[0])) {
+                int acc = 0;
+#pragma unroll
+                for (int w = 0; w < kSkWaves; ++w) acc += red[(hi ? kRedSet : 0) + w * 256 + col];
+                const float inv_a = __builtin_amdgcn_rcpf(FUSED ? a_m1 : a_in);
+                store_out(out, (int64_t)(hi ? nv0[1] : nv0[0]) + col, p.out_dtype, acc,
+                          hi ? ws_n[1] : ws_n[0], inv_a);
+            }
+        }
+        return;
+    }
     for (int idx = tid; idx < 16 * M; idx += kSkThreads) {
         // 16x16 int32 accumulator layout: lane l, register r -> row 4*(l/16)+r, column l%16
         const int m = idx >> 4, col = idx & 15;
@@ -609,10 +649,11 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
 constexpr int kSkMaxDevices = 64;
 constexpr int kSkLdsMax = 160 * 1024;
 
-template <bool FUSED, bool FAST, int XH, int U, bool SINGLE, int MC = 0, int MT = 1, bool PAIR = false>
+template <bool FUSED, bool FAST, int XH, int U, bool SINGLE, int MC = 0, int MT = 1, bool PAIR = false,
+          int NR = 1>
 hipError_t launch_one(const SkinnyArgs& a, dim3 grid, size_t lds, hipStream_t stream) {
     static std::atomic<bool> granted[kSkMaxDevices];
-    auto* kernel = &skinny_kernel<FUSED, FAST, XH, U, SINGLE, MC, MT, PAIR>;
+    auto* kernel = &skinny_kernel<FUSED, FAST, XH, U, SINGLE, MC, MT, PAIR, NR>;
     if (lds > 65536) {
         if (lds > (size_t)kSkLdsMax) return hipErrorInvalidValue;
         int dev = 0;
@@ -640,18 +681,26 @@ hipError_t launch_fast(const SkinnyArgs& a, dim3 grid, size_t lds, hipStream_t s
     return launch_one<FUSED, true, XH, 8, false, 0, 1, PAIR>(a, grid, lds, stream);
 }
 
+// One token (decode), a single K stage of at most 32 chunks per wave: the M = 1
+// specializations, by K.
+template <bool FUSED, bool PAIR = false, int NR = 1>
+hipError_t launch_m1(const SkinnyArgs& a, dim3 grid, size_t lds, hipStream_t stream) {
+    const int cpw = chunks_of_wave(0, a.Kp / 256);
+    if (cpw <= 4) return launch_one<FUSED, true, 1, 4, true, 1, 1, PAIR, NR>(a, grid, lds, stream);
+    if (cpw <= 8) return launch_one<FUSED, true, 2, 8, true, 1, 1, PAIR, NR>(a, grid, lds, stream);
+    if (cpw <= 16) return launch_one<FUSED, true, 4, 8, false, 1, 1, PAIR, NR>(a, grid, lds, stream);
+    return launch_one<FUSED, true, 8, 8, false, 1, 1, PAIR, NR>(a, grid, lds, stream);
+}
+bool m1_fits(const SkinnyArgs& a) {
+    return a.M == 1 && a.KS >= a.Kp && chunks_of_wave(0, a.Kp / 256) <= 32;
+}
+
 // Held activation groups per lane: M * (chunks per wave) * 16 groups over 64 lanes.
 template <bool FUSED, bool PAIR = false>
 hipError_t launch_held(const SkinnyArgs& a, dim3 grid, size_t lds, hipStream_t stream) {
     const int cpw = chunks_of_wave(0, a.Kp / 256);
     const int per_lane = (a.M * cpw + 3) / 4;
-    if (a.M == 1 && a.KS >= a.Kp) {
-        // one token (decode): the M = 1 specializations, by K
-        if (cpw <= 4) return launch_one<FUSED, true, 1, 4, true, 1, 1, PAIR>(a, grid, lds, stream);
-        if (cpw <= 8) return launch_one<FUSED, true, 2, 8, true, 1, 1, PAIR>(a, grid, lds, stream);
-        if (cpw <= 16) return launch_one<FUSED, true, 4, 8, false, 1, 1, PAIR>(a, grid, lds, stream);
-        if (cpw <= 32) return launch_one<FUSED, true, 8, 8, false, 1, 1, PAIR>(a, grid, lds, stream);
-    }
+    if (m1_fits(a)) return launch_m1<FUSED, PAIR>(a, grid, lds, stream);
     if (a.KS >= a.Kp) {
         if (per_lane <= 1) return launch_fast<FUSED, 1, PAIR>(a, grid, lds, stream);
         if (per_lane <= 2) return launch_fast<FUSED, 2, PAIR>(a, grid, lds, stream);
@@ -694,6 +743,13 @@ hipError_t launch_skinny_grouped(const int8_t* xq, const float* a_scale, const u
     a.xq_out = xq_out;
     a.a_out = a_out;
     a.groups = groups;
+    set_stage(a, M, K);
+    a.out_dtype = out_dtype;
+    // One token over many rows: blocks of two 16-row tiles, so half as many blocks read
+    // (and, fused, quantize) the activations.
+    int64_t blocks16 = 0;
+    for (int g = 0; g < groups; ++g) blocks16 += (N[g] + 15) / 16;
+    const int nr = (K % 64 == 0 && m1_fits(a) && blocks16 >= kSkTwoTileMinBlocks) ? 2 : 1;
     int64_t blocks = 0;
     for (int g = 0; g < kSkGroups; ++g) {
         const bool live = g < groups;
@@ -702,15 +758,16 @@ hipError_t launch_skinny_grouped(const int8_t* xq, const float* a_scale, const u
         a.g_packed[g] = live ? packed[g] : nullptr;
         a.g_wscale[g] = live ? w_scale[g] : nullptr;
         a.g_out[g] = live ? out[g] : nullptr;
-        if (live) blocks += (N[g] + 15) / 16;
+        if (live) blocks += (N[g] + 16 * nr - 1) / (16 * nr);
     }
     if (blocks == 0) return hipSuccess;
     if (blocks > INT32_MAX) return hipErrorInvalidValue;
-    set_stage(a, M, K);
-    a.out_dtype = out_dtype;
-    const size_t lds = (size_t)M * (a.KS + 16) + kSkMisc + (size_t)kSkWaves * 4 * 64 * 4;
+    const size_t lds = (size_t)M * (a.KS + 16) + kSkMisc + (size_t)nr * kSkWaves * 4 * 64 * 4;
     const dim3 grid((unsigned)blocks);
     const bool fused = x_bf16 != nullptr;
+    if (nr == 2)
+        return fused ? launch_m1<true, false, 2>(a, grid, lds, stream)
+                     : launch_m1<false, false, 2>(a, grid, lds, stream);
     if (M > 16) {
         if (fused) return hipErrorInvalidValue;  // the fused entry point takes M <= 16
         // 17..64 tokens (int8 input only): 2 or 4 token tiles per chunk of weights.  The

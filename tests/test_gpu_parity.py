@@ -254,6 +254,32 @@ def test_fused_scan_finds_each_rows_peak(M, N, K):
         check_out(to_np(out), o["acc"], o["ref"], dt, f"fused scan M={M} N={N} K={K} {dt}")
 
 
+@pytest.mark.parametrize("K,Ns", [(512, [12304]), (256, [12312]), (256, [6912, 6912, 300]),
+                                  (2560, [13824, 13830])])
+def test_one_token_two_tile_blocks(K, Ns):
+    """One token over 768+ row blocks runs blocks of two 16-row tiles: ragged ends where
+    the second tile is partial or empty, grouped launches whose groups end mid-block,
+    int8 and fused inputs."""
+    pb = Problem(1, 1, K, seed=K + len(Ns))
+    o1 = pb.oracle(full=False)
+    xq, a = dev(o1["xq"]), dev(o1["a_scale"])
+    packs, scales, refs = [], [], []
+    for g, N in enumerate(Ns):
+        W = workloads.latent_weights(N, K, seed=g + 5)
+        p, s = oracle.pack_weights(W.numpy())
+        acc = oracle.accumulate(o1["xq"], p, K)
+        ref, _, _ = oracle.rescale(acc, o1["a_scale"], s)
+        packs.append(dev(p)); scales.append(dev(s)); refs.append((acc, ref))
+    for dt in DT:
+        outs = (bw.quant_gemv_grouped(pb.x_dev, packs, scales, dt) if len(Ns) > 1
+                else [bw.quant_gemv(pb.x_dev, packs[0], scales[0], dt)])
+        for g, (out, (acc, ref)) in enumerate(zip(outs, refs)):
+            check_out(to_np(out), acc, ref, dt, f"two-tile fused K={K} group {g} {dt}")
+        if len(Ns) == 1:
+            out = bw.gemv(xq, a, packs[0], scales[0], dt)
+            check_out(to_np(out), refs[0][0], refs[0][1], dt, f"two-tile int8 K={K} {dt}")
+
+
 @pytest.mark.parametrize("M", [1, 3, 16])
 @pytest.mark.parametrize("K,Ns", [(1024, [300, 37, 16]), (2560, [640, 640, 2560]),
                                   (260, [129, 0, 50]), (256, [16]),
