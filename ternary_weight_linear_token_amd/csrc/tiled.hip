@@ -28,12 +28,15 @@
 //    per lane per 32 columns and stage, and unpacked there: field i of each byte is masked out and mapped by a
 //    v_perm byte lookup to the signed weight (c - 1), so register i, byte b holds weight
 //    k = 4 b + i -- the same k-order as operand A.
-//  * No split across blocks: handing int32 partial tiles between blocks needs
-//    device-scope release/acquire, which on this chip (one L2 per XCD) costs more than
-//    the split saves.  Small grids instead split K inside the block: 128x128 blocks of
-//    two four-wave k-groups and 64x128 blocks of four (alternate k-stages, accumulators
-//    combined through LDS), so each SIMD interleaves two or four waves.  The tile shape
-//    and k-stage of a launch are the ones with the least estimated time (plan_tiles).
+//  * Small grids split K inside the block: 128x128 blocks of two four-wave k-groups and
+//    64x128 blocks of four (alternate k-stages, accumulators combined through LDS), so
+//    each SIMD interleaves two or four waves.  Across blocks, K is split only through a
+//    second launch: units write int32 partial tiles to the caller's workspace and the
+//    reduce kernel adds them (handing partials between blocks inside one launch needs
+//    device-scope release/acquire across the XCDs' L2s, which costs more than it saves).
+//  * Full-chip grids use 128x128 blocks of one k-group (waves 1 x 4): two blocks per CU,
+//    so each SIMD interleaves two waves of different tiles.  The tile shape, k-stage and
+//    K slices of a launch are the ones with the least estimated time (plan_tiles).
 //  * Blocks are mapped to work units XCD by XCD (dispatch assigns consecutive blocks to
 //    the 8 XCDs in turn), and units are ordered in panels of tile rows, so an XCD's L2
 //    holds a few activation row panels and a few weight column panels.
@@ -575,7 +578,7 @@ int device_cus() {
 }
 
 // Optional override for tuning: BITNET_TILED_CONFIG="bm,bn,g" or "bm,bn,g,ksplit", one of
-// the compiled configurations (256,256,1 / 256,128,1 / 128,128,2 / 64,128,4), with an
+// the compiled configurations (256,256,1 / 256,128,1 / 128,128,2 / 128,128,1 / 64,128,4), with an
 // optional number of K slices (used only where splitting is allowed); read once per
 // process.
 struct ConfigOverride {
@@ -591,7 +594,8 @@ const ConfigOverride& config_override() {
         const int n = e ? std::sscanf(e, "%d,%d,%d,%d", &a, &b, &g, &ks) : 0;
         r.on = n >= 3 &&
                ((a == 256 && b == 256 && g == 1) || (a == 256 && b == 128 && g == 1) ||
-                (a == 128 && b == 128 && g == 2) || (a == 64 && b == 128 && g == 4)) &&
+                (a == 128 && b == 128 && g == 2) || (a == 128 && b == 128 && g == 1) ||
+                (a == 64 && b == 128 && g == 4)) &&
                (n == 3 || (ks >= 1 && ks <= 64));
         r.bm = a;
         r.bn = b;
@@ -687,6 +691,22 @@ TilePlan plan_tiles(int64_t M, int64_t K, const int64_t* N, int groups, int64_t 
                 t.ksplit = ks;
                 t.split_stages = stages;
             }
+        }
+    }
+    // Full-chip grids: where the model picks a 256-row tile unsplit and 128x128 tiles
+    // give every CU at least one, the 128x128 tile with one k-group runs instead.  Two of
+    // its blocks fit a CU (registers and LDS), so each SIMD interleaves two waves, which
+    // the one-round fits above cannot see; measured 2-12% faster on the 8B (M = 2048)
+    // and 70B (M = 1024) products, never slower there.
+    if (t.bm == 256 && t.ksplit == 1) {
+        int64_t tiles_n = 0;
+        for (int i = 0; i < groups; ++i) tiles_n += (N[i] + 127) / 128;
+        if (((M + 127) / 128) * tiles_n >= cus) {
+            t.bm = 128;
+            t.bn = 128;
+            t.g = 1;
+            t.bk = K % 128 == 0 ? 128 : 64;
+            t.split_stages = (int)((K + t.bk - 1) / t.bk);
         }
     }
     return t;
@@ -872,6 +892,11 @@ hipError_t launch_tiled_impl(const int8_t* xq, const float* a_scale, int groups,
     // register sets in flight: 64-k stages 4 (2 for 256x256); 128-k stages 2, or 4 for
     // the 256x128 tile (its accumulators live in the matrix-core registers)
     if (t.bm == 256 && t.bn == 256) return launch_plan<256, 256, 2, 1, 4, 64>(a, n_all, t, part, stream);
+    // 128x128, one k-group: waves in a 1 x 4 grid (128 x 32 each), four register sets
+    if (t.bm == 128 && t.g == 1) {
+        if (t.bk == 128) return launch_plan<128, 128, 4, 1, 4, 128>(a, n_all, t, part, stream);
+        return launch_plan<128, 128, 4, 1, 4, 64>(a, n_all, t, part, stream);
+    }
     if (t.bk == 128) {
         if (t.bm == 256) return launch_plan<256, 128, 4, 1, 2, 128>(a, n_all, t, part, stream);
         if (t.bm == 64) return launch_plan<64, 128, 2, 4, 4, 128>(a, n_all, t, part, stream);
