@@ -246,28 +246,32 @@ def test_gemm_plan_validation(L):
     assert f(512, 2560, 2, ctypes.cast(neg, P), 256, ctypes.cast(out, P)) == INVALID
 
 
-# (M, K, N per group) -> (block rows, block cols, k-groups, k per stage) on 256 CUs: the
-# launches of the 2B prefill step and the 8B/70B prefill shapes, and the shapes the GPU
-# parity tests use to reach every compiled (tile, k-stage) pair.
+# (M, K, N per group) -> (block rows, block cols, k-groups, k per stage, K slices) on 256
+# CUs: the launches of the 2B prefill step and the 8B/70B prefill shapes, and the shapes
+# the GPU parity tests use to reach every compiled (tile, k-stage) pair.
 PLAN_CASES = [
     ((512, 2560, [2560, 640, 640]), (64, 128, 4, 128, 1)),    # 2B q|k|v: 240 tiles, one round
     ((512, 2560, [2560]), (64, 128, 4, 128, 1)),              # 2B o
-    ((512, 2560, [6912, 6912]), (256, 128, 1, 128, 1)),       # 2B gate|up: 216 tiles, one round
+    ((512, 2560, [6912, 6912]), (128, 128, 1, 128, 1)),       # 2B gate|up: 432 tiles, two per CU
     ((512, 6912, [2560]), (64, 128, 4, 128, 1)),              # 2B down
-    ((2048, 4096, [14336]), (256, 256, 1, 64, 1)),            # 8B gate: two rounds of 256x256
-    ((2048, 14336, [4096]), (256, 128, 1, 128, 1)),           # 8B down
-    ((1024, 8192, [28672, 28672]), (256, 256, 1, 64, 1)),     # 70B gate|up
+    ((2048, 4096, [14336]), (128, 128, 1, 128, 1)),           # 8B gate
+    ((2048, 14336, [4096]), (128, 128, 1, 128, 1)),           # 8B down
+    ((1024, 8192, [28672, 28672]), (128, 128, 1, 128, 1)),    # 70B gate|up
     ((130, 320, [257, 64, 0, 96]), (64, 128, 4, 64, 1)),      # K % 128 != 0: 64-k stages
-    ((512, 2560, [2560, 640, 640]), (64, 128, 4, 128, 1)),
-    ((600, 256, [6912, 6912]), (256, 256, 1, 64, 1)),
-    ((500, 2048, [6000, 7000]), (256, 128, 1, 128, 1)),
-    ((1024, 128, [4096, 1024, 1024, 300]), (256, 128, 1, 64, 1)),
+    ((600, 256, [6912, 6912]), (128, 128, 1, 128, 1)),
+    ((500, 2048, [6000, 7000]), (128, 128, 1, 128, 1)),
+    ((1024, 128, [4096, 1024, 1024, 300]), (128, 128, 1, 128, 1)),
+    ((520, 320, [33000]), (128, 128, 1, 64, 1)),
     ((257, 320, [5000, 4000]), (128, 128, 2, 64, 1)),
     ((300, 384, [4100, 4100]), (128, 128, 2, 128, 1)),
     ((32, 8192, [8192]), (64, 128, 4, 128, 4)),            # 70B q, M=32: 64 tiles, 4 slices
     ((32, 28672, [8192]), (64, 128, 4, 128, 4)),           # 70B down, M=32
     ((32, 8192, [8192, 1024]), (64, 128, 4, 128, 1)),      # grouped launches never split
     ((2048, 4096, [1024]), (64, 128, 4, 128, 1)),          # 512 tiles: no split
+    # the 256-row tiles run only where K is split across blocks
+    ((400, 28672, [5000]), (256, 128, 1, 128, 3)),
+    ((400, 20416, [3000]), (256, 128, 1, 64, 5)),
+    ((600, 16320, [6912]), (256, 256, 1, 64, 3)),
 ]
 
 
@@ -281,16 +285,16 @@ def test_gemm_plan_covers_every_compiled_configuration():
     # every (tile, k-stage) pair the launcher instantiates is chosen for some shape, and
     # 128-k stages only when K % 128 == 0
     seen = set()
-    for M in (17, 130, 300, 512, 1024, 2048):
-        for K in (128, 192, 320, 384, 1024, 2048, 2560, 4096, 6912, 14336):
-            for Ns in ([640], [2560], [6912, 6912], [4096, 1024, 1024], [14336], [28672]):
+    for M in (17, 130, 300, 400, 512, 1024, 2048):
+        for K in (128, 192, 320, 384, 1024, 2048, 2560, 4096, 6912, 14336, 28608, 28672):
+            for Ns in ([640], [2560], [5000], [6912, 6912], [4096, 1024, 1024], [14336], [28672]):
                 p = bw.gemm_plan(M, K, Ns, cus=256)
                 seen.add(p[:4])
                 if K % 128:
                     assert p[3] == 64, (M, K, Ns, p)
-    assert seen == {(64, 128, 4, 128), (128, 128, 2, 128), (256, 128, 1, 128),
-                    (64, 128, 4, 64), (128, 128, 2, 64), (256, 128, 1, 64),
-                    (256, 256, 1, 64)}, seen
+    assert seen == {(64, 128, 4, 128), (128, 128, 2, 128), (128, 128, 1, 128),
+                    (256, 128, 1, 128), (64, 128, 4, 64), (128, 128, 2, 64),
+                    (128, 128, 1, 64), (256, 128, 1, 64), (256, 256, 1, 64)}, seen
 
 
 def test_gemm_plan_grids_of_one_round_take_small_tiles():

@@ -310,9 +310,9 @@ def test_quant_gemv_grouped_matches_oracle(M, K, Ns):
     (130, 320, [257, 64, 0, 96], DT),             # 64x128, 64-k, an empty group
     (512, 384, [2560, 640, 640], DT),             # q|k|v shapes: 64x128, 64-k
     (512, 2560, [2560, 640, 640], ("bf16", "i32")),  # q|k|v at full size: 64x128, 128-k
-    (600, 256, [6912, 6912], ("bf16", "i32")),    # gate|up shapes: 256x256, 64-k
-    (500, 2048, [6000, 7000], ("f32", "i32")),    # 256x128, 128-k
-    (1024, 128, [4096, 1024, 1024, 300], ("f32", "i32")),  # 256x128, 64-k
+    (600, 256, [6912, 6912], ("bf16", "i32")),    # gate|up shapes: 128x128 one k-group, 128-k
+    (500, 2048, [6000, 7000], ("f32", "i32")),    # 128x128 one k-group, 128-k
+    (1024, 128, [4096, 1024, 1024, 300], ("f32", "i32")),  # 128x128 one k-group, 128-k
     (257, 320, [5000, 4000], ("bf16", "i32")),    # 128x128, 64-k
     (300, 384, [4100, 4100], ("bf16", "i32")),    # 128x128, 128-k
 ])
@@ -665,8 +665,8 @@ def test_graph_replay_of_grouped_swiglu_and_a16_launches():
 
 
 def test_gemm_small_and_large_tile_grids():
-    # Shapes that select each tile configuration (64x128 with four k-groups, 128x128 with
-    # two, 256x128, 256x256; 64-k and 128-k stages), including grids far smaller than
+    # Shapes that select each unsplit tile configuration (64x128 with four k-groups,
+    # 128x128 with two or one; 64-k and 128-k stages), including grids far smaller than
     # the CU count and ragged edges, with and without a workspace (with one, the small
     # grids split K across blocks)
     for (M, N, K) in [(300, 257, 2560), (512, 2560, 2560), (130, 640, 6912), (17, 1024, 4096),
@@ -681,10 +681,12 @@ def test_gemm_small_and_large_tile_grids():
 
 
 # (M, N, K) whose tiled plan splits K across blocks (on 256 CUs): aligned and ragged N
-# (vector and element-wise reduce), 64-k and 128-k stages, up to 16 slices
+# (vector and element-wise reduce), 64-k and 128-k stages, up to 16 slices; the last three
+# reach the 256x128 (128-k and 64-k) and 256x256 tiles, which run only split
 SPLIT_CASES = [(32, 8192, 4096), (64, 1024, 4096), (17, 300, 2560), (33, 1000, 6912),
                (96, 130, 8192), (5, 2000, 2048), (1, 640, 2560), (300, 257, 2560),
-               (128, 512, 16384), (256, 4096, 14336)]
+               (128, 512, 16384), (256, 4096, 14336),
+               (400, 5000, 28672), (400, 3000, 20416), (600, 6912, 16320)]
 
 
 @pytest.mark.parametrize("M,N,K", SPLIT_CASES)
