@@ -61,22 +61,19 @@ __global__ __launch_bounds__(256) void mfma_i8_loop(const int32_t* __restrict__ 
 // flight per thread (contiguous per-block regions sustain more than a grid-stride walk).
 __global__ __launch_bounds__(256) void stream_read(const uint4* __restrict__ src, int64_t n,
                                                    uint32_t* __restrict__ out) {
+    // every pass issues its U loads (predicated past the share's end) before any is
+    // used, so a thread with a short share still waits for one memory trip per pass
     constexpr int U = 8;
     const int64_t per = (n + gridDim.x - 1) / gridDim.x;
     const int64_t lo = (int64_t)blockIdx.x * per;
     const int64_t hi = lo + per < n ? lo + per : n;
     uint32_t a = 0;
-    int64_t i = lo + threadIdx.x;
-    for (; i + (U - 1) * 256 < hi; i += U * 256) {
+    for (int64_t i = lo + threadIdx.x; i < hi; i += U * 256) {
         uint4 x[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) x[u] = src[i + u * 256];
+        for (int u = 0; u < U; ++u) x[u] = i + u * 256 < hi ? src[i + u * 256] : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
         for (int u = 0; u < U; ++u) a ^= x[u].x ^ x[u].y ^ x[u].z ^ x[u].w;
-    }
-    for (; i < hi; i += 256) {
-        const uint4 x = src[i];
-        a ^= x.x ^ x.y ^ x.z ^ x.w;
     }
     out[(int64_t)blockIdx.x * 256 + threadIdx.x] = a;
 }
