@@ -330,7 +330,15 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
 #pragma unroll
                 for (int t = 0; t < MT; ++t) {  // the unpacked weights feed every token tile
                     v4i A[4];
-                    if (16 * t + mrow < M) {
+                    if constexpr (MC == 1) {
+                        // one token: every lane reads row 0's fragment (a broadcast read),
+                        // so no branch guards it and the reads can be issued before the
+                        // weights arrive; rows 1-15 of the products repeat row 0 and are
+                        // never read
+                        const unsigned char* src = x_lds + (c * 4 + q) * 64;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) A[i] = *reinterpret_cast<const v4i*>(src + 16 * i);
+                    } else if (16 * t + mrow < M) {
                         const unsigned char* src = x_lds + (16 * t + mrow) * KSP + (c * 4 + q) * 64;
 #pragma unroll
                         for (int i = 0; i < 4; ++i) A[i] = *reinterpret_cast<const v4i*>(src + 16 * i);
