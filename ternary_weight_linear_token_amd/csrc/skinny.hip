@@ -338,13 +338,14 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
                         const unsigned char* src = x_lds + (c * 4 + q) * 64;
 #pragma unroll
                         for (int i = 0; i < 4; ++i) A[i] = *reinterpret_cast<const v4i*>(src + 16 * i);
-                    } else if (16 * t + mrow < M) {
-                        const unsigned char* src = x_lds + (16 * t + mrow) * KSP + (c * 4 + q) * 64;
+                    } else {
+                        // rows past M read row M - 1 (staged, so inside the block's LDS):
+                        // no branch guards the read, and the products of those rows are
+                        // never combined or stored
+                        const int row = min(16 * t + mrow, M - 1);
+                        const unsigned char* src = x_lds + row * KSP + (c * 4 + q) * 64;
 #pragma unroll
                         for (int i = 0; i < 4; ++i) A[i] = *reinterpret_cast<const v4i*>(src + 16 * i);
-                    } else {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) A[i] = v4i{0, 0, 0, 0};
                     }
 #pragma unroll
                     for (int v = 0; v < NW; ++v) {
