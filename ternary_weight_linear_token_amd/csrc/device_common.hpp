@@ -58,19 +58,40 @@ __device__ __forceinline__ uint32_t ternary_field_i8(uint32_t d) {
     return __builtin_amdgcn_perm(0u, 0x020100FFu, sel);
 }
 
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        uint32_t o = (uint32_t)__shfl_xor((int)v, off, 64);
-        v = v > o ? v : o;
-    }
+// Reductions over the 16 lanes of a DPP row (lanes 16r .. 16r+15): xor 1 and xor 2 by
+// quad permutes, then the 8-lane and 16-lane mirrors; every lane of the row gets the
+// result.  All on the VALU: no LDS round trip per step, unlike lane shuffles.
+template <typename Op>
+__device__ __forceinline__ uint32_t row16_reduce(uint32_t v, Op op) {
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // [1,0,3,2]
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // [2,3,0,1]
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // half mirror
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));  // mirror
     return v;
+}
+__device__ __forceinline__ uint32_t row16_max(uint32_t v) {
+    return row16_reduce(v, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+}
+__device__ __forceinline__ int row16_sum(int v) {
+    return (int)row16_reduce((uint32_t)v, [](uint32_t a, uint32_t b) { return a + b; });
+}
+
+// Wave-wide reductions (every lane active) with a uniform result: the row reduction,
+// then the four row results read out with v_readlane.
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce_dpp(uint32_t v, Op op) {
+    v = row16_reduce(v, op);
+    const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+    const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+    return op(op(a, b), op(c, d));
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    return wave_reduce_dpp(v, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
 }
 
 __device__ __forceinline__ int wave_sum_i32(int v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
+    return (int)wave_reduce_dpp((uint32_t)v, [](uint32_t a, uint32_t b) { return a + b; });
 }
 
 // Store one output element in the requested dtype (0 = f32, 1 = bf16, 2 = int32).

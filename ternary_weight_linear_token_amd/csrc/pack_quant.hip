@@ -119,19 +119,6 @@ __global__ __launch_bounds__(256) void unpack_kernel(const uint8_t* __restrict__
 // pass 1 only and leaves the row's max magnitude bits in a_scale[m]; tensor_scale_kernel
 // reduces them and writes the common scale to every a_scale[m]; MODE 2 runs pass 2 with
 // the scale read from a_scale[m].
-// Wave-wide max with the result in every lane, on the VALU: DPP within each 16-lane row
-// (xor 1 and xor 2 by quad permutes, then the 8- and 16-lane mirrors), then the four row
-// maxima read out with v_readlane -- no LDS round trip, unlike lane shuffles.
-__device__ __forceinline__ uint32_t wave_max_dpp(uint32_t v) {
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // [1,0,3,2]
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // [2,3,0,1]
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // half mirror
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));  // mirror
-    const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
-    const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
-    return max(max(a, b), max(c, d));
-}
-
 template <int V>
 struct QVec {
     uint32_t w[V / 2];  // V bf16 values, two per word, low half first
@@ -203,7 +190,7 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restri
     if constexpr (MODE == 2) {
         if (live) a = a_scale[m];
     } else {
-        mx = wave_max_dpp(mx);
+        mx = wave_max_u32(mx);
         if constexpr (WPR > 1) {
             if ((threadIdx.x & 63) == 0) s_max[wave] = mx;
             __syncthreads();

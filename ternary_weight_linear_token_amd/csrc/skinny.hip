@@ -131,37 +131,6 @@ __device__ __forceinline__ float buf_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t
     return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
 
-// Reductions over the 16 lanes of a DPP row (lanes 16r .. 16r+15): xor 1 and xor 2 by
-// quad permutes, then the 8-lane and 16-lane mirrors; every lane of the row gets the result.
-template <typename Op>
-__device__ __forceinline__ uint32_t row16_reduce(uint32_t v, Op op) {
-    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // [1,0,3,2]
-    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // [2,3,0,1]
-    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // half mirror
-    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));  // mirror
-    return v;
-}
-__device__ __forceinline__ uint32_t row16_max(uint32_t v) {
-    return row16_reduce(v, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
-}
-__device__ __forceinline__ int row16_sum(int v) {
-    return (int)row16_reduce((uint32_t)v, [](uint32_t a, uint32_t b) { return a + b; });
-}
-
-// Wave-wide reductions with a uniform (scalar) result: DPP within each row, then the
-// four row results read out with v_readlane.
-__device__ __forceinline__ uint32_t wave_max_uniform(uint32_t v) {
-    v = row16_max(v);
-    const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
-    const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
-    return max(max(a, b), max(c, d));
-}
-__device__ __forceinline__ int wave_sum_uniform(int v) {
-    v = row16_sum(v);
-    return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
-           __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
-}
-
 // 16 packed bytes at byte offset `off` of packed row `n`, byte by byte, zeros past the
 // row end (the path for K not a multiple of 64, whose rows are not 16-byte aligned).
 __device__ __forceinline__ uint4 load_w16_bytes(const uint8_t* __restrict__ packed,
@@ -417,7 +386,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
                 uint32_t mx = 0;
 #pragma unroll
                 for (int t = 0; t < XH; ++t) mx = max(mx, absmax_bits16(held[t]));  // 0 if unused
-                mx = wave_max_uniform(mx);
+                mx = wave_max_u32(mx);
                 if (lane == 0) s_wmax[wave * kSkMaxM] = mx;
             } else {
 #pragma unroll
@@ -456,7 +425,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
                 if (row_leader && c < nch0) atomicAdd(&s_wsum[wave * kSkMaxM + m], rs);
             }
         }
-        if (MC == 1) wsum_m1 = wave_sum_uniform(rsum);
+        if (MC == 1) wsum_m1 = wave_sum_i32(rsum);
     } else {
         // the first weights of stage 0 are requested before the activations are read
         load_batch(wa, 0, 0, nch0);
