@@ -102,6 +102,11 @@ def load_summary(path: str, kernel_hash: str):
     return vals if vals.get("kernel_source_sha256") == kernel_hash else None
 
 
+# launches per graph when the activation quantization is timed on its own (its input is
+# the same tensor each time, as a layer's input would come from the layer before)
+QUANT_LAUNCHES = 32
+
+
 def rotation(tensors, nbytes):
     """Copies of `tensors` (nbytes together) whose total exceeds ROTATE_BYTES: entry r
     of the returned list is the r-th copy (entry 0 the tensors themselves)."""
@@ -501,7 +506,7 @@ def bench_sweep(bw, workloads, torch, dev, reps):
                     us = graph_launch_us(torch, lambda r: bw.gemm(xq, a, cp[r][0], s, "bf16", out=o),
                                          R, reps)
                     quant_us = graph_launch_us(torch, lambda r: bw.quant_act(x, xq=xq, a_scale=a),
-                                               8, reps)
+                                               QUANT_LAUNCHES, reps)
                     nbytes = N * K // 4 + 4 * N + M * K + 4 * M + 2 * M * N
                     entry = "bitnet_w2a8_gemm"
                 ops = 2.0 * M * N * K
@@ -829,7 +834,8 @@ def bench_gemm(bw, workloads, torch, dev, layer, reps, probe=False):
         del cp
     torch.cuda.empty_cache()
     quant_us = {"|".join(g): round(graph_launch_us(
-        torch, lambda r, i0=index[g[0]]: bw.quant_act(xs[i0], xq=xqs[i0], a_scale=avs[i0]), 8,
+        torch, lambda r, i0=index[g[0]]: bw.quant_act(xs[i0], xq=xqs[i0], a_scale=avs[i0]),
+        QUANT_LAUNCHES,
         reps), 3) for g in workloads.DECODE_GROUPS}
     tops = ops / (sum(per_group_us) * 1e-6) / 1e12
     # context: the vendor int8 GEMM (hipBLASLt, dense int8 weights) on the same four
