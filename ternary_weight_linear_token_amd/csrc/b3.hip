@@ -66,7 +66,7 @@ __device__ __forceinline__ uint4 b3_load16(__amdgpu_buffer_rsrc_t r, uint32_t of
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
-// wave-wide max with a uniform result (xor shuffles)
+// wave-wide max with a uniform result (DPP row steps, then v_readlane)
 __device__ __forceinline__ uint32_t b3_wave_max(uint32_t v) {
     v = wave_max_u32(v);
     return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
