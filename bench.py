@@ -17,9 +17,10 @@ one launch per projection is reported beside it (value_ungrouped).
   the weights it reads that together exceed 1 GiB (four times the 256 MB Infinity
   Cache), so the weights come from HBM: the step over copies of the whole set, and each
   per-launch graph over copies of that launch's own matrices.
-* Steps are captured in HIP graphs, ten consecutive steps (each on the next weight
-  copy) per graph, so host submission does not pace the GPU; W warmup steps, then
-  exactly K steps between two synchronizations timed with events.
+* Steps are captured in HIP graphs, thirty consecutive steps (each on the next weight
+  copy; thirty is the 2B model's layer count, so one graph is one model decode step) per
+  graph, so host submission does not pace the GPU; W warmup steps, then exactly K steps
+  between two synchronizations timed with events.
 * value = packed-weight bytes of the set / step time (GB/s).
 * roofline: the fused quant+GEMV kernel, algorithmic bytes (N*K/4 packed bytes per
   launch) / its mean launch duration (a graph of back-to-back launches over the
@@ -178,19 +179,6 @@ def main():
         bench_gemm(bw, workloads, torch, dev, layer, reps=args.kernel_reps, probe=True)
         return
 
-    # Steps are captured STEPS_PER_GRAPH at a time, each on the next weight copy, so the
-    # host's graph submissions never pace the GPU; one-step graphs cover the remainder.
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        launch_set(0)  # eager warm-up on the capture stream
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    ms_step = run_steps(torch, launch_set, R, args.warmup, args.steps)
-    value = set_bytes / (ms_step * 1e-3) / 1e9
-    ms_step_ungrouped = run_steps(torch, launch_set_ungrouped, R, args.warmup, args.steps)
-    del copies
-    torch.cuda.empty_cache()
 
     # ---- per-launch kernel durations: one graph per launch holding back-to-back
     # launches over that launch's own weight copies (> 1 GiB together); event time of
@@ -249,6 +237,22 @@ def main():
                                    for (name, _, _), us in zip(layer, per_shape_us)},
         "ungrouped_achieved": round(set_bytes / (sum(per_shape_us) * 1e-6) / 1e9, 1),
     }
+    # ---- the step: timed after the per-launch measurements above, so that it runs on a
+    # GPU already at its working clocks rather than ramping up from idle during a short
+    # timed region.  Steps are captured STEPS_PER_GRAPH at a time, each on the next
+    # weight copy, so the host's graph submissions never pace the GPU; one shorter graph
+    # covers the remainder. ----
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        launch_set(0)  # eager warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    ms_step = run_steps(torch, launch_set, R, args.warmup, args.steps)
+    value = set_bytes / (ms_step * 1e-3) / 1e9
+    ms_step_ungrouped = run_steps(torch, launch_set_ungrouped, R, args.warmup, args.steps)
+    del copies
+    torch.cuda.empty_cache()
     del packed0
     torch.cuda.empty_cache()
 
@@ -301,14 +305,17 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-STEPS_PER_GRAPH = 10
+# Layer steps per captured graph: 30, the layer count of the 2B model, i.e. one graph per
+# model decode step, as a serving loop would replay it.  A graph replay costs a few µs of
+# its own (about 8 µs here), which this spreads over the step's layers.
+STEPS_PER_GRAPH = 30
 
 
 def run_steps(torch, launch_step, R, warmup, steps):
     """Run `warmup` untimed steps, then time exactly `steps` steps (ms per step).
 
     Step s uses weight copy s % R.  Steps run as graph replays: graphs of STEPS_PER_GRAPH
-    consecutive steps, then one-step graphs for what is left of `steps`."""
+    consecutive steps, then one graph of what is left of `steps`."""
     S = STEPS_PER_GRAPH
 
     def capture(first, count):
@@ -321,11 +328,11 @@ def run_steps(torch, launch_step, R, warmup, steps):
     # the sequence of (first step, count) replays for warmup + timed steps
     def plan(first, count):
         out = []
-        while count >= S:
-            out.append((first, S))
-            first += S
-            count -= S
-        out += [(first + j, 1) for j in range(count)]
+        while count > 0:
+            c = min(S, count)
+            out.append((first, c))
+            first += c
+            count -= c
         return out
 
     graphs = {}
