@@ -75,6 +75,20 @@ __host__ __device__ constexpr int chunks_of_wave(int w, int nch) {
     const int span = kSkRun * kSkWaves, r = nch % span - kSkRun * w;
     return (nch / span) * kSkRun + (r < 0 ? 0 : (r > kSkRun ? kSkRun : r));
 }
+// The same with the last, partial round of runs spread one chunk per wave in turn, so
+// that no wave owns more than one chunk above another (one token, one K stage of at most
+// three chunks per wave: the 2560-wide projections take 3, 3, 2, 2 chunks instead of 4,
+// 2, 2, 2).  Only for launches with a single K stage: with several, a wave's LDS slots
+// must not depend on the stage, or it would overwrite activations that another wave
+// still reads.  Slots j past a wave's share map to chunks >= nch.
+__host__ __device__ constexpr int chunk_of_spread(int w, int j, int nch) {
+    const int span = kSkRun * kSkWaves, full = nch / span;
+    return j < full * kSkRun ? chunk_of(w, j) : full * span + w + kSkWaves * (j - full * kSkRun);
+}
+__host__ __device__ constexpr int chunks_of_wave_spread(int w, int nch) {
+    const int span = kSkRun * kSkWaves, tail = nch % span;
+    return (nch / span) * kSkRun + (tail > w ? (tail - w + kSkWaves - 1) / kSkWaves : 0);
+}
 constexpr int kSkXBudget = 48 * 1024;   // LDS bytes for the staged activations
 constexpr int kSkMaxM = 64;                    // rows of activations (tokens) per launch
 constexpr int kSkMisc = kSkWaves * kSkMaxM * 8 + kSkMaxM * 4;  // s_wmax, s_wsum [waves][64]; s_inva [64]
@@ -186,6 +200,11 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
     constexpr int NW = PAIR ? 2 : NR;  // weight operands per chunk (matrices or row tiles)
     extern __shared__ __align__(16) unsigned char smem[];
     const int KSP = p.KS + 16;  // padded LDS row stride: spreads rows over the banks
+    // one token, one batch of three chunks: the spread deal (see chunk_of_spread)
+    constexpr bool kSpread = MC == 1 && SINGLE && U == 3;
+    auto chunk_at = [](int w, int j, int nch) {
+        return kSpread ? chunk_of_spread(w, j, nch) : chunk_of(w, j);
+    };
     const int M = MC > 0 ? MC : p.M;
     const int K = p.K;
     // this block's group: uniform, resolved with scalar selects
@@ -253,7 +272,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
     auto load_batch = [&](uint4 (&w)[U * NW], int j0, int stage_off, int nch) {
 #pragma unroll
         for (int uu = 0; uu < U; ++uu) {
-            const int c = chunk_of(wave, j0 + uu);
+            const int c = chunk_at(wave, j0 + uu, nch);
             const int cb = stage_off + c * 64;  // the chunk's first byte in the row
 #pragma unroll
             for (int v = 0; v < NW; ++v) {
@@ -279,7 +298,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
     auto compute_batch = [&](const uint4 (&w)[U * NW], int j0, int nch) {
 #pragma unroll
         for (int uu = 0; uu < U; ++uu) {
-            const int c = chunk_of(wave, j0 + uu);
+            const int c = chunk_at(wave, j0 + uu, nch);
             // With M = 1 and one batch, chunks past the stage are multiplied as well: their
             // weights read as zeros and their operand-A reads stay inside the LDS block.
             if ((MC == 1 && SINGLE) || c < nch) {
@@ -346,15 +365,15 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs p) {
     // groups are numbered g = (j * M + m) * 16 + i (activations k = 256 c + 16 i ..
     // + 15 of row m); lane l takes g = l + 64 t, so the 16 lanes of a DPP row share
     // (j, m) and reduce their per-row partials with DPP before one LDS atomic.
+    const int nch0 = min(p.KS, p.Kp) >> 8;  // chunks of the first (or only) K stage
     auto group_of = [&](int g, int& m, int& c, int& i) {
         i = g & 15;
         const int jm = g >> 4, j = jm / M;
         m = jm - j * M;
-        c = chunk_of(wave, j);
+        c = chunk_at(wave, j, nch0);
     };
 
     uint4 wa[U * NW];
-    const int nch0 = min(p.KS, p.Kp) >> 8;
     float a_m1 = 0.0f;  // M = 1, fused: the token's scale, uniform
     int wsum_m1 = 0;    // M = 1: code sum of the activations this wave staged, uniform
     if constexpr (XH > 0) {
@@ -664,6 +683,10 @@ hipError_t launch_fast(const SkinnyArgs& a, dim3 grid, size_t lds, hipStream_t s
 template <bool FUSED, bool PAIR = false, int NR = 1>
 hipError_t launch_m1(const SkinnyArgs& a, dim3 grid, size_t lds, hipStream_t stream) {
     const int cpw = chunks_of_wave(0, a.Kp / 256);
+    // more than one round of runs, and three chunks per wave at most under the spread
+    // deal (9 to 12 chunks): one batch of exactly three
+    if (a.Kp / 256 > kSkRun * kSkWaves && chunks_of_wave_spread(0, a.Kp / 256) <= 3)
+        return launch_one<FUSED, true, 1, 3, true, 1, 1, PAIR, NR>(a, grid, lds, stream);
     if (cpw <= 4) return launch_one<FUSED, true, 1, 4, true, 1, 1, PAIR, NR>(a, grid, lds, stream);
     if (cpw <= 8) return launch_one<FUSED, true, 2, 8, true, 1, 1, PAIR, NR>(a, grid, lds, stream);
     if (cpw <= 16) return launch_one<FUSED, true, 4, 8, false, 1, 1, PAIR, NR>(a, grid, lds, stream);
